@@ -1,0 +1,270 @@
+"""fp64 CPU oracle for DART chunk state memories and state-memory attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers or tables) and imports nothing from it.
+
+Every function below is the plain definition from the paper
+"DART: Decoded Attention over Recurrent States for Efficient Long-Context
+Sequence Modeling" (arXiv 2608.02032), evaluated in float64 with numpy.
+Citations name the paper's section and equation, e.g. [§3 Eq. 5].
+
+Conventions (the paper's notation, 0-based indices):
+  * tokens t = 0..L-1, chunk size S, chunk(t) = t // S (the paper writes the
+    1-based c(t) = ceil(t/S)); chunk c holds tokens [cS, min((c+1)S, L)), so
+    M = ceil(L/S) chunks, the last one possibly shorter;
+  * X (L, P), B (L, N), C (L, N), Q (L, N), E (L, P): one row per token;
+  * chunk state memories dH (M, N, P), each the paper's N x P matrix
+    (key axis N, value axis P) -- the oracle keeps the paper's orientation;
+  * a (L,): the scalar decay a_t of A_t = a_t I_N  [§2 Eq. 2].
+
+Readings where the paper leaves a step open (each is also listed in the
+design notes):
+  * a token sees chunk c iff c < chunk(t) -- strictly earlier chunks only
+    [§3 Eq. 10, Algorithm 1 "for historical chunk j < i"];
+  * a token with no visible chunk gets R_t = 0 and lse_t = -inf
+    [§3 text after Eq. 10; Algorithm 1 steps 15-16];
+  * the gate is given after its activation, either one scalar per token
+    (the paper's G_t) or one value per channel, and out = Y_ssm + g * R
+    [§3 Eq. 11];
+  * a partial last chunk decays to its own last token (e(c) is the last index
+    actually in the chunk) [§3 text under Eq. 5].
+
+Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
+against brute force, closed forms, special cases and the paper's printed
+numbers; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "num_chunks",
+    "chunk_bounds",
+    "decay_weights",
+    "chunk_states_head",
+    "chunk_states",
+    "ssm_recurrence",
+    "boundary_states",
+    "sma_token",
+    "sma_head",
+    "sma_forward",
+    "gated_residual",
+    "sma_decode",
+    "cache_ratio",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def num_chunks(L: int, S: int) -> int:
+    """M = ceil(L / S)  [§4 "Training Complexity"; Algorithm 1 step 1]."""
+    return -(-L // S)
+
+
+def chunk_bounds(c: int, L: int, S: int) -> tuple[int, int]:
+    """Token range [s0, s1) of chunk c; e(c) = s1 - 1 is its last index [§3]."""
+    return c * S, min((c + 1) * S, L)
+
+
+def decay_weights(a_chunk) -> np.ndarray:
+    """Weights w_s = A_{s+1:e(c)} = prod_{k=s+1}^{e(c)} a_k for the tokens of
+    one chunk, in token order  [§3 Eq. 5 and the text under it; §2 Eq. 3].
+
+    The product starts at s+1: the writing token's own decay is not applied,
+    and the chunk's last token gets the empty product, 1.  Computed as a
+    suffix product (never as a ratio of prefix products, which would divide
+    0 by 0 once the prefix underflows)."""
+    a = _f64(a_chunk)
+    n = a.shape[0]
+    w = np.empty(n, dtype=np.float64)
+    if n == 0:
+        return w
+    w[n - 1] = 1.0
+    for s in range(n - 2, -1, -1):
+        w[s] = w[s + 1] * a[s + 1]
+    return w
+
+
+def chunk_states_head(X, B, a, S: int) -> np.ndarray:
+    """Chunk state contributions of one head  [§3 Eq. 5; App. A Eq. 20]:
+
+        dH_[c] = sum_{s in [c]} A_{s+1:e(c)} B_s^T X_s      (N x P)
+
+    X (L, P), B (L, N), a (L,)  ->  dH (M, N, P)."""
+    X, B, a = _f64(X), _f64(B), _f64(a)
+    L, P = X.shape
+    N = B.shape[1]
+    M = num_chunks(L, S)
+    dH = np.zeros((M, N, P), dtype=np.float64)
+    for c in range(M):
+        s0, s1 = chunk_bounds(c, L, S)
+        w = decay_weights(a[s0:s1])
+        # sum_s w_s * outer(B_s, X_s), written as one matrix product
+        dH[c] = B[s0:s1].T @ (w[:, None] * X[s0:s1])
+    return dH
+
+
+def chunk_states(X, B, A, S: int) -> np.ndarray:
+    """Batched chunk_states_head.  X (b, L, H, P), B (b, L, G, N),
+    A (b, L, H)  ->  dH (b, H, M, N, P).  Head h reads projection group
+    h // (H // G)  [§3 Fig. 2 caption; App. B.2]."""
+    X, B, A = _f64(X), _f64(B), _f64(A)
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    assert H % G == 0
+    hpg = H // G
+    out = np.zeros((b, H, num_chunks(L, S), N, P), dtype=np.float64)
+    for bi in range(b):
+        for h in range(H):
+            out[bi, h] = chunk_states_head(X[bi, :, h], B[bi, :, h // hpg], A[bi, :, h], S)
+    return out
+
+
+def ssm_recurrence(X, B, a, H0=None) -> np.ndarray:
+    """Brute-force Mamba-2 step recurrence  [§2 Eq. 2; App. A Eq. 15]:
+
+        H_t = a_t H_{t-1} + B_t^T X_t,   H_{-1} = H0 (zero by default)
+
+    X (L, P), B (L, N), a (L,)  ->  all states H (L, N, P)."""
+    X, B, a = _f64(X), _f64(B), _f64(a)
+    L, P = X.shape
+    N = B.shape[1]
+    Hs = np.zeros((L, N, P), dtype=np.float64)
+    h = np.zeros((N, P)) if H0 is None else _f64(H0).copy()
+    for t in range(L):
+        h = a[t] * h + np.outer(B[t], X[t])
+        Hs[t] = h
+    return Hs
+
+
+def boundary_states(dH, a, S: int) -> np.ndarray:
+    """Chunk-boundary states from the chunk contributions  [App. A Eq. 17-18]:
+
+        H_[c] = A_{a_c:b_c} H_[c-1] + dH_[c],   H_[-1] = 0
+
+    where A_{a_c:b_c} is the product of the decays of every token of chunk c.
+    dH (M, N, P), a (L,)  ->  H_[c] (M, N, P)."""
+    dH, a = _f64(dH), _f64(a)
+    L = a.shape[0]
+    M = dH.shape[0]
+    out = np.zeros_like(dH)
+    prev = np.zeros(dH.shape[1:])
+    for c in range(M):
+        s0, s1 = chunk_bounds(c, L, S)
+        decay = 1.0
+        for k in range(s0, s1):
+            decay *= a[k]
+        prev = decay * prev + dH[c]
+        out[c] = prev
+    return out
+
+
+def sma_token(q, c, e, dH_visible):
+    """State-memory attention of one token over its visible chunk memories
+    [§3 Eq. 8-10]:
+
+        V_c = C_t dH_c (P),  K_c = dH_c E_t (N),  l_c = Q_t K_c / sqrt(N)
+        g = softmax_c(l),    R_t = sum_c g_c V_c
+
+    q, c (N,), e (P,), dH_visible (n, N, P).  Returns (R (P,), lse) with
+    lse = log sum_c exp(l_c)  [App. C Eq. 32]; an empty set gives (0, -inf)
+    [§3 text after Eq. 10]."""
+    q, c, e, dH = _f64(q), _f64(c), _f64(e), _f64(dH_visible)
+    N, P = dH.shape[1], dH.shape[2]
+    n = dH.shape[0]
+    if n == 0:
+        return np.zeros(P), -math.inf
+    V = np.einsum("n,cnp->cp", c, dH)          # value readout C_t dH_c  [Eq. 6, 8]
+    K = np.einsum("cnp,p->cn", dH, e)          # key readout dH_c E_t    [Eq. 6, 8]
+    logits = (K @ q) / math.sqrt(N)            # [Eq. 9]
+    m = logits.max()
+    p = np.exp(logits - m)                     # stable softmax [App. C Eq. 28]
+    d = p.sum()
+    R = (p[:, None] * V).sum(axis=0) / d       # [Eq. 10]
+    return R, m + math.log(d)                  # [App. C Eq. 32]
+
+
+def sma_head(Q, C, E, dH, S: int):
+    """SMA readout of one head for every token  [§3 Eq. 8-10]:
+    Q, C (L, N), E (L, P), dH (M, N, P)  ->  R (L, P), lse (L,).
+
+    The tokens of one target chunk i share the visible set {0..i-1}, so the
+    same formulas as ``sma_token`` are evaluated for all of them at once with
+    matrix products; no term is reordered or dropped."""
+    Q, C, E, dH = _f64(Q), _f64(C), _f64(E), _f64(dH)
+    L, N = Q.shape
+    P = E.shape[1]
+    M = num_chunks(L, S)
+    R = np.zeros((L, P), dtype=np.float64)
+    lse = np.full(L, -math.inf, dtype=np.float64)
+    scale = 1.0 / math.sqrt(N)
+    for i in range(1, M):
+        s0, s1 = chunk_bounds(i, L, S)
+        hist = dH[:i]                                       # (i, N, P)
+        V = np.einsum("tn,cnp->tcp", C[s0:s1], hist)        # C_t dH_c
+        K = np.einsum("cnp,tp->tcn", hist, E[s0:s1])        # dH_c E_t
+        logits = np.einsum("tn,tcn->tc", Q[s0:s1], K) * scale
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        d = p.sum(axis=1, keepdims=True)
+        R[s0:s1] = np.einsum("tc,tcp->tp", p, V) / d
+        lse[s0:s1] = (m + np.log(d))[:, 0]
+    return R, lse
+
+
+def sma_forward(Q, C, E, dH, S: int):
+    """Batched sma_head.  Q, C (b, L, G, N), E (b, L, G, P),
+    dH (b, H, M, N, P)  ->  R (b, L, H, P), lse (b, H, L)."""
+    Q, C, E = _f64(Q), _f64(C), _f64(E)
+    b, L, G, N = Q.shape
+    H = dH.shape[1]
+    P = E.shape[3]
+    hpg = H // G
+    R = np.zeros((b, L, H, P))
+    lse = np.zeros((b, H, L))
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            R[bi, :, h], lse[bi, h] = sma_head(Q[bi, :, g], C[bi, :, g], E[bi, :, g], dH[bi, h], S)
+    return R, lse
+
+
+def gated_residual(Y, gate, R, gate_per_channel: bool = True) -> np.ndarray:
+    """Gated residual  Y_t = C_t H_t + G_t R_t  [§3 Eq. 11], with the SSM
+    branch output C_t H_t given as Y.  ``gate`` is post-activation: shape
+    (..., P) when per channel, else (...) and broadcast over P."""
+    Y, gate, R = _f64(Y), _f64(gate), _f64(R)
+    g = gate if gate_per_channel else gate[..., None]
+    return Y + g * R
+
+
+def sma_decode(q, c, e, cache, n_chunks, hpg: int = 1):
+    """Decode: one new token per batch row against its chunk-memory cache
+    [§4 "Inference Cache"; §3 Eq. 8-10].  The new token lies after the last
+    complete cached chunk, so every cached chunk 0..n_b-1 is visible.
+
+    q, c (b, G, N), e (b, G, P), cache (b, H, Mmax, N, P), n_chunks (b,)
+    ->  R (b, H, P), lse (b, H)."""
+    q, c, e, cache = _f64(q), _f64(c), _f64(e), _f64(cache)
+    b, H = cache.shape[0], cache.shape[1]
+    P = cache.shape[4]
+    R = np.zeros((b, H, P))
+    lse = np.zeros((b, H))
+    for bi in range(b):
+        nb = int(n_chunks[bi])
+        for h in range(H):
+            g = h // hpg
+            R[bi, h], lse[bi, h] = sma_token(q[bi, g], c[bi, g], e[bi, g], cache[bi, h, :nb])
+    return R, lse
+
+
+def cache_ratio(N: int, S: int) -> float:
+    """Chunk-memory cache over the matched token-level KV cache, per head
+    [§4 Eq. 14]: (L N P / S) / (2 L P) = N / (2 S)."""
+    return N / (2.0 * S)
