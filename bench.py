@@ -1,0 +1,216 @@
+"""Benchmark of the DART hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3] [--no-cpu-baseline]
+
+One step = dart_chunk_states + dart_sma_fwd over one batch of synthetic input
+(the long-context bf16 forward: b=2, H=24, L=16384, S=256, N=128, P=64 by
+default), inputs resident in HBM before the timed region.  Prints one JSON
+line: whole-job tokens/s, the roofline of the dominant kernel (dart_sma_fwd,
+bound by bf16 MFMA) measured with HIP events on the launch stream, the
+decode call's HBM roofline, and the fp64 oracle timed on a bounded sample on
+the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "SMA+chunk-state fwd tokens/s at L=16K,N=128,P=64,S=256; % bf16 MFMA peak"
+KERNEL_SOURCES = {
+    "sma_fwd": "state_memory_attention_amd/csrc/sma_fwd_mfma.hip",
+    "chunk_states": "state_memory_attention_amd/csrc/chunk_states_mfma.hip",
+    "decode": "state_memory_attention_amd/csrc/sma_decode_mfma.hip",
+}
+
+
+def source_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def fwd_pairs(b, H, L, S):
+    """(token, visible chunk) pairs: sum over tokens of chunk(t)."""
+    M = -(-L // S)
+    full = sum(i * S for i in range(M - 1))
+    last = (M - 1) * (L - (M - 1) * S)
+    return b * H * (full + last)
+
+
+def fwd_flops(cfg):
+    """Algorithmic flops: 4NP per (token, visible chunk) pair for the two
+    products Q dH and C dH, plus 2SNP per chunk memory built (2 N P per token)."""
+    b, H, L, S, N, P = (cfg[k] for k in ("batch", "nheads", "seqlen", "chunk", "d_state", "d_head"))
+    return 4 * N * P * fwd_pairs(b, H, L, S), 2 * N * P * b * H * L
+
+
+def traffic_record(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The fp64 oracle (chunk states + SMA of whole heads, the same recipe,
+    seed 0, numpy generator) timed on the host, one head at a time until the
+    budget is spent; scaled to tokens/s of the full workload."""
+    import numpy as np
+
+    import oracle as O
+    from state_memory_attention_amd import synth
+
+    one = dict(cfg, batch=1, nheads=1, ngroups=1)
+    heads, t_total = 0, 0.0
+    while t_total < budget_s and heads < cfg["batch"] * cfg["nheads"]:
+        d = synth.draw_fwd(**one, seed=heads)
+        t0 = time.perf_counter()
+        dH = O.chunk_states(d["X"], d["B"], d["A"], cfg["chunk"])
+        R, _ = O.sma_forward(d["Q"], d["C"], d["E"], dH, cfg["chunk"])
+        O.gated_residual(d["Y"], d["gate"], R)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    # the full workload is batch * nheads such head-sequences of L tokens each
+    value = heads * cfg["seqlen"] / (t_total * cfg["nheads"])
+    return {"value": value, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{heads} whole head-sequence(s) of the same workload (L={cfg['seqlen']}, "
+                      f"S={cfg['chunk']}, N={cfg['d_state']}, P={cfg['d_head']}), chunk states + SMA + "
+                      f"gated residual in fp64 numpy, {t_total:.1f} s; scaled by heads/(batch*nheads)"}
+
+
+def time_decode(torch, dart, synth, steps=20, warmup=3):
+    cfg = dict(synth.CONFIGS[4])
+    d = synth.draw_decode_torch(**cfg, seed=0)
+    ws = torch.empty(dart.decode_workspace_bytes(cfg["batch"], cfg["nheads"], cfg["d_head"],
+                                                 cfg["max_chunks"]), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["y"])
+    args = (d["q"], d["c"], d["e"], d["cache"], d["y"], d["gate"])
+    for _ in range(warmup):
+        dart.dart_sma_decode(*args, out=out, workspace=ws)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        dart.dart_sma_decode(*args, out=out, workspace=ws)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = d["cache"].numel() * 2 + sum(d[k].numel() * 2 for k in ("q", "c", "e", "y", "gate")) + out.numel() * 2
+    gbs = nbytes / t / 1e9
+    res = {"workload": cfg["name"], "us_per_call": t * 1e6, "bytes_per_call": nbytes,
+           "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
+           "traffic": traffic_record("decode", cfg["name"])}
+    del d, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build runs the "
+              "hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import state_memory_attention_amd as dart
+    from state_memory_attention_amd import synth
+
+    cfg = dict(synth.CONFIGS[args.config])
+    b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    M = dart.num_chunks(L, S)
+    dH = torch.empty((b, H, M, cfg["d_head"], cfg["d_state"]), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(d["Y"])
+
+    def step():
+        dart.dart_chunk_states(d["X"], d["B"], d["A"], S, dH=dH)
+        dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    st = torch.cuda.current_stream()  # the library launches on this stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(st)
+        dart.dart_chunk_states(d["X"], d["B"], d["A"], S, dH=dH)
+        ev[k][1].record(st)
+        dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S, out=out)
+        ev[k][2].record(st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    t_cs = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps / 1e3
+    t_fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps / 1e3
+
+    f_sma, f_cs = fwd_flops(cfg)
+    achieved = f_sma / t_fwd / 1e12
+    value = b * L * args.steps / elapsed
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded torch generator on the GPU; recipe in DESIGN.md)",
+        "config": {"workload": cfg["name"], "batch": b, "nheads": H, "ngroups": cfg["ngroups"],
+                   "seqlen": L, "chunk": S, "d_state": cfg["d_state"], "d_head": cfg["d_head"]},
+        "roofline": {"bound": "mfma", "kernel": "dart_sma_fwd", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_record("sma_fwd", cfg["name"]),
+                     "flop_per_launch": f_sma, "us_per_launch": t_fwd * 1e6},
+        "kernels_us": {"dart_chunk_states": t_cs * 1e6, "dart_sma_fwd": t_fwd * 1e6},
+        "path_mfma_frac": (f_sma + f_cs) / (t_cs + t_fwd) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+    del d, dH, out
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        result["decode"] = time_decode(torch, dart, synth)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

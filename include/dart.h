@@ -1,0 +1,150 @@
+/*
+ * dart.h -- C ABI of the DART hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the data-parallel hot path of
+ *   "DART: Decoded Attention over Recurrent States for Efficient Long-Context
+ *    Sequence Modeling" (arXiv 2608.02032):
+ *   - chunk state memories            dart_chunk_states   [§3 Eq. 5; App. A Eq. 20]
+ *   - state-memory attention (SMA)    dart_sma_fwd        [§3 Eq. 8-11; §4 Algorithm 1]
+ *     with the gated residual
+ *   - SMA for one new token against   dart_sma_decode     [§4 "Inference Cache"]
+ *     a cache of chunk memories
+ *
+ * Notation: b = batch, L = sequence length, H = heads, G = projection groups
+ * (B, C, Q, E are shared by the H/G consecutive heads of a group; head h reads
+ * group h / (H/G)) [§3 Fig. 2 caption; App. B.2], S = chunk size,
+ * M = ceil(L/S) chunks, N = state size (key axis), P = head dim (value axis).
+ * Tokens and chunks are 0-based: token t lies in chunk t / S.
+ *
+ * Memory layouts (all tensors dense, C order, innermost index last):
+ *   X, Y_ssm, out           [b][L][H][P]      (dtype)
+ *   R (optional)            [b][L][H][P]      float32
+ *   B, C, Q                 [b][L][G][N]      (dtype)
+ *   E                       [b][L][G][P]      (dtype)
+ *   A (decay a_t)           [b][L][H]         float32, values in [0, 1]
+ *   gate                    [b][L][H][P] if gate_per_channel, else [b][L][H]   (dtype)
+ *   lse (optional)          [b][H][L]         float32
+ *   dH (chunk memories)     [b][H][M][P][N]   (dtype)
+ *       dH[b][h][c][p][n] holds entry (n, p) of the paper's N x P matrix
+ *       dH_[c]: each memory is stored with its key axis N innermost.
+ *
+ * Ownership and execution:
+ *   - Every data pointer is a device pointer on the current HIP device; the
+ *     caller owns every buffer.  The library never allocates, frees or
+ *     synchronises.
+ *   - Every call validates its arguments on the host before any HIP call,
+ *     then enqueues its kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream) and returns without waiting.
+ *   - Inputs are read only.  Outputs (including the optional R and lse) are
+ *     fully overwritten.  `out` may alias `Y_ssm` (same pointer, same layout);
+ *     no other aliasing is allowed.
+ *   - Every pointer must be 16-byte aligned.
+ *
+ * Errors:
+ *   - Calls return DART_OK (0) or a negative dart_status_t.  On failure the
+ *     call launches nothing (argument errors) or stops at the failed launch
+ *     (DART_ERR_HIP), and dart_last_error() returns a message for this
+ *     thread's last failing call.
+ *   - Faults inside a kernel surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.  The library keeps no global
+ *     state beyond thread-local error text and path selection, so calls from
+ *     several threads are safe.
+ *
+ * Supported shapes: dtype float32 or bfloat16 (all arithmetic in float32),
+ * 1 <= N <= 256, 1 <= P <= 256, any S >= 1, any L (L % S != 0 allowed).
+ * bfloat16 with N = 128 and P = 64 runs the MFMA kernels; every other case
+ * runs the general kernels.  b = 0 or L = 0 is a valid empty call.
+ */
+#ifndef DART_H_
+#define DART_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DART_ABI_VERSION 1
+
+typedef enum { DART_F32 = 0, DART_BF16 = 1 } dart_dtype_t;
+
+typedef enum {
+  DART_OK = 0,
+  DART_ERR_NULL = -1,        /* a required pointer is NULL */
+  DART_ERR_SHAPE = -2,       /* a dimension is negative, zero where it must not be, or inconsistent */
+  DART_ERR_UNSUPPORTED = -3, /* dtype or (N, P) outside the supported set */
+  DART_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  DART_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+  DART_ERR_ALIGN = -6        /* a pointer is not 16-byte aligned */
+} dart_status_t;
+
+typedef struct {
+  int64_t batch;   /* b */
+  int64_t seqlen;  /* L */
+  int64_t nheads;  /* H */
+  int64_t ngroups; /* G, divides H */
+  int64_t d_state; /* N */
+  int64_t d_head;  /* P */
+  int64_t chunk;   /* S */
+} dart_dims_t;
+
+/* Kernel selection for this thread: DART_PATH_AUTO picks the MFMA kernels
+ * where supported; DART_PATH_GENERAL forces the general kernels everywhere
+ * (used to cross-check the two on the GPU).  Returns the previous value. */
+#define DART_PATH_AUTO 0
+#define DART_PATH_GENERAL 1
+int dart_set_path(int path);
+
+/* Chunk state memories [§3 Eq. 5; App. A Eq. 20]:
+ *   dH_[c] = sum_{s in chunk c} A_{s+1:e(c)} B_s^T X_s,
+ *   A_{s+1:e(c)} = prod_{k=s+1}^{e(c)} a_k  (1 for the chunk's last token),
+ * where e(c) is the last token actually in chunk c (a partial last chunk
+ * decays to token L-1).  Accumulates in float32 and rounds once to dtype.
+ *   X [b][L][H][P], B [b][L][G][N], A [b][L][H] -> dH [b][H][M][P][N]. */
+int dart_chunk_states(const dart_dims_t* dims, int dtype, const void* X, const void* B,
+                      const float* A, void* dH, void* stream);
+
+/* State-memory attention with the gated residual [§3 Eq. 8-11; §4 Algorithm 1]:
+ * for every token t and every chunk c < chunk(t)
+ *   V = C_t dH_c,  K = dH_c E_t,  l = Q_t K / sqrt(N),
+ *   R_t = sum_c softmax_c(l) V  (R_t = 0 when chunk(t) = 0),
+ *   lse_t = log sum_c exp(l)    (-inf when chunk(t) = 0),
+ *   out_t = Y_ssm_t + g_t * R_t, g given after its activation.
+ * R and lse are optional outputs (NULL skips them).  out is rounded once
+ * from float32 to dtype. */
+int dart_sma_fwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
+                 const void* dH, const void* Y_ssm, const void* gate, int gate_per_channel,
+                 void* out, float* R, float* lse, void* stream);
+
+/* SMA for one new token per batch row against a chunk-memory cache
+ * [§4 "Inference Cache"; §3 Eq. 8-11].  Every cached chunk 0..n_b-1 is
+ * visible to the new token.  dims->seqlen and dims->chunk are ignored.
+ *   q, c [b][G][N], e [b][G][P] (dtype)
+ *   cache [b][H][max_chunks][P][N] (dtype; the dH layout above)
+ *   n_chunks [b] int32 on the device, number of valid cached chunks per row,
+ *            clamped to [0, max_chunks]; NULL means max_chunks for every row
+ *   y_ssm, out [b][H][P] (dtype); gate [b][H][P] or [b][H] (dtype)
+ *   R [b][H][P] float32 (optional), lse [b][H] float32 (optional)
+ *   workspace: device scratch of at least dart_sma_decode_workspace_bytes()
+ *              bytes; contents on entry are ignored.
+ * n_b = 0 gives R = 0, lse = -inf, out = y_ssm. */
+int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                    const void* c, const void* e, const void* cache, const int32_t* n_chunks,
+                    const void* y_ssm, const void* gate, int gate_per_channel, void* out,
+                    float* R, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dart_sma_decode needs for these dims and max_chunks
+ * (0 on invalid dims; dtype does not matter). */
+size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chunks);
+
+const char* dart_status_string(int status);
+/* Message for this thread's last failing call ("" if none). */
+const char* dart_last_error(void);
+int dart_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DART_H_ */

@@ -207,13 +207,13 @@ def sma_head(Q, C, E, dH, S: int):
     for i in range(1, M):
         s0, s1 = chunk_bounds(i, L, S)
         hist = dH[:i]                                       # (i, N, P)
-        V = np.einsum("tn,cnp->tcp", C[s0:s1], hist)        # C_t dH_c
-        K = np.einsum("cnp,tp->tcn", hist, E[s0:s1])        # dH_c E_t
+        V = np.einsum("tn,cnp->tcp", C[s0:s1], hist, optimize=True)   # C_t dH_c
+        K = np.einsum("cnp,tp->tcn", hist, E[s0:s1], optimize=True)   # dH_c E_t
         logits = np.einsum("tn,tcn->tc", Q[s0:s1], K) * scale
         m = logits.max(axis=1, keepdims=True)
         p = np.exp(logits - m)
         d = p.sum(axis=1, keepdims=True)
-        R[s0:s1] = np.einsum("tc,tcp->tp", p, V) / d
+        R[s0:s1] = np.einsum("tc,tcp->tp", p, V, optimize=True) / d
         lse[s0:s1] = (m + np.log(d))[:, 0]
     return R, lse
 

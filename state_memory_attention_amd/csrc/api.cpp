@@ -1,0 +1,276 @@
+// C ABI of the DART hot path: argument validation (host only, before any HIP
+// call) and dispatch to the MFMA or general kernels.  See include/dart.h for
+// the contract of every entry point.
+#include "dart.h"
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <initializer_list>
+
+#include "dart_internal.h"
+
+namespace {
+
+thread_local char t_err[512] = "";
+thread_local int t_path = DART_PATH_AUTO;
+
+constexpr int64_t kMaxDim = 256;          // N, P limit of the general kernels
+constexpr int64_t kMaxIndex = INT64_C(1) << 31;  // grid and per-call index limits
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_err, sizeof(t_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Product of the given non-negative factors, or -1 on overflow.
+int64_t prod(std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs)
+    if (!mul_ok(r, x, &r)) return -1;
+  return r;
+}
+
+struct Buf {
+  const void* p;
+  int64_t bytes;
+  const char* name;
+};
+
+int check_ptrs(std::initializer_list<Buf> req) {
+  for (const Buf& b : req) {
+    if (b.p == nullptr) return fail(DART_ERR_NULL, "%s is NULL", b.name);
+    if (((uintptr_t)b.p & 15u) != 0) return fail(DART_ERR_ALIGN, "%s is not 16-byte aligned", b.name);
+  }
+  return DART_OK;
+}
+
+int check_opt_align(const void* p, const char* name) {
+  if (p != nullptr && ((uintptr_t)p & 15u) != 0)
+    return fail(DART_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return DART_OK;
+}
+
+bool overlap(const Buf& a, const Buf& b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + (uintptr_t)a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + (uintptr_t)b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// `outs` must not overlap each other or any of `ins`, except `allowed_alias`
+// (out == Y_ssm, identical pointer).
+int check_alias(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins,
+                const void* alias_out, const void* alias_in) {
+  for (const Buf& o : outs) {
+    for (const Buf& i : ins) {
+      if (o.p == alias_out && i.p == alias_in && o.p == i.p) continue;
+      if (overlap(o, i)) return fail(DART_ERR_SHAPE, "output %s overlaps input %s", o.name, i.name);
+    }
+    for (const Buf& o2 : outs)
+      if (&o2 < &o && overlap(o, o2)) return fail(DART_ERR_SHAPE, "outputs %s and %s overlap", o.name, o2.name);
+  }
+  return DART_OK;
+}
+
+// Common dimension checks.  need_seq: seqlen and chunk are used.
+int check_dims(const dart_dims_t* d, int dtype, bool need_seq) {
+  if (d == nullptr) return fail(DART_ERR_NULL, "dims is NULL");
+  if (dtype != DART_F32 && dtype != DART_BF16)
+    return fail(DART_ERR_UNSUPPORTED, "dtype %d is not DART_F32 or DART_BF16", dtype);
+  if (d->batch < 0) return fail(DART_ERR_SHAPE, "batch = %lld < 0", (long long)d->batch);
+  if (need_seq && d->seqlen < 0) return fail(DART_ERR_SHAPE, "seqlen = %lld < 0", (long long)d->seqlen);
+  if (d->nheads <= 0) return fail(DART_ERR_SHAPE, "nheads = %lld must be > 0", (long long)d->nheads);
+  if (d->ngroups <= 0) return fail(DART_ERR_SHAPE, "ngroups = %lld must be > 0", (long long)d->ngroups);
+  if (d->nheads % d->ngroups != 0)
+    return fail(DART_ERR_SHAPE, "ngroups = %lld does not divide nheads = %lld", (long long)d->ngroups,
+                (long long)d->nheads);
+  if (d->d_state <= 0) return fail(DART_ERR_SHAPE, "d_state = %lld must be > 0", (long long)d->d_state);
+  if (d->d_head <= 0) return fail(DART_ERR_SHAPE, "d_head = %lld must be > 0", (long long)d->d_head);
+  if (need_seq && d->chunk <= 0) return fail(DART_ERR_SHAPE, "chunk = %lld must be > 0", (long long)d->chunk);
+  if (d->d_state > kMaxDim || d->d_head > kMaxDim)
+    return fail(DART_ERR_UNSUPPORTED, "d_state = %lld, d_head = %lld: both must be <= %lld",
+                (long long)d->d_state, (long long)d->d_head, (long long)kMaxDim);
+  if (need_seq && d->seqlen >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "seqlen = %lld must be < 2^31", (long long)d->seqlen);
+  const int64_t rows = prod({d->batch, need_seq ? d->seqlen : 1, d->nheads, kMaxDim, kMaxDim});
+  if (rows < 0 || rows > INT64_MAX / 16) return fail(DART_ERR_SHAPE, "problem size overflows 64-bit indexing");
+  return DART_OK;
+}
+
+dart::Shape make_shape(const dart_dims_t* d) {
+  dart::Shape s;
+  s.b = d->batch;
+  s.L = d->seqlen;
+  s.H = d->nheads;
+  s.G = d->ngroups;
+  s.N = d->d_state;
+  s.P = d->d_head;
+  // A chunk longer than the sequence behaves as one chunk of length L.
+  s.S = (d->chunk > d->seqlen && d->seqlen > 0) ? d->seqlen : d->chunk;
+  s.M = s.S > 0 ? (s.L + s.S - 1) / s.S : 0;
+  return s;
+}
+
+bool use_mfma(int dtype, const dart_dims_t* d) {
+  return t_path == DART_PATH_AUTO && dtype == DART_BF16 && d->d_state == 128 && d->d_head == 64;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DART_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DART_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dart_abi_version(void) { return DART_ABI_VERSION; }
+
+const char* dart_last_error(void) { return t_err; }
+
+int dart_set_path(int path) {
+  const int prev = t_path;
+  t_path = (path == DART_PATH_GENERAL) ? DART_PATH_GENERAL : DART_PATH_AUTO;
+  return prev;
+}
+
+const char* dart_status_string(int status) {
+  switch (status) {
+    case DART_OK: return "DART_OK";
+    case DART_ERR_NULL: return "DART_ERR_NULL";
+    case DART_ERR_SHAPE: return "DART_ERR_SHAPE";
+    case DART_ERR_UNSUPPORTED: return "DART_ERR_UNSUPPORTED";
+    case DART_ERR_WORKSPACE: return "DART_ERR_WORKSPACE";
+    case DART_ERR_HIP: return "DART_ERR_HIP";
+    case DART_ERR_ALIGN: return "DART_ERR_ALIGN";
+    default: return "DART_ERR_UNKNOWN";
+  }
+}
+
+int dart_chunk_states(const dart_dims_t* dims, int dtype, const void* X, const void* B,
+                      const float* A, void* dH, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const Buf bx{X, prod({s.b, s.L, s.H, s.P}) * es, "X"};
+  const Buf bb{B, prod({s.b, s.L, s.G, s.N}) * es, "B"};
+  const Buf ba{A, prod({s.b, s.L, s.H}) * 4, "A"};
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  if ((st = check_ptrs({bx, bb, ba, bd}))) return st;
+  if ((st = check_alias({bd}, {bx, bb, ba}, nullptr, nullptr))) return st;
+  const int64_t tiles = (s.N * s.P + 255) / 256;
+  if (prod({s.b, s.H, s.M, tiles}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "b * H * M is too large for one launch");
+  hipStream_t strm = (hipStream_t)stream;
+  if (use_mfma(dtype, dims))
+    return hip_status(dart::launch_chunk_states_mfma(s, X, B, A, dH, strm), "dart_chunk_states");
+  return hip_status(dart::launch_chunk_states_general(s, dtype == DART_BF16, X, B, A, dH, strm),
+                    "dart_chunk_states");
+}
+
+int dart_sma_fwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
+                 const void* dH, const void* Y_ssm, const void* gate, int gate_per_channel,
+                 void* out, float* R, float* lse, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const int gpc = gate_per_channel ? 1 : 0;
+  const Buf bq{Q, prod({s.b, s.L, s.G, s.N}) * es, "Q"};
+  const Buf bc{C, prod({s.b, s.L, s.G, s.N}) * es, "C"};
+  const Buf be{E, prod({s.b, s.L, s.G, s.P}) * es, "E"};
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf by{Y_ssm, prod({s.b, s.L, s.H, s.P}) * es, "Y_ssm"};
+  const Buf bg{gate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * es, "gate"};
+  const Buf bo{out, prod({s.b, s.L, s.H, s.P}) * es, "out"};
+  const Buf br{R, prod({s.b, s.L, s.H, s.P}) * 4, "R"};
+  const Buf bl{lse, prod({s.b, s.H, s.L}) * 4, "lse"};
+  if ((st = check_ptrs({bq, bc, be, bd, by, bg, bo}))) return st;
+  if ((st = check_opt_align(R, "R")) || (st = check_opt_align(lse, "lse"))) return st;
+  if ((st = check_alias({bo, br, bl}, {bq, bc, be, bd, by, bg}, out, Y_ssm))) return st;
+  if (prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "b * H * L is too large for one launch");
+  hipStream_t strm = (hipStream_t)stream;
+  if (use_mfma(dtype, dims))
+    return hip_status(dart::launch_sma_fwd_mfma(s, Q, C, E, dH, Y_ssm, gate, gpc, out, R, lse, strm),
+                      "dart_sma_fwd");
+  return hip_status(dart::launch_sma_fwd_general(s, dtype == DART_BF16, Q, C, E, dH, Y_ssm, gate, gpc,
+                                                 out, R, lse, strm),
+                    "dart_sma_fwd");
+}
+
+size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chunks) {
+  if (dims == nullptr || dims->batch < 0 || dims->nheads <= 0 || dims->d_head <= 0 || max_chunks < 0)
+    return 0;
+  if (prod({dims->batch, dims->nheads, max_chunks + 1, dims->d_head + 2}) < 0) return 0;
+  return dart::decode_plan(dims->batch, dims->nheads, dims->d_head, max_chunks).workspace_bytes;
+}
+
+int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                    const void* c, const void* e, const void* cache, const int32_t* n_chunks,
+                    const void* y_ssm, const void* gate, int gate_per_channel, void* out,
+                    float* R, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, false);
+  if (st) return st;
+  if (max_chunks < 0) return fail(DART_ERR_SHAPE, "max_chunks = %lld < 0", (long long)max_chunks);
+  if (max_chunks >= kMaxIndex) return fail(DART_ERR_SHAPE, "max_chunks must be < 2^31");
+  dart::Shape s = make_shape(dims);
+  s.L = 1;
+  s.S = 1;
+  s.M = max_chunks;
+  if (s.b == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const int gpc = gate_per_channel ? 1 : 0;
+  const Buf bq{q, prod({s.b, s.G, s.N}) * es, "q"};
+  const Buf bc{c, prod({s.b, s.G, s.N}) * es, "c"};
+  const Buf be{e, prod({s.b, s.G, s.P}) * es, "e"};
+  const Buf bk{cache, prod({s.b, s.H, max_chunks, s.P, s.N}) * es, "cache"};
+  const Buf by{y_ssm, prod({s.b, s.H, s.P}) * es, "y_ssm"};
+  const Buf bg{gate, prod({s.b, s.H, gpc ? s.P : 1}) * es, "gate"};
+  const Buf bo{out, prod({s.b, s.H, s.P}) * es, "out"};
+  const Buf br{R, prod({s.b, s.H, s.P}) * 4, "R"};
+  const Buf bl{lse, prod({s.b, s.H}) * 4, "lse"};
+  const dart::DecodePlan plan = dart::decode_plan(s.b, s.H, s.P, max_chunks);
+  const Buf bw{workspace, (int64_t)plan.workspace_bytes, "workspace"};
+  if (max_chunks > 0 && cache == nullptr) return fail(DART_ERR_NULL, "cache is NULL");
+  if ((st = check_ptrs({bq, bc, be, by, bg, bo}))) return st;
+  if ((st = check_opt_align(cache, "cache")) || (st = check_opt_align(R, "R")) ||
+      (st = check_opt_align(lse, "lse")) || (st = check_opt_align(n_chunks, "n_chunks")))
+    return st;
+  if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+    return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                plan.workspace_bytes);
+  if ((st = check_opt_align(workspace, "workspace"))) return st;
+  const Buf bn{n_chunks, s.b * 4, "n_chunks"};
+  if ((st = check_alias({bo, br, bl, bw}, {bq, bc, be, bk, by, bg, bn}, out, y_ssm))) return st;
+  if (prod({s.b, s.H, plan.splits}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "b * H is too large for one launch");
+  hipStream_t strm = (hipStream_t)stream;
+  if (use_mfma(dtype, dims))
+    return hip_status(dart::launch_sma_decode_mfma(s, max_chunks, plan, q, c, e, cache, n_chunks, y_ssm,
+                                                   gate, gpc, out, R, lse, (float*)workspace, strm),
+                      "dart_sma_decode");
+  return hip_status(dart::launch_sma_decode_general(s, dtype == DART_BF16, max_chunks, q, c, e, cache,
+                                                    n_chunks, y_ssm, gate, gpc, out, R, lse, strm),
+                    "dart_sma_decode");
+}
+
+}  // extern "C"

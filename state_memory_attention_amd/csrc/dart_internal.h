@@ -1,0 +1,47 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel files.
+// Host-side launchers only; every launcher enqueues on `stream` and returns
+// hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dart {
+
+struct Shape {
+  int64_t b, L, H, G, N, P, S, M;  // M = ceil(L / S)
+};
+
+// ---- general kernels (any N, P <= 256; float32 or bfloat16) ---------------
+hipError_t launch_chunk_states_general(const Shape& s, bool bf16, const void* X, const void* B,
+                                       const float* A, void* dH, hipStream_t st);
+hipError_t launch_sma_fwd_general(const Shape& s, bool bf16, const void* Q, const void* C,
+                                  const void* E, const void* dH, const void* Y, const void* gate,
+                                  int gate_pc, void* out, float* R, float* lse, hipStream_t st);
+hipError_t launch_sma_decode_general(const Shape& s, bool bf16, int64_t max_chunks, const void* q,
+                                     const void* c, const void* e, const void* cache,
+                                     const int32_t* n_chunks, const void* y, const void* gate,
+                                     int gate_pc, void* out, float* R, float* lse, hipStream_t st);
+
+// ---- MFMA kernels (bfloat16, N = 128, P = 64) -----------------------------
+hipError_t launch_chunk_states_mfma(const Shape& s, const void* X, const void* B, const float* A,
+                                    void* dH, hipStream_t st);
+hipError_t launch_sma_fwd_mfma(const Shape& s, const void* Q, const void* C, const void* E,
+                               const void* dH, const void* Y, const void* gate, int gate_pc,
+                               void* out, float* R, float* lse, hipStream_t st);
+
+// Split-chunk decode: per (b, h, split) partial softmax states in the
+// workspace, then a fixed-order combine.
+struct DecodePlan {
+  int64_t splits;           // chunk ranges per (b, h)
+  int64_t chunks_per_split;
+  size_t workspace_bytes;
+};
+DecodePlan decode_plan(int64_t b, int64_t H, int64_t P, int64_t max_chunks);
+hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const DecodePlan& plan,
+                                  const void* q, const void* c, const void* e, const void* cache,
+                                  const int32_t* n_chunks, const void* y, const void* gate,
+                                  int gate_pc, void* out, float* R, float* lse, float* ws,
+                                  hipStream_t st);
+
+}  // namespace dart

@@ -1,0 +1,225 @@
+"""Python binding of the DART C ABI (libdart.so).
+
+Argument marshalling only: shapes and dtypes are read from torch tensors, the
+pointers and torch's current HIP stream are handed to the library, and every
+step of the computation runs in its HIP kernels.  If libdart.so is missing or
+cannot be loaded, every call raises: there is no fallback implementation.
+
+Layouts (see include/dart.h):
+    X, Y, out, R  (b, L, H, P)     B, C, Q  (b, L, G, N)     E  (b, L, G, P)
+    A             (b, L, H) float32            gate (b, L, H, P) or (b, L, H)
+    dH            (b, H, M, P, N)  -- each chunk memory with its N axis innermost
+    lse           (b, H, L) float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdart.so")
+
+DART_F32, DART_BF16 = 0, 1
+DART_PATH_AUTO, DART_PATH_GENERAL = 0, 1
+STATUS = {0: "DART_OK", -1: "DART_ERR_NULL", -2: "DART_ERR_SHAPE", -3: "DART_ERR_UNSUPPORTED",
+          -4: "DART_ERR_WORKSPACE", -5: "DART_ERR_HIP", -6: "DART_ERR_ALIGN"}
+
+ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
+                "dart_sma_decode_workspace_bytes", "dart_status_string", "dart_last_error",
+                "dart_abi_version", "dart_set_path")
+
+
+class DartError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("d_state", ctypes.c_int64), ("d_head", ctypes.c_int64),
+                ("chunk", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdart.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m state_memory_attention_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    dp = ctypes.POINTER(Dims)
+    L.dart_chunk_states.argtypes = [dp, i32, vp, vp, vp, vp, vp]
+    L.dart_chunk_states.restype = i32
+    L.dart_sma_fwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    L.dart_sma_fwd.restype = i32
+    L.dart_sma_decode.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
+    L.dart_sma_decode.restype = i32
+    L.dart_sma_decode_workspace_bytes.argtypes = [dp, i64]
+    L.dart_sma_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.dart_status_string.argtypes = [i32]
+    L.dart_status_string.restype = ctypes.c_char_p
+    L.dart_last_error.argtypes = []
+    L.dart_last_error.restype = ctypes.c_char_p
+    L.dart_abi_version.argtypes = []
+    L.dart_abi_version.restype = i32
+    L.dart_set_path.argtypes = [i32]
+    L.dart_set_path.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DartError(status, lib().dart_last_error().decode())
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return DART_F32
+    if dtype == torch.bfloat16:
+        return DART_BF16
+    raise DartError(-3, f"unsupported dtype {dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    if t.device.type != "cuda":
+        raise DartError(-1, "tensors must live on the GPU")
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        raise DartError(-1, f"{name} is None")
+    if tuple(t.shape) != tuple(shape):
+        raise DartError(-2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise DartError(-3, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise DartError(-2, f"{name} must be contiguous")
+    if t.device != device:
+        raise DartError(-2, f"{name} is on {t.device}, expected {device}")
+
+
+def num_chunks(L: int, S: int) -> int:
+    return -(-L // S)
+
+
+def set_path(path: int) -> int:
+    """Select the kernels for this thread (DART_PATH_AUTO or DART_PATH_GENERAL)."""
+    return lib().dart_set_path(path)
+
+
+def abi_version() -> int:
+    return lib().dart_abi_version()
+
+
+def dart_chunk_states(X: torch.Tensor, B: torch.Tensor, A: torch.Tensor, chunk: int,
+                      dH: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunk state memories dH (b, H, M, P, N) from X (b, L, H, P),
+    B (b, L, G, N) and the float32 decays A (b, L, H)."""
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = X.device, X.dtype
+    _need(B, "B", (b, L, G, N), dt, dev)
+    _need(A, "A", (b, L, H), torch.float32, dev)
+    _need(X, "X", (b, L, H, P), dt, dev)
+    if dH is None:
+        dH = torch.empty((b, H, M, P, N), dtype=dt, device=dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    dims = Dims(b, L, H, G, N, P, chunk)
+    _check(lib().dart_chunk_states(ctypes.byref(dims), _code(dt), _ptr(X), _ptr(B), _ptr(A),
+                                   _ptr(dH), _stream(X)))
+    return dH
+
+
+def dart_sma_fwd(Q: torch.Tensor, C: torch.Tensor, E: torch.Tensor, dH: torch.Tensor,
+                 Y: torch.Tensor, gate: torch.Tensor, chunk: int,
+                 out: Optional[torch.Tensor] = None, R: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, want_R: bool = False,
+                 want_lse: bool = False):
+    """SMA readout and gated residual.  Returns (out, R, lse); R and lse are
+    None unless requested (want_R / want_lse) or passed in."""
+    b, L, G, N = Q.shape
+    H, P = Y.shape[2], Y.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = Q.device, Q.dtype
+    _need(C, "C", (b, L, G, N), dt, dev)
+    _need(E, "E", (b, L, G, P), dt, dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    _need(Y, "Y", (b, L, H, P), dt, dev)
+    gpc = gate.dim() == 4
+    _need(gate, "gate", (b, L, H, P) if gpc else (b, L, H), dt, dev)
+    if out is None:
+        out = torch.empty((b, L, H, P), dtype=dt, device=dev)
+    _need(out, "out", (b, L, H, P), dt, dev)
+    if R is None and want_R:
+        R = torch.empty((b, L, H, P), dtype=torch.float32, device=dev)
+    if R is not None:
+        _need(R, "R", (b, L, H, P), torch.float32, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((b, H, L), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (b, H, L), torch.float32, dev)
+    dims = Dims(b, L, H, G, N, P, chunk)
+    _check(lib().dart_sma_fwd(ctypes.byref(dims), _code(dt), _ptr(Q), _ptr(C), _ptr(E), _ptr(dH),
+                              _ptr(Y), _ptr(gate), int(gpc), _ptr(out), _ptr(R), _ptr(lse),
+                              _stream(Q)))
+    return out, R, lse
+
+
+def decode_workspace_bytes(batch: int, nheads: int, d_head: int, max_chunks: int,
+                           ngroups: int = 1, d_state: int = 1) -> int:
+    dims = Dims(batch, 1, nheads, ngroups, d_state, d_head, 1)
+    return int(lib().dart_sma_decode_workspace_bytes(ctypes.byref(dims), max_chunks))
+
+
+def dart_sma_decode(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: torch.Tensor,
+                    y: torch.Tensor, gate: torch.Tensor, n_chunks: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, R: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    want_R: bool = False, want_lse: bool = False):
+    """Decode one new token per batch row against cache (b, H, Mmax, P, N).
+    Returns (out, R, lse)."""
+    b, G, N = q.shape
+    H, Mx, P = cache.shape[1], cache.shape[2], cache.shape[3]
+    dev, dt = q.device, q.dtype
+    _need(c, "c", (b, G, N), dt, dev)
+    _need(e, "e", (b, G, P), dt, dev)
+    _need(cache, "cache", (b, H, Mx, P, N), dt, dev)
+    _need(y, "y", (b, H, P), dt, dev)
+    gpc = gate.dim() == 3
+    _need(gate, "gate", (b, H, P) if gpc else (b, H), dt, dev)
+    if n_chunks is not None:
+        _need(n_chunks, "n_chunks", (b,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((b, H, P), dtype=dt, device=dev)
+    _need(out, "out", (b, H, P), dt, dev)
+    if R is None and want_R:
+        R = torch.empty((b, H, P), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((b, H), dtype=torch.float32, device=dev)
+    dims = Dims(b, 1, H, G, N, P, 1)
+    need = int(lib().dart_sma_decode_workspace_bytes(ctypes.byref(dims), Mx))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib().dart_sma_decode(ctypes.byref(dims), _code(dt), Mx, _ptr(q), _ptr(c), _ptr(e),
+                                 _ptr(cache), _ptr(n_chunks), _ptr(y), _ptr(gate), int(gpc),
+                                 _ptr(out), _ptr(R), _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, R, lse

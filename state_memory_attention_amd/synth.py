@@ -184,3 +184,13 @@ def draw_decode_torch(batch, nheads, ngroups, max_chunks, d_state, d_head, dtype
     for k in ("q", "c", "e", "y", "gate"):
         out[k] = out[k].to(tdt).contiguous()
     return out
+
+
+def draw_memories(batch, nheads, n_chunks, d_state, d_head, dtype="bf16", std=1.0, seed=0):
+    """Host draw of chunk memories for the forward or decode call alone:
+    i.i.d. N(0, std^2) in the library's storage layout [b][H][M][P][N]
+    (each memory with its N axis innermost), bf16-rounded for bf16."""
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal((batch, nheads, n_chunks, d_head, d_state), dtype=np.float32)
+    m *= np.float32(std)
+    return round_bf16(m) if dtype == "bf16" else m

@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/dart.h, and rejects bad arguments on the host before any
+HIP call (so no error path below touches a device)."""
+import ctypes
+import os
+import re
+import subprocess
+import threading
+
+import pytest
+
+from state_memory_attention_amd import dart as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dart.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(D.LIB_PATH), reason="libdart.so not built")
+
+GiB = 1 << 30
+# fake, 16-byte aligned, widely spaced device addresses: never dereferenced,
+# because every call below fails validation before launching anything
+ADDR = [ctypes.c_void_p((k + 1) << 40) for k in range(16)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dart_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = D.lib()
+    names = declared_functions()
+    assert set(names) == set(D.ENTRY_POINTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (dart_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert D.abi_version() == 1
+    lib = D.lib()
+    for code, name in D.STATUS.items():
+        assert lib.dart_status_string(code).decode() == name
+    assert lib.dart_status_string(-99).decode() == "DART_ERR_UNKNOWN"
+
+
+def dims(b=2, L=512, H=4, G=2, N=128, P=64, S=256):
+    return D.Dims(b, L, H, G, N, P, S)
+
+
+def cs(d, dtype=1, X=ADDR[0], B=ADDR[1], A=ADDR[2], dH=ADDR[3]):
+    return D.lib().dart_chunk_states(None if d is None else ctypes.byref(d), dtype, X, B, A, dH, None)
+
+
+def fwd(d, dtype=1, ptrs=None, gpc=1, R=None, lse=None, out=None):
+    p = list(ADDR[:7]) if ptrs is None else ptrs
+    if out is not None:
+        p[6] = out
+    return D.lib().dart_sma_fwd(ctypes.byref(d), dtype, p[0], p[1], p[2], p[3], p[4], p[5], gpc,
+                                p[6], R, lse, None)
+
+
+def dec(d, max_chunks=8, ws=ADDR[10], ws_bytes=GiB, dtype=1, n_chunks=None, cache=ADDR[3]):
+    return D.lib().dart_sma_decode(ctypes.byref(d), dtype, max_chunks, ADDR[0], ADDR[1], ADDR[2],
+                                   cache, n_chunks, ADDR[4], ADDR[5], 1, ADDR[6], None, None,
+                                   ws, ws_bytes, None)
+
+
+def last():
+    return D.lib().dart_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", -1, -2), ("seqlen", -5, -2), ("nheads", 0, -2), ("ngroups", 0, -2), ("ngroups", 3, -2),
+    ("d_state", 0, -2), ("d_head", -1, -2), ("chunk", 0, -2), ("d_state", 257, -3), ("d_head", 512, -3),
+    ("seqlen", 1 << 31, -2),
+])
+def test_bad_dims(field, value, code):
+    d = dims()
+    setattr(d, field, value)
+    assert cs(d) == code and last() != ""
+    assert fwd(d) == code and last() != ""
+
+
+def test_null_dims_and_bad_dtype():
+    assert cs(None) == -1 and "dims" in last()
+    assert cs(dims(), dtype=2) == -3
+    assert fwd(dims(), dtype=7) == -3
+
+
+def test_null_and_misaligned_pointers():
+    assert cs(dims(), X=None) == -1 and "X" in last()
+    assert cs(dims(), A=None) == -1 and "A" in last()
+    assert cs(dims(), dH=ctypes.c_void_p((5 << 40) + 8)) == -6 and "dH" in last()
+    p = list(ADDR[:7])
+    p[5] = None
+    assert fwd(dims(), ptrs=p) == -1 and "gate" in last()
+    assert fwd(dims(), R=ctypes.c_void_p((9 << 40) + 4)) == -6 and "R" in last()
+
+
+def test_aliasing_rules():
+    d = dims()
+    # out overlapping Q is rejected; out == Y_ssm (index 4) is the allowed alias
+    assert fwd(d, out=ctypes.c_void_p(ADDR[0].value + 64)) == -2 and "overlaps" in last()
+    assert fwd(d, out=ctypes.c_void_p(ADDR[4].value + 64)) == -2
+    assert cs(d, dH=ctypes.c_void_p(ADDR[0].value)) == -2
+
+
+def test_empty_calls_launch_nothing():
+    # b = 0 or L = 0 return OK before touching pointers or the device
+    assert cs(dims(b=0), X=None) == 0
+    assert fwd(dims(L=0)) == 0
+    assert dec(dims(b=0)) == 0
+
+
+def test_decode_validation():
+    d = dims()
+    assert dec(d, max_chunks=-1) == -2
+    need = D.lib().dart_sma_decode_workspace_bytes(ctypes.byref(d), 8)
+    assert need > 0
+    assert dec(d, ws=None) == -4 and "workspace" in last()
+    assert dec(d, ws_bytes=need - 1) == -4
+    assert dec(d, cache=None) == -1 and "cache" in last()
+    assert dec(d, n_chunks=ctypes.c_void_p((11 << 40) + 2)) == -6
+
+
+def test_decode_workspace_size_function():
+    f = D.lib().dart_sma_decode_workspace_bytes
+    d = dims(b=64, H=24)
+    assert f(None, 256) == 0 and f(ctypes.byref(d), -1) == 0
+    sizes = [f(ctypes.byref(d), m) for m in (0, 1, 16, 256)]
+    assert all(s >= 64 * 24 * (64 + 2) * 4 for s in sizes)
+    assert sizes == sorted(sizes)
+
+
+def test_error_text_is_thread_local():
+    assert cs(None) == -1 and last() != ""
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(last()))
+    t.start()
+    t.join()
+    assert seen == [""]
+    # a successful (empty) call clears this thread's message
+    assert cs(dims(b=0)) == 0 and last() == ""
+
+
+def test_path_selection_round_trips():
+    prev = D.set_path(D.DART_PATH_GENERAL)
+    assert D.set_path(D.DART_PATH_AUTO) == D.DART_PATH_GENERAL
+    D.set_path(prev)
