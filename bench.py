@@ -130,6 +130,105 @@ def time_decode(torch, dart, synth, steps=20, warmup=3):
     return res
 
 
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+
+
+def profile_kernels(launches=3):
+    """Program for hardware-counter runs: a plain 1 GiB device copy (whose
+    HBM bytes are known), then `launches` calls of each hot-path kernel on
+    the full-size workloads, synchronised between phases."""
+    import torch
+
+    import state_memory_attention_amd as dart
+    from state_memory_attention_amd import synth
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for ci in (2, 3):
+        cfg = dict(synth.CONFIGS[ci])
+        d = synth.draw_fwd_torch(**cfg, seed=0)
+        dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], cfg["chunk"])
+        for _ in range(launches):
+            dart.dart_chunk_states(d["X"], d["B"], d["A"], cfg["chunk"], dH=dH)
+        torch.cuda.synchronize()
+        out = torch.empty_like(d["Y"])
+        for _ in range(launches):
+            dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], cfg["chunk"], out=out)
+        torch.cuda.synchronize()
+        del d, dH, out
+        torch.cuda.empty_cache()
+    cfg = dict(synth.CONFIGS[4])
+    d = synth.draw_decode_torch(**cfg, seed=0)
+    for _ in range(launches):
+        dart.dart_sma_decode(d["q"], d["c"], d["e"], d["cache"], d["y"], d["gate"])
+    torch.cuda.synchronize()
+    print("profile-kernels done", flush=True)
+
+
+def _read_counter_csv(path, counter):
+    """Per-dispatch values of one counter from rocprofv3's counter_collection
+    CSV: list of (dispatch_id, kernel_name, value) in dispatch order."""
+    import csv
+
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            did = int(r["Dispatch_Id"])
+            name = r["Kernel_Name"]
+            rows.setdefault(did, [name, 0.0])
+            rows[did][1] += float(r["Counter_Value"])
+    return [(k, v[0], v[1]) for k, v in sorted(rows.items())]
+
+
+def summarize_counters(fetch_csv, write_csv, launches=3):
+    """Turn the FETCH_SIZE and WRITE_SIZE runs of ``--profile-kernels`` into
+    HBM bytes per launch of each hot kernel, scaled by the calibration copy,
+    and write profiles/traffic_<kernel>_<workload>.json."""
+    from state_memory_attention_amd import synth
+
+    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+    assert len(fetch) == len(write), (len(fetch), len(write))
+    # dispatch order: fill, copies, (chunk_states x (1 + launches), sma_fwd x launches) x 2
+    # configs, decode.  The calibration copies are the last `launches` dispatches
+    # before the first library kernel.
+    first_lib = next(i for i, (_, n, _) in enumerate(fetch) if "dart" in n)
+    copies = [v for _, n, v in fetch[first_lib - launches:first_lib]]
+    wcopies = [v for _, n, v in write[first_lib - launches:first_lib]]
+    f_scale = COPY_BYTES / (sum(copies) / len(copies) * 1024)   # counters are KiB per dispatch
+    w_scale = COPY_BYTES / (sum(wcopies) / len(wcopies) * 1024)
+
+    def per_kernel(substr, first, count):
+        sel_f = [v for _, n, v in fetch if substr in n][first:first + count]
+        sel_w = [v for _, n, v in write if substr in n][first:first + count]
+        return (sum(sel_f) / len(sel_f) * 1024 * f_scale, sum(sel_w) / len(sel_w) * 1024 * w_scale)
+
+    out = []
+    plan = [("chunk_states", "chunk_states_mfma_kernel", synth.CONFIGS[2]["name"], 1),
+            ("sma_fwd", "sma_fwd_mfma_kernel", synth.CONFIGS[2]["name"], 0),
+            ("chunk_states", "chunk_states_mfma_kernel", synth.CONFIGS[3]["name"], 1 + launches + 1),
+            ("sma_fwd", "sma_fwd_mfma_kernel", synth.CONFIGS[3]["name"], launches),
+            ("decode", "sma_decode_partial_kernel", synth.CONFIGS[4]["name"], 0)]
+    for kernel, sym, workload, first in plan:
+        rd, wr = per_kernel(sym, first, launches)
+        rec = {"kernel": sym, "workload": workload, "source_sha256_16": source_hash(KERNEL_SOURCES[kernel]),
+               "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+               "hbm_bytes_per_launch": rd + wr, "fetch_scale": f_scale, "write_scale": w_scale,
+               "calibration": f"torch copy of {COPY_BYTES} bytes: FETCH_SIZE and WRITE_SIZE (KiB) "
+                              "scaled so that the copy reads and writes exactly its size"}
+        path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        out.append(rec)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,7 +237,17 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="run each hot kernel a few times for a hardware-counter pass, then exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn FETCH_SIZE/WRITE_SIZE runs of --profile-kernels into profiles/traffic_*.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.profile_kernels:
+        profile_kernels()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build runs the "
               "hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)

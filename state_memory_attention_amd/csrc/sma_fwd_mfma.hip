@@ -143,6 +143,10 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   } while (0)
     DART_GLOAD(0);
     DART_LSTORE(0);
+    // Drain every prologue load here: otherwise the waits for the token
+    // operands are placed inside the loop, where they would also wait for
+    // the prefetch of the next chunk memory on every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int j = 0; j < n_hist; ++j) {

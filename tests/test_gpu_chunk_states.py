@@ -113,7 +113,7 @@ def test_full_size_sampled(ci):
 
 
 def test_deterministic():
-    cfg = dict(synth.CONFIGS[1], batch=1, nheads=4)
+    cfg = dict(synth.CONFIGS[1], batch=1, nheads=4, ngroups=4)
     d = synth.draw_fwd(**cfg, seed=9)
     a, b = run_cs(d, cfg), run_cs(d, cfg)
     assert np.array_equal(a, b)
