@@ -8,9 +8,11 @@
 // Work decomposition.  A block owns 128 consecutive tokens of one head
 // (4 waves x 32 tokens) and streams the chunk memories dH_j, j = 0..n-1,
 // where n is the chunk of the tile's last token.  Each dH_j^T (64 x 128 bf16,
-// 16 KB) is staged once per block in LDS (double-buffered, XOR-swizzled
-// 16-byte pieces, so the MFMA operand reads are bank-conflict free) and
-// shared by the four waves.
+// 16 KB) is staged once per block in LDS and shared by the four waves: a ring
+// of 4 buffers filled by direct global->LDS loads three chunks ahead (the
+// memories mostly come from the last-level cache, whose latency one chunk of
+// MFMA work does not cover), with XOR-swizzled 16-byte pieces so the MFMA
+// operand reads are bank-conflict free.
 //
 // Per wave and history chunk, two products on v_mfma_f32_32x32x16_bf16:
 //     W^T = dH_j^T Q_tile^T   (64 x 32)       V^T = dH_j^T C_tile^T   (64 x 32)
@@ -43,7 +45,9 @@ constexpr int kP = 64;
 constexpr int kTile = 128;       // tokens per block
 constexpr int kThreads = 256;    // 4 waves x 32 tokens
 constexpr int kMemBytes = kP * kN * 2;
+constexpr int kRing = 4;         // LDS buffers for chunk memories (3 in flight)
 constexpr float kTau = 8.f;
+static_assert(kRing == 4, "the loop's wait counts assume 3 chunks in flight");
 
 struct FwdArgs {
   const bf16_t* Q;
@@ -67,9 +71,22 @@ __device__ __forceinline__ uint32_t mem_off(int row, int piece) {
   return (uint32_t)(row * 256 + ((piece ^ (row & 15)) << 4));
 }
 
+// One direct global->LDS load: every lane fetches 16 bytes from `src`, and
+// lane l's bytes land at lds + 16 l (the LDS address is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sma_fwd_mfma_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_mem[2][kMemBytes];
+  // 64 KB ring of chunk memories (first used to stage the Q and C tiles) and
+  // 16 KB for the E tile: 80 KB, two blocks per CU.  One LDS object on
+  // purpose: the loop's waits for the in-flight chunk loads are explicit
+  // (below), and with a single object the compiler adds no wait of its own
+  // for them before each read of the ring.
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kRing * kMemBytes + kTile * kP * 2];
+  uint8_t* const s_mem = s_lds;
+  uint8_t* const s_e = s_lds + kRing * kMemBytes;
 
   const int blk = blockIdx.x;
   const int bh = blk % a.BHp;
@@ -78,37 +95,55 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int64_t t0 = (int64_t)tile * kTile;
-  const int64_t t = t0 + wave * 32 + col;
-  const bool tok_ok = t < a.L;
-  const int64_t tc = tok_ok ? t : a.L - 1;
   const int64_t t_last = (t0 + kTile < a.L ? t0 + kTile : a.L) - 1;
-  const int n_hist = (int)(t_last / a.S);             // chunks read by the tile
-  const int my_hist = tok_ok ? (int)(t / a.S) : 0;    // this token sees chunks < my_hist
+  const int n_hist = (int)(t_last / a.S);  // chunks read by the tile
+  // this lane's token t0 + 32 wave + col sees chunks < my_hist
+  const int my_hist = (t0 + wave * 32 + col < a.L) ? (int)((t0 + wave * 32 + col) / a.S) : 0;
 
-  // ---- token operands: Q, C as MFMA B operands (8 n per lane per k-step)
-  const int64_t grow = ((int64_t)b * a.L + tc) * a.G + g;
+  // ---- token operands.  Consecutive tokens are G*N*2 bytes apart, so the
+  // tiles are fetched as whole rows (one direct-to-LDS load = 4 rows of Q or C,
+  // 8 rows of E, all bytes used) and then read from LDS in the MFMA layouts;
+  // reading 16 bytes per token row per instruction instead wastes most of each
+  // memory request.  Each wave stages and reads only its own 32 token rows.
+  // Rows carry the same XOR swizzle as the chunk memories (Q, C: 16 pieces of
+  // 16 B per row; E: 8 pieces) so the operand reads are conflict free.
+  const int64_t row0 = (int64_t)b * a.L;  // token index of this batch row
   bf16x8_t qf[8], cf[8];
-  {
-    const bf16x8_t* qp = (const bf16x8_t*)(a.Q + grow * kN + 8 * half);
-    const bf16x8_t* cp = (const bf16x8_t*)(a.C + grow * kN + 8 * half);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = qp[2 * ks];
-      cf[ks] = cp[2 * ks];
-    }
-  }
-  // E in the accumulator layout: register r of row-block rb holds
-  // p = 32 rb + 8 (r / 4) + 4 half + r % 4.
   float ef[2][16];
   {
-    const bf16_t* ep = a.E + grow * kP + 4 * half;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 32 * wave + 4 * k + (lane >> 4);
+      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
+      const int64_t off = ((row0 + tok) * a.G + g) * kN + (((lane & 15) ^ (r & 15)) << 3);
+      dma16(a.Q + off, s_mem + (32 * wave + 4 * k) * 256);
+      dma16(a.C + off, s_mem + 32768 + (32 * wave + 4 * k) * 256);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 32 * wave + 8 * k + (lane >> 3);
+      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
+      const int64_t off = ((row0 + tok) * a.G + g) * kP + (((lane & 7) ^ (r & 7)) << 3);
+      dma16(a.E + off, s_e + (32 * wave + 8 * k) * 128);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Q, C as MFMA B operands: lane holds token `col`, n = 16 ks + 8 half + 0..7
+    const int r = 32 * wave + col;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
+      qf[ks] = *(const bf16x8_t*)(s_mem + o);
+      cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
+    }
+    // E in the accumulator layout: register r of row-block rb holds
+    // p = 32 rb + 8 (r / 4) + 4 half + r % 4.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const uint2 v = *(const uint2*)(ep + 32 * rb + 8 * gq);
+        const uint2 v = *(const uint2*)(s_e + r * 128 + (((4 * rb + gq) ^ (r & 7)) << 4) + 8 * half);
         ef[rb][4 * gq + 0] = bf16lo(v.x) * a.e_scale;
         ef[rb][4 * gq + 1] = bf16hi(v.x) * a.e_scale;
         ef[rb][4 * gq + 2] = bf16lo(v.y) * a.e_scale;
@@ -121,117 +156,158 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
   float m = -INFINITY, d = 0.f;
 
-  if (n_hist > 0) {
-    const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
-    const int srow = tid >> 4, spiece = tid & 15;  // staging: rows srow + 16 i, piece spiece
-    const uint8_t* src0 = mem_head + spiece * 16 + srow * 256;
-    uint4 st0, st1, st2, st3;  // this thread's four 16-byte pieces of the next memory
-#define DART_GLOAD(j)                                                     \
-  do {                                                                    \
-    const uint8_t* src_ = src0 + (int64_t)(j) * kMemBytes;                \
-    st0 = *(const uint4*)(src_);                                          \
-    st1 = *(const uint4*)(src_ + 16 * 256);                               \
-    st2 = *(const uint4*)(src_ + 32 * 256);                               \
-    st3 = *(const uint4*)(src_ + 48 * 256);                               \
-  } while (0)
-#define DART_LSTORE(buf)                                                  \
-  do {                                                                    \
-    *(uint4*)(s_mem[buf] + mem_off(srow, spiece)) = st0;                  \
-    *(uint4*)(s_mem[buf] + mem_off(srow + 16, spiece)) = st1;             \
-    *(uint4*)(s_mem[buf] + mem_off(srow + 32, spiece)) = st2;             \
-    *(uint4*)(s_mem[buf] + mem_off(srow + 48, spiece)) = st3;             \
-  } while (0)
-    DART_GLOAD(0);
-    DART_LSTORE(0);
-    // Drain every prologue load here: otherwise the waits for the token
-    // operands are placed inside the loop, where they would also wait for
-    // the prefetch of the next chunk memory on every iteration.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // Every wave is done reading its token rows before the ring is refilled.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    for (int j = 0; j < n_hist; ++j) {
-      const int buf = j & 1;
-      const bool more = j + 1 < n_hist;
-      if (more) DART_GLOAD(j + 1);
-
-      f32x16_t w0 = {}, w1 = {}, v0 = {}, v1 = {};
-      const uint8_t* sm = s_mem[buf];
+  // ---- streamed inputs.  Ring slots in order: chunk memories 0..n_hist-1,
+  // then the Y tile, then the per-channel gate tile.  Slot s goes to buffer
+  // s % kRing and costs every wave exactly 4 direct-to-LDS loads, so the waits
+  // below only count slots.  Y and gate thus arrive during the last chunk
+  // iterations, in buffers the chunks no longer need.
+  // A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4 loads of 4
+  // rows); a Y or gate load of wave w writes the wave's own token rows
+  // 32w .. 32w+31 (4 loads of 8 rows of 128 B).  One such load writes 1 KB
+  // contiguously, so the XOR swizzle is applied on the global side: the lane
+  // that fills physical piece f of row r fetches logical piece f ^ (r & 15)
+  // (chunk rows) or f ^ (r & 7) (token rows).
+  const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
+  // lane part of a chunk load: row 16 wave + 4 i + lane/16 (+ 4 rows per i)
+  const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
+  const int n_slots = n_hist + 1 + (a.gate_pc ? 1 : 0);
+  auto issue_mem = [&](int s) {
+    const uint8_t* src = mem_head + (int64_t)s * kMemBytes;
+    uint8_t* dst = s_mem + (s % kRing) * kMemBytes + wave * 16 * 256;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t a0 = *(const bf16x8_t*)(sm + mem_off(col, 2 * ks + half));
-        const bf16x8_t a1 = *(const bf16x8_t*)(sm + mem_off(32 + col, 2 * ks + half));
-        w0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], w0, 0, 0, 0);
-        w1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], w1, 0, 0, 0);
-        v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cf[ks], v0, 0, 0, 0);
-        v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cf[ks], v1, 0, 0, 0);
-      }
-
-      // chunk logit (base 2): this half-wave's 32 p values, then the other half's
-      float part = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        part = fmaf(w0[r], ef[0][r], part);
-        part = fmaf(w1[r], ef[1][r], part);
-      }
-      const float l2 = part + __shfl_xor(part, 32);
-
-      const bool valid = j < my_hist;
-      const float mn = (valid && l2 > m + kTau) ? l2 : m;
-      if (__any(mn != m)) {
-        const float alpha = (mn == m) ? 1.f : fast_exp2(m - mn);
-        d *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          o[0][r] *= alpha;
-          o[1][r] *= alpha;
-        }
-        m = mn;
-      }
-      const float pj = valid ? fast_exp2(l2 - m) : 0.f;
-      d += pj;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        o[0][r] = fmaf(pj, v0[r], o[0][r]);
-        o[1][r] = fmaf(pj, v1[r], o[1][r]);
-      }
-
-      if (more) DART_LSTORE(buf ^ 1);
-      __syncthreads();
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      dma16(src + mem_dma + i * 1024 + (((lane & 15) ^ (row & 15)) << 4), dst + i * 4 * 256);
     }
-#undef DART_GLOAD
-#undef DART_LSTORE
+  };
+  // token rows of this tile past the sequence end re-read the last token
+  const int last_r = (int)(a.L - 1 - t0);
+  auto issue_tok = [&](int s) {
+    const bf16_t* base = (s == n_hist ? a.Y : a.gate) + ((row0 + t0) * a.H + h) * kP;
+    uint8_t* dst = s_mem + (s % kRing) * kMemBytes + wave * 16 * 256;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 32 * wave + 8 * k + (lane >> 3);
+      const int rr = r < last_r ? r : last_r;
+      dma16(base + (uint32_t)(rr * a.H * kP + (((lane & 7) ^ (r & 7)) << 3)), dst + k * 8 * 128);
+    }
+  };
+  auto issue = [&](int s) {
+    if (s < n_hist) issue_mem(s);
+    else issue_tok(s);
+  };
+  for (int s = 0; s < kRing - 1 && s < n_slots; ++s) issue(s);
+
+  for (int j = 0; j < n_hist; ++j) {
+    // Chunk j must have landed in every wave's part, and every wave must be
+    // done with chunk j-1 before its buffer is refilled (by slot j+kRing-1: a
+    // chunk prefetch is issued inside the MFMA burst below so that its issue
+    // cost hides behind queued matrix work).  The only vector-memory operations in flight are
+    // these slot loads, so wait until at most slots j+1 .. j+kRing-2 remain.
+    // (__syncthreads() would wait for all of them.)
+    if (n_slots - 1 - j >= 2)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    if (j + kRing - 1 >= n_hist && j + kRing - 1 < n_slots) issue_tok(j + kRing - 1);
+
+    // The MFMA burst runs at raised wave priority, so that a wave entering
+    // it is not held back by the other block's softmax work on this SIMD.
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t w0 = {}, w1 = {}, v0 = {}, v1 = {};
+    const uint8_t* sm = s_mem + (j % kRing) * kMemBytes;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t a0 = *(const bf16x8_t*)(sm + mem_off(col, 2 * ks + half));
+      const bf16x8_t a1 = *(const bf16x8_t*)(sm + mem_off(32 + col, 2 * ks + half));
+      w0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], w0, 0, 0, 0);
+      w1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], w1, 0, 0, 0);
+      v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cf[ks], v0, 0, 0, 0);
+      v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cf[ks], v1, 0, 0, 0);
+      if (ks == 1 && j + kRing - 1 < n_hist) issue_mem(j + kRing - 1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    // chunk logit (base 2): this half-wave's 32 p values, then the other half's
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part = fmaf(w0[r], ef[0][r], part);
+      part = fmaf(w1[r], ef[1][r], part);
+    }
+    const float l2 = part + __shfl_xor(part, 32);
+
+    const bool valid = j < my_hist;
+    const float mn = (valid && l2 > m + kTau) ? l2 : m;
+    if (__any(mn != m)) {
+      const float alpha = (mn == m) ? 1.f : fast_exp2(m - mn);
+      d *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[0][r] *= alpha;
+        o[1][r] *= alpha;
+      }
+      m = mn;
+    }
+    const float pj = valid ? fast_exp2(l2 - m) : 0.f;
+    d += pj;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o[0][r] = fmaf(pj, v0[r], o[0][r]);
+      o[1][r] = fmaf(pj, v1[r], o[1][r]);
+    }
   }
 
   // ---- epilogue: R = O / d, lse = m + log d, out = Y + g * R  [§3 Eq. 10-11]
-  if (!tok_ok) return;
+  // Each wave reads only the Y / gate rows it loaded itself, so waiting for
+  // its own loads is enough.  `out` goes through this wave's rows of the
+  // (now free) E area and leaves as whole 128-byte rows.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int64_t t = t0 + wave * 32 + col;
+  const bool tok_ok = t < a.L;
+  const int64_t tc = tok_ok ? t : a.L - 1;
   const float inv = d > 0.f ? 1.f / d : 0.f;
-  const int64_t orow = ((int64_t)b * a.L + t) * a.H + h;
-  const bf16_t* yp = a.Y + orow * kP + 4 * half;
-  const bf16_t* gp = a.gate + (a.gate_pc ? orow * kP + 4 * half : orow);
-  bf16_t* op = a.out + orow * kP + 4 * half;
-  float* rp = a.R ? a.R + orow * kP + 4 * half : nullptr;
-  const float gs = a.gate_pc ? 0.f : bf16_to_f32(*gp);
+  const int tr = 32 * wave + col;  // this lane's token row in the tile
+  const uint8_t* ybuf = s_mem + (n_hist % kRing) * kMemBytes;
+  const uint8_t* gbuf = s_mem + ((n_hist + 1) % kRing) * kMemBytes;
+  const int64_t orow = (row0 + tc) * a.H + h;
+  const float gs = a.gate_pc ? 0.f : bf16_to_f32(a.gate[orow]);
+  float* rp = (a.R && tok_ok) ? a.R + orow * kP + 4 * half : nullptr;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int off = 32 * rb + 8 * gq;
+      const uint32_t lo = tr * 128 + (((4 * rb + gq) ^ (tr & 7)) << 4) + 8 * half;
       const float r0 = o[rb][4 * gq + 0] * inv, r1 = o[rb][4 * gq + 1] * inv;
       const float r2 = o[rb][4 * gq + 2] * inv, r3 = o[rb][4 * gq + 3] * inv;
-      const uint2 yv = *(const uint2*)(yp + off);
+      const uint2 yv = *(const uint2*)(ybuf + lo);
       float g0 = gs, g1 = gs, g2 = gs, g3 = gs;
       if (a.gate_pc) {
-        const uint2 gv = *(const uint2*)(gp + off);
+        const uint2 gv = *(const uint2*)(gbuf + lo);
         g0 = bf16lo(gv.x); g1 = bf16hi(gv.x); g2 = bf16lo(gv.y); g3 = bf16hi(gv.y);
       }
       uint2 ov;
       ov.x = pack_bf16x2(fmaf(g0, r0, bf16lo(yv.x)), fmaf(g1, r1, bf16hi(yv.x)));
       ov.y = pack_bf16x2(fmaf(g2, r2, bf16lo(yv.y)), fmaf(g3, r3, bf16hi(yv.y)));
-      *(uint2*)(op + off) = ov;
-      if (rp) *(float4*)(rp + off) = make_float4(r0, r1, r2, r3);
+      *(uint2*)(s_e + lo) = ov;
+      if (rp) *(float4*)(rp + 32 * rb + 8 * gq) = make_float4(r0, r1, r2, r3);
     }
-  if (a.lse && half == 0)
+  if (a.lse && half == 0 && tok_ok)
     a.lse[(int64_t)bh * a.L + t] = d > 0.f ? (m + fast_log2(d)) * kLn2 : -INFINITY;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 32 * wave + 8 * k + (lane >> 3);
+    const int f = lane & 7;
+    if (t0 + r < a.L) {
+      const uint4 v = *(const uint4*)(s_e + r * 128 + ((f ^ (r & 7)) << 4));
+      *(uint4*)(a.out + ((row0 + t0 + r) * a.H + h) * kP + f * 8) = v;
+    }
+  }
 }
 
 }  // namespace
