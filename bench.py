@@ -142,10 +142,15 @@ def profile_kernels(launches=3):
     import state_memory_attention_amd as dart
     from state_memory_attention_amd import synth
 
+    import ctypes
+
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "libdart_probe.so"))
+    probe.dart_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for _ in range(launches):
-        torch.mul(src, 1.0, out=dst)  # a plain elementwise kernel (copy_ would use the runtime blit)
+        assert probe.dart_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, stream) == 0
     torch.cuda.synchronize()
     del src, dst
     for ci in (2, 3):
@@ -195,12 +200,10 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
     fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = _read_counter_csv(write_csv, "WRITE_SIZE")
     assert len(fetch) == len(write), (len(fetch), len(write))
-    # dispatch order: fill, copies, (chunk_states x (1 + launches), sma_fwd x launches) x 2
-    # configs, decode.  The calibration copies are the last `launches` dispatches
-    # before the first library kernel.
-    first_lib = next(i for i, (_, n, _) in enumerate(fetch) if "dart" in n)
-    copies = [v for _, n, v in fetch[first_lib - launches:first_lib]]
-    wcopies = [v for _, n, v in write[first_lib - launches:first_lib]]
+    # the calibration copies: `launches` dispatches of copy16_kernel (1 GiB each way)
+    copies = [v for _, n, v in fetch if "copy16_kernel" in n]
+    wcopies = [v for _, n, v in write if "copy16_kernel" in n]
+    assert len(copies) == launches and len(wcopies) == launches
     f_scale = COPY_BYTES / (sum(copies) / len(copies) * 1024)   # counters are KiB per dispatch
     w_scale = COPY_BYTES / (sum(wcopies) / len(wcopies) * 1024)
 
@@ -220,7 +223,7 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
         rec = {"kernel": sym, "workload": workload, "source_sha256_16": source_hash(KERNEL_SOURCES[kernel]),
                "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
                "hbm_bytes_per_launch": rd + wr, "fetch_scale": f_scale, "write_scale": w_scale,
-               "calibration": f"elementwise copy (torch.mul by 1) of {COPY_BYTES} bytes: FETCH_SIZE and WRITE_SIZE (KiB) "
+               "calibration": f"plain 16-byte-vector copy (libdart_probe.so) of {COPY_BYTES} bytes: FETCH_SIZE and WRITE_SIZE (KiB) "
                               "scaled so that the copy reads and writes exactly its size"}
         path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
         with open(path, "w") as f:

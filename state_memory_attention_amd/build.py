@@ -28,6 +28,10 @@ SOURCES = [
     "sma_fwd_mfma.hip",
     "sma_decode_mfma.hip",
 ]
+# A plain 16-byte-vector copy kernel in its own library, used only to
+# calibrate hardware memory-traffic counters (bench.py --profile-kernels).
+PROBE_SOURCE = "probe_copy.hip"
+PROBE_LIB = os.path.join(PKG, "libdart_probe.so")
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for every HIP source.
@@ -59,18 +63,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + [PROBE_SOURCE]
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB, verbose)
+    _link(objs[-1:], PROBE_LIB, verbose)
     return LIB
 
 
