@@ -102,81 +102,29 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   // this lane's token t0 + 32 wave + col sees chunks < my_hist
   const int my_hist = (t0 + wave * 32 + col < a.L) ? (int)((t0 + wave * 32 + col) / a.S) : 0;
 
-  // ---- token operands.  Consecutive tokens are G*N*2 bytes apart, so the
-  // tiles are fetched as whole rows (one direct-to-LDS load = 4 rows of Q or C,
-  // 8 rows of E, all bytes used) and then read from LDS in the MFMA layouts;
-  // reading 16 bytes per token row per instruction instead wastes most of each
-  // memory request.  Each wave stages and reads only its own 32 token rows.
-  // Rows carry the same XOR swizzle as the chunk memories (Q, C: 16 pieces of
-  // 16 B per row; E: 8 pieces) so the operand reads are conflict free.
-  const int64_t row0 = (int64_t)b * a.L;  // token index of this batch row
-  bf16x8_t qf[8], cf[8];
-  float ef[2][16];
-  {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 32 * wave + 4 * k + (lane >> 4);
-      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
-      const int64_t off = ((row0 + tok) * a.G + g) * kN + (((lane & 15) ^ (r & 15)) << 3);
-      dma16(a.Q + off, s_mem + (32 * wave + 4 * k) * 256);
-      dma16(a.C + off, s_mem + 32768 + (32 * wave + 4 * k) * 256);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = 32 * wave + 8 * k + (lane >> 3);
-      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
-      const int64_t off = ((row0 + tok) * a.G + g) * kP + (((lane & 7) ^ (r & 7)) << 3);
-      dma16(a.E + off, s_e + (32 * wave + 8 * k) * 128);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // Q, C as MFMA B operands: lane holds token `col`, n = 16 ks + 8 half + 0..7
-    const int r = 32 * wave + col;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
-      qf[ks] = *(const bf16x8_t*)(s_mem + o);
-      cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
-    }
-    // E in the accumulator layout: register r of row-block rb holds
-    // p = 32 rb + 8 (r / 4) + 4 half + r % 4.
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const uint2 v = *(const uint2*)(s_e + r * 128 + (((4 * rb + gq) ^ (r & 7)) << 4) + 8 * half);
-        ef[rb][4 * gq + 0] = bf16lo(v.x) * a.e_scale;
-        ef[rb][4 * gq + 1] = bf16hi(v.x) * a.e_scale;
-        ef[rb][4 * gq + 2] = bf16lo(v.y) * a.e_scale;
-        ef[rb][4 * gq + 3] = bf16hi(v.y) * a.e_scale;
-      }
-  }
-
-  float o[2][16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
-  float m = -INFINITY, d = 0.f;
-
-  // Every wave is done reading its token rows before the ring is refilled.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // ---- streamed inputs.  Ring slots in order: chunk memories 0..n_hist-1,
-  // then the Y tile, then the per-channel gate tile.  Slot s goes to buffer
-  // s % kRing and costs every wave exactly 4 direct-to-LDS loads, so the waits
-  // below only count slots.  Y and gate thus arrive during the last chunk
-  // iterations, in buffers the chunks no longer need.
-  // A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4 loads of 4
-  // rows); a Y or gate load of wave w writes the wave's own token rows
+  // ---- streamed inputs.  Slots in order: chunk memories 0..n_hist-1, then
+  // the Y tile, then the per-channel gate tile.  Slot 0 lands in the 16 KB
+  // E/out area while the Q and C tiles are staged in the ring; slot s >= 1
+  // goes to ring buffer (s-1) % kRing.  Every slot costs every wave exactly 4
+  // direct-to-LDS loads, so the waits below only count slots; Y and gate
+  // arrive during the last chunk iterations in buffers the chunks no longer
+  // need.  A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4 loads
+  // of 4 rows); a token-tile load of wave w writes the wave's own token rows
   // 32w .. 32w+31 (4 loads of 8 rows of 128 B).  One such load writes 1 KB
   // contiguously, so the XOR swizzle is applied on the global side: the lane
   // that fills physical piece f of row r fetches logical piece f ^ (r & 15)
-  // (chunk rows) or f ^ (r & 7) (token rows).
+  // (256-byte rows) or f ^ (r & 7) (128-byte rows).
+  const int64_t row0 = (int64_t)b * a.L;  // token index of this batch row
   const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
   // lane part of a chunk load: row 16 wave + 4 i + lane/16 (+ 4 rows per i)
   const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
   const int n_slots = n_hist + 1 + (a.gate_pc ? 1 : 0);
+  auto slot_buf = [&](int s) -> uint8_t* {
+    return s == 0 ? s_e : s_mem + ((s - 1) % kRing) * kMemBytes;
+  };
   auto issue_mem = [&](int s) {
     const uint8_t* src = mem_head + (int64_t)s * kMemBytes;
-    uint8_t* dst = s_mem + (s % kRing) * kMemBytes + wave * 16 * 256;
+    uint8_t* dst = slot_buf(s) + wave * 16 * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * wave + 4 * i + (lane >> 4);
@@ -187,7 +135,7 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   const int last_r = (int)(a.L - 1 - t0);
   auto issue_tok = [&](int s) {
     const bf16_t* base = (s == n_hist ? a.Y : a.gate) + ((row0 + t0) * a.H + h) * kP;
-    uint8_t* dst = s_mem + (s % kRing) * kMemBytes + wave * 16 * 256;
+    uint8_t* dst = slot_buf(s) + wave * 16 * 256;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 32 * wave + 8 * k + (lane >> 3);
@@ -199,19 +147,86 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     if (s < n_hist) issue_mem(s);
     else issue_tok(s);
   };
-  for (int s = 0; s < kRing - 1 && s < n_slots; ++s) issue(s);
+
+  // ---- token operands.  Consecutive tokens are G*N*2 bytes apart, so the Q
+  // and C tiles are fetched as whole rows (one direct-to-LDS load = 4 rows, all
+  // bytes used) and then read from LDS in the MFMA layout, with the 256-byte
+  // row swizzle so the reads are conflict free.  Each wave stages and reads
+  // only its own 32 token rows.  E goes straight to registers, which leaves
+  // the E/out area free for slot 0: the first chunk memory then arrives in the
+  // same memory round trip as the token tiles.
+  bf16x8_t qf[8], cf[8];
+  float ef[2][16];
+  {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 32 * wave + 4 * k + (lane >> 4);
+      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
+      const int64_t off = ((row0 + tok) * a.G + g) * kN + (((lane & 15) ^ (r & 15)) << 3);
+      dma16(a.Q + off, s_mem + (32 * wave + 4 * k) * 256);
+      dma16(a.C + off, s_mem + 32768 + (32 * wave + 4 * k) * 256);
+    }
+    issue(0);
+    // E in the accumulator layout: register r of row-block rb holds
+    // p = 32 rb + 8 (r / 4) + 4 half + r % 4.
+    uint2 ev[2][4];
+    {
+      const int64_t tl = t0 + wave * 32 + col;
+      const bf16_t* ep = a.E + ((row0 + (tl < a.L ? tl : a.L - 1)) * a.G + g) * kP + 4 * half;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) ev[rb][gq] = *(const uint2*)(ep + 32 * rb + 8 * gq);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // The compiler's own wait for the E loads goes here, where every load is
+    // already drained; left to itself it waits before the first use of E in
+    // the loop, and so for the chunk prefetches issued since.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint2 v = ev[rb][gq];
+        asm volatile("" : "+v"(v.x), "+v"(v.y));
+        ef[rb][4 * gq + 0] = bf16lo(v.x) * a.e_scale;
+        ef[rb][4 * gq + 1] = bf16hi(v.x) * a.e_scale;
+        ef[rb][4 * gq + 2] = bf16lo(v.y) * a.e_scale;
+        ef[rb][4 * gq + 3] = bf16hi(v.y) * a.e_scale;
+      }
+    // Q, C as MFMA B operands: lane holds token `col`, n = 16 ks + 8 half + 0..7
+    const int r = 32 * wave + col;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
+      qf[ks] = *(const bf16x8_t*)(s_mem + o);
+      cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
+    }
+  }
+
+  float o[2][16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
+  float m = -INFINITY, d = 0.f;
+
+  // Every wave is done reading its token rows before the ring is refilled,
+  // and slot 0 has landed in every wave's part.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int s = 1; s < kRing - 1 && s < n_slots; ++s) issue(s);
 
   for (int j = 0; j < n_hist; ++j) {
     // Chunk j must have landed in every wave's part, and every wave must be
     // done with chunk j-1 before its buffer is refilled (by slot j+kRing-1: a
     // chunk prefetch is issued inside the MFMA burst below so that its issue
-    // cost hides behind queued matrix work).  The only vector-memory operations in flight are
-    // these slot loads, so wait until at most slots j+1 .. j+kRing-2 remain.
-    // (__syncthreads() would wait for all of them.)
-    if (n_slots - 1 - j >= 2)
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // cost hides behind queued matrix work).  The only vector-memory
+    // operations in flight are these slot loads, so wait until at most slots
+    // j+1 .. j+kRing-2 remain (__syncthreads() would wait for all of them).
+    // Chunk 0 was drained before the barrier above.
+    if (j > 0) {
+      if (n_slots - 1 - j >= 2)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 
     if (j + kRing - 1 >= n_hist && j + kRing - 1 < n_slots) issue_tok(j + kRing - 1);
 
@@ -219,16 +234,31 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     // it is not held back by the other block's softmax work on this SIMD.
     __builtin_amdgcn_s_setprio(1);
     f32x16_t w0 = {}, w1 = {}, v0 = {}, v1 = {};
-    const uint8_t* sm = s_mem + (j % kRing) * kMemBytes;
+    const uint8_t* sm = slot_buf(j);
+    // dH_j^T operands are read one k-step ahead of the MFMAs that use them;
+    // the scheduling barriers after the loop pin that order (left alone, the
+    // scheduler sinks each read to just before its use and the LDS latency
+    // shows up between MFMA groups).
+    bf16x8_t n0 = *(const bf16x8_t*)(sm + mem_off(col, half));
+    bf16x8_t n1 = *(const bf16x8_t*)(sm + mem_off(32 + col, half));
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t a0 = *(const bf16x8_t*)(sm + mem_off(col, 2 * ks + half));
-      const bf16x8_t a1 = *(const bf16x8_t*)(sm + mem_off(32 + col, 2 * ks + half));
+      const bf16x8_t a0 = n0, a1 = n1;
+      if (ks < 7) {
+        n0 = *(const bf16x8_t*)(sm + mem_off(col, 2 * ks + 2 + half));
+        n1 = *(const bf16x8_t*)(sm + mem_off(32 + col, 2 * ks + 2 + half));
+      }
       w0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], w0, 0, 0, 0);
       w1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], w1, 0, 0, 0);
       v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cf[ks], v0, 0, 0, 0);
       v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cf[ks], v1, 0, 0, 0);
       if (ks == 1 && j + kRing - 1 < n_hist) issue_mem(j + kRing - 1);
+    }
+    // burst order: [2 LDS reads for step k+1][4 MFMAs of step k], k = 0..7
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);              // MFMA
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -267,13 +297,16 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   // its own loads is enough.  `out` goes through this wave's rows of the
   // (now free) E area and leaves as whole 128-byte rows.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // with a single chunk no barrier separates its reads of the E/out area from
+  // the out rows written there below
+  if (n_hist == 1) asm volatile("s_barrier" ::: "memory");
   const int64_t t = t0 + wave * 32 + col;
   const bool tok_ok = t < a.L;
   const int64_t tc = tok_ok ? t : a.L - 1;
   const float inv = d > 0.f ? 1.f / d : 0.f;
   const int tr = 32 * wave + col;  // this lane's token row in the tile
-  const uint8_t* ybuf = s_mem + (n_hist % kRing) * kMemBytes;
-  const uint8_t* gbuf = s_mem + ((n_hist + 1) % kRing) * kMemBytes;
+  const uint8_t* ybuf = slot_buf(n_hist);
+  const uint8_t* gbuf = slot_buf(n_hist + 1);
   const int64_t orow = (row0 + tc) * a.H + h;
   const float gs = a.gate_pc ? 0.f : bf16_to_f32(a.gate[orow]);
   float* rp = (a.R && tok_ok) ? a.R + orow * kP + 4 * half : nullptr;
