@@ -77,6 +77,30 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// The same through a buffer resource (bytes [0, nbytes) of `base`; a lane
+// offset past the end reads zeros).  The compiler counts a global-to-LDS load
+// as an access that may still be outstanding on the LDS counter as well, which
+// turns every LDS wait it places while one is in flight into a full drain; the
+// buffer form is counted on the vector-memory counter only.  The loads that
+// stay in flight across the chunk loop use this form.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
+  // word 3: 32-bit data format, the value every gfx9 raw buffer access uses
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           0, 0, 0);
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt
+// in 11:8; a field at its maximum does not wait).  Issued as builtins, not as
+// inline asm, so that the compiler's own wait insertion takes them into account.
+constexpr unsigned kWaitAll = 0x0000;
+constexpr unsigned kWaitVm0 = 0x0f70;
+constexpr unsigned kWaitLgkm0 = 0xc07f;
+constexpr unsigned kWaitVm4Lgkm0 = 0x0074;
+constexpr unsigned kWaitVm8Lgkm0 = 0x0078;
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sma_fwd_mfma_kernel(FwdArgs a) {
   // 64 KB ring of chunk memories (first used to stage the Q and C tiles) and
@@ -123,24 +147,25 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     return s == 0 ? s_e : s_mem + ((s - 1) % kRing) * kMemBytes;
   };
   auto issue_mem = [&](int s) {
-    const uint8_t* src = mem_head + (int64_t)s * kMemBytes;
+    const auto rs = buf_rsrc(mem_head + (int64_t)s * kMemBytes, kMemBytes);
     uint8_t* dst = slot_buf(s) + wave * 16 * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * wave + 4 * i + (lane >> 4);
-      dma16(src + mem_dma + i * 1024 + (((lane & 15) ^ (row & 15)) << 4), dst + i * 4 * 256);
+      buf_dma16(rs, mem_dma + i * 1024 + (((lane & 15) ^ (row & 15)) << 4), dst + i * 4 * 256);
     }
   };
   // token rows of this tile past the sequence end re-read the last token
-  const int last_r = (int)(a.L - 1 - t0);
+  const int last_r = (int)(a.L - 1 - t0 < kTile - 1 ? a.L - 1 - t0 : kTile - 1);
+  const uint32_t tok_bytes = (uint32_t)(last_r * a.H * kP + kP) * 2;
   auto issue_tok = [&](int s) {
-    const bf16_t* base = (s == n_hist ? a.Y : a.gate) + ((row0 + t0) * a.H + h) * kP;
+    const auto rs = buf_rsrc((s == n_hist ? a.Y : a.gate) + ((row0 + t0) * a.H + h) * kP, tok_bytes);
     uint8_t* dst = slot_buf(s) + wave * 16 * 256;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 32 * wave + 8 * k + (lane >> 3);
       const int rr = r < last_r ? r : last_r;
-      dma16(base + (uint32_t)(rr * a.H * kP + (((lane & 7) ^ (r & 7)) << 3)), dst + k * 8 * 128);
+      buf_dma16(rs, (uint32_t)(rr * a.H * kP + (((lane & 7) ^ (r & 7)) << 3)) * 2, dst + k * 8 * 128);
     }
   };
   auto issue = [&](int s) {
@@ -178,10 +203,10 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) ev[rb][gq] = *(const uint2*)(ep + 32 * rb + 8 * gq);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // The compiler's own wait for the E loads goes here, where every load is
-    // already drained; left to itself it waits before the first use of E in
-    // the loop, and so for the chunk prefetches issued since.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    // Pin the E values here, where every load is drained: left to itself the
+    // compiler converts them in the first loop iteration, behind a wait that
+    // also covers the chunk prefetches issued by then.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -210,7 +235,8 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
 
   // Every wave is done reading its token rows before the ring is refilled,
   // and slot 0 has landed in every wave's part.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
   for (int s = 1; s < kRing - 1 && s < n_slots; ++s) issue(s);
 
   for (int j = 0; j < n_hist; ++j) {
@@ -223,9 +249,10 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     // Chunk 0 was drained before the barrier above.
     if (j > 0) {
       if (n_slots - 1 - j >= 2)
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
       else
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
+      __builtin_amdgcn_s_barrier();
     }
 
     if (j + kRing - 1 >= n_hist && j + kRing - 1 < n_slots) issue_tok(j + kRing - 1);
@@ -269,7 +296,10 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
       part = fmaf(w0[r], ef[0][r], part);
       part = fmaf(w1[r], ef[1][r], part);
     }
-    const float l2 = part + __shfl_xor(part, 32);
+    // + the other half-wave's part (lanes l and l ^ 32 swap halves)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                     false, false);
+    const float l2 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 
     const bool valid = j < my_hist;
     const float mn = (valid && l2 > m + kTau) ? l2 : m;
@@ -296,10 +326,10 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   // Each wave reads only the Y / gate rows it loaded itself, so waiting for
   // its own loads is enough.  `out` goes through this wave's rows of the
   // (now free) E area and leaves as whole 128-byte rows.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   // with a single chunk no barrier separates its reads of the E/out area from
   // the out rows written there below
-  if (n_hist == 1) asm volatile("s_barrier" ::: "memory");
+  if (n_hist == 1) __builtin_amdgcn_s_barrier();
   const int64_t t = t0 + wave * 32 + col;
   const bool tok_ok = t < a.L;
   const int64_t tc = tok_ok ? t : a.L - 1;
@@ -331,7 +361,7 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     }
   if (a.lse && half == 0 && tok_ok)
     a.lse[(int64_t)bh * a.L + t] = d > 0.f ? (m + fast_log2(d)) * kLn2 : -INFINITY;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = 32 * wave + 8 * k + (lane >> 3);
