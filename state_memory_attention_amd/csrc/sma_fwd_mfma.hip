@@ -280,6 +280,12 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
       v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cf[ks], v0, 0, 0, 0);
       v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cf[ks], v1, 0, 0, 0);
       if (ks == 1 && j + kRing - 1 < n_hist) issue_mem(j + kRing - 1);
+      // A wave whose burst is under way outranks one about to start its own,
+      // so the two waves sharing a SIMD take the matrix core in turns and
+      // each one's softmax tail overlaps the other's burst (at equal priority
+      // they interleave, finish together and then idle the matrix core
+      // through both tails).
+      if (ks == 0) __builtin_amdgcn_s_setprio(2);
     }
     // burst order: [2 LDS reads for step k+1][4 MFMAs of step k], k = 0..7
 #pragma unroll
