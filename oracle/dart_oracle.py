@@ -31,9 +31,15 @@ design notes):
   * a partial last chunk decays to its own last token (e(c) is the last index
     actually in the chunk) [§3 text under Eq. 5].
 
+  * the backward pass takes the loss gradient of ``out`` (or of R) and the
+    forward's saved lse, and recovers the chunk weights as p = exp(l - lse)
+    [App. C Eq. 33-35]; gradients of projections shared by a group of heads
+    are summed over those heads.
+
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
-against brute force, closed forms, special cases and the paper's printed
-numbers; none is "parity unpinned".
+and ``tests/test_oracle_backward_pins.py`` against brute force, closed forms,
+special cases, central finite differences (the backward) and the paper's
+printed numbers; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -55,6 +61,11 @@ __all__ = [
     "gated_residual",
     "sma_decode",
     "cache_ratio",
+    "sma_head_backward",
+    "sma_backward",
+    "gated_residual_backward",
+    "chunk_states_head_backward",
+    "chunk_states_backward",
 ]
 
 
@@ -268,3 +279,145 @@ def cache_ratio(N: int, S: int) -> float:
     """Chunk-memory cache over the matched token-level KV cache, per head
     [§4 Eq. 14]: (L N P / S) / (2 L P) = N / (2 S)."""
     return N / (2.0 * S)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass.  The paper trains through the SMA branch with recomputation
+# [§4 "Efficient Training"; App. C "Recomputation"]: the forward keeps only R
+# and lse, and the backward recovers the chunk weights from recomputed logits
+# as p = exp(l - lse)  [App. C Eq. 33-35].  The gradients below are the chain
+# rule through the forward definitions, written out term by term.
+# ---------------------------------------------------------------------------
+
+
+def gated_residual_backward(dout, gate, R, gate_per_channel: bool = True):
+    """Gradients of out = Y + g * R  [§3 Eq. 11] for a loss gradient dout:
+    returns (dY, dR, dgate) with dY = dout, dR = g * dout and dgate = dout * R
+    (summed over P for a scalar gate)."""
+    dout, gate, R = _f64(dout), _f64(gate), _f64(R)
+    g = gate if gate_per_channel else gate[..., None]
+    dg = dout * R if gate_per_channel else (dout * R).sum(axis=-1)
+    return dout.copy(), g * dout, dg
+
+
+def sma_head_backward(Q, C, E, dH, S: int, dR, lse=None):
+    """Gradients of the SMA readout of one head  [§3 Eq. 8-10]:
+    Q, C (L, N), E (L, P), dH (M, N, P), dR (L, P) = dLoss/dR
+    ->  dQ (L, N), dC (L, N), dE (L, P), d_dH (M, N, P).
+
+    With l_tc = Q_t dH_c E_t / sqrt(N), p_tc = exp(l_tc - lse_t) the chunk
+    weights [App. C Eq. 35], V_tc = C_t dH_c and R_t = sum_c p_tc V_tc:
+        dV_tc = p_tc dR_t
+        dp_tc = dR_t . V_tc,      dl_tc = p_tc (dp_tc - sum_c' p_tc' dp_tc')
+        dC_t  = sum_c dH_c dV_tc
+        dQ_t  = sum_c dl_tc dH_c E_t / sqrt(N)
+        dE_t  = sum_c dl_tc dH_c^T Q_t / sqrt(N)
+        d dH_c = sum_{t: c < chunk(t)} C_t^T dV_tc + dl_tc Q_t^T E_t / sqrt(N)
+    (sum_c' p_tc' dp_tc' = dR_t . R_t).  ``lse`` defaults to the forward's."""
+    Q, C, E, dH, dR = _f64(Q), _f64(C), _f64(E), _f64(dH), _f64(dR)
+    L, N = Q.shape
+    P = E.shape[1]
+    M = num_chunks(L, S)
+    if lse is None:
+        _, lse = sma_head(Q, C, E, dH, S)
+    lse = _f64(lse)
+    scale = 1.0 / math.sqrt(N)
+    dQ = np.zeros((L, N))
+    dC = np.zeros((L, N))
+    dE = np.zeros((L, P))
+    ddH = np.zeros((M, N, P))
+    for i in range(1, M):
+        s0, s1 = chunk_bounds(i, L, S)
+        hist = dH[:i]                                                       # (i, N, P)
+        V = np.einsum("tn,cnp->tcp", C[s0:s1], hist, optimize=True)          # C_t dH_c
+        K = np.einsum("cnp,tp->tcn", hist, E[s0:s1], optimize=True)          # dH_c E_t
+        logits = np.einsum("tn,tcn->tc", Q[s0:s1], K) * scale                # [Eq. 9]
+        p = np.exp(logits - lse[s0:s1, None])                                # [App. C Eq. 35]
+        g = dR[s0:s1]
+        dp = np.einsum("tp,tcp->tc", g, V)
+        dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dC[s0:s1] = np.einsum("tc,cnp,tp->tn", p, hist, g, optimize=True)
+        dQ[s0:s1] = np.einsum("tc,tcn->tn", dl, K) * scale
+        W = np.einsum("tn,cnp->tcp", Q[s0:s1], hist, optimize=True)          # Q_t dH_c
+        dE[s0:s1] = np.einsum("tc,tcp->tp", dl, W) * scale
+        ddH[:i] += np.einsum("tc,tn,tp->cnp", p, C[s0:s1], g, optimize=True)
+        ddH[:i] += np.einsum("tc,tn,tp->cnp", dl, Q[s0:s1], E[s0:s1], optimize=True) * scale
+    return dQ, dC, dE, ddH
+
+
+def sma_backward(Q, C, E, dH, S: int, dR, lse=None):
+    """Batched sma_head_backward.  Q, C (b, L, G, N), E (b, L, G, P),
+    dH (b, H, M, N, P), dR (b, L, H, P), lse (b, H, L) or None
+    ->  dQ, dC (b, L, G, N), dE (b, L, G, P) (each summed over the heads that
+    share the group), d_dH (b, H, M, N, P)."""
+    Q, C, E, dR = _f64(Q), _f64(C), _f64(E), _f64(dR)
+    b, L, G, N = Q.shape
+    H = dH.shape[1]
+    hpg = H // G
+    dQ, dC, dE = np.zeros_like(Q), np.zeros_like(C), np.zeros_like(E)
+    ddH = np.zeros(dH.shape)
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            q, c, e, dd = sma_head_backward(Q[bi, :, g], C[bi, :, g], E[bi, :, g], dH[bi, h], S,
+                                            dR[bi, :, h], None if lse is None else lse[bi, h])
+            dQ[bi, :, g] += q
+            dC[bi, :, g] += c
+            dE[bi, :, g] += e
+            ddH[bi, h] = dd
+    return dQ, dC, dE, ddH
+
+
+def chunk_states_head_backward(X, B, a, S: int, d_dH):
+    """Gradients of dH_[c] = sum_{s in [c]} w_s B_s^T X_s, w_s = A_{s+1:e(c)}
+    [§3 Eq. 5] for d_dH (M, N, P):  ->  dX (L, P), dB (L, N), da (L,).
+
+        dX_s = w_s B_s d_dH_c,   dB_s = w_s d_dH_c X_s^T,
+        dw_s = B_s d_dH_c X_s^T,
+        da_k = sum_{s<k in [c]} dw_s dw_s/da_k
+             = sum_{s<k} dw_s (prod_{j=s+1}^{k-1} a_j) (prod_{j=k+1}^{e(c)} a_j).
+    The products are formed directly, without dividing by a_k (which may
+    be 0); a chunk's first token gets da = 0 (its decay is not in the chunk's
+    weights)."""
+    X, B, a, d_dH = _f64(X), _f64(B), _f64(a), _f64(d_dH)
+    L, P = X.shape
+    N = B.shape[1]
+    M = num_chunks(L, S)
+    dX = np.zeros((L, P))
+    dB = np.zeros((L, N))
+    da = np.zeros(L)
+    for c in range(M):
+        s0, s1 = chunk_bounds(c, L, S)
+        w = decay_weights(a[s0:s1])
+        G = d_dH[c]                                   # (N, P)
+        BG = B[s0:s1] @ G                             # B_s d_dH_c     (n, P)
+        dX[s0:s1] = w[:, None] * BG
+        dB[s0:s1] = w[:, None] * (X[s0:s1] @ G.T)     # (d_dH_c X_s^T)^T
+        dw = (BG * X[s0:s1]).sum(axis=1)
+        n = s1 - s0
+        for k in range(1, n):
+            # prod_{j=s+1}^{k-1} a_j for s = 0..k-1 (chunk-local indices)
+            inner = np.ones(k)
+            for s in range(k - 2, -1, -1):
+                inner[s] = inner[s + 1] * a[s0 + s + 1]
+            da[s0 + k] = (dw[:k] * inner).sum() * w[k]
+    return dX, dB, da
+
+
+def chunk_states_backward(X, B, A, S: int, d_dH):
+    """Batched chunk_states_head_backward.  X (b, L, H, P), B (b, L, G, N),
+    A (b, L, H), d_dH (b, H, M, N, P)  ->  dX (b, L, H, P), dB (b, L, G, N)
+    (summed over the heads of a group), dA (b, L, H)."""
+    X, B, A = _f64(X), _f64(B), _f64(A)
+    b, L, H, P = X.shape
+    G = B.shape[2]
+    hpg = H // G
+    dX, dB, dA = np.zeros_like(X), np.zeros_like(B), np.zeros_like(A)
+    for bi in range(b):
+        for h in range(H):
+            x, bb, aa = chunk_states_head_backward(X[bi, :, h], B[bi, :, h // hpg], A[bi, :, h], S,
+                                                   d_dH[bi, h])
+            dX[bi, :, h] = x
+            dB[bi, :, h // hpg] += bb
+            dA[bi, :, h] = aa
+    return dX, dB, dA
