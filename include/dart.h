@@ -9,6 +9,8 @@
  *     with the gated residual
  *   - SMA for one new token against   dart_sma_decode     [§4 "Inference Cache"]
  *     a cache of chunk memories
+ *   - gradients of the SMA branch     dart_sma_bwd        [§4 "Efficient Training";
+ *     and of the chunk states         dart_chunk_states_bwd   App. C Eq. 33-35]
  *
  * Notation: b = batch, L = sequence length, H = heads, G = projection groups
  * (B, C, Q, E are shared by the H/G consecutive heads of a group; head h reads
@@ -137,6 +139,43 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
 /* Workspace bytes dart_sma_decode needs for these dims and max_chunks
  * (0 on invalid dims; dtype does not matter). */
 size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chunks);
+
+/* SMA backward with the gated residual [§3 Eq. 8-11 differentiated; §4
+ * "Efficient Training"; App. C "Recomputation", Eq. 33-35].  For the loss
+ * gradient dout of out = Y_ssm + g * R, every logit is recomputed and the
+ * chunk weights are recovered from the forward's lse as p = exp(l - lse):
+ *   dR_t = g_t * dout_t,  D_t = dR_t . R_t,  dl = p (dR_t . V_tc - D_t),
+ *   dQ_t = sum_c dl dH_c E_t / sqrt(N),   dE_t = sum_c dl dH_c^T Q_t / sqrt(N),
+ *   dC_t = sum_c p dH_c dR_t,
+ *   d_dH_c = sum_{t: chunk(t) > c} p C_t^T dR_t + dl Q_t^T E_t / sqrt(N),
+ *   dgate = dout * R (per channel) or sum_p dout * R (one gate per token).
+ * The gradient of Y_ssm is dout itself and is not written.
+ *   Inputs: the forward's Q, C, E, dH, gate (as for dart_sma_fwd), its
+ *           outputs R [b][L][H][P] and lse [b][H][L] (float32), and
+ *           dout [b][L][H][P] (dtype).
+ *   Outputs, float32, fully overwritten: dQ, dC [b][L][G][N] and
+ *           dE [b][L][G][P] (summed over the heads of a group); d_dH in the
+ *           dH layout [b][H][M][P][N] (the last chunk, never read, gets 0);
+ *           dgate shaped like gate (NULL skips it).
+ *   workspace: device scratch of at least dart_sma_bwd_workspace_bytes()
+ *           bytes; contents on entry are ignored. */
+int dart_sma_bwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
+                 const void* dH, const void* gate, int gate_per_channel, const float* R,
+                 const float* lse, const void* dout, float* dQ, float* dC, float* dE, float* d_dH,
+                 float* dgate, void* workspace, size_t workspace_bytes, void* stream);
+size_t dart_sma_bwd_workspace_bytes(const dart_dims_t* dims);
+
+/* Chunk-state backward [§3 Eq. 5 differentiated].  For d_dH (float32, the dH
+ * layout [b][H][M][P][N]) and w_s = A_{s+1:e(c)}:
+ *   dX_s = w_s B_s d_dH_c,   dB_s = w_s d_dH_c X_s^T (summed over the heads
+ *   of a group),   dA_k = sum_{s<k in chunk(k)} (B_s d_dH_c X_s^T) dw_s/da_k,
+ * which is 0 at a chunk's first token.
+ *   Outputs, float32, fully overwritten: dX [b][L][H][P], dB [b][L][G][N],
+ *   dA [b][L][H].  workspace: at least dart_chunk_states_bwd_workspace_bytes(). */
+int dart_chunk_states_bwd(const dart_dims_t* dims, int dtype, const void* X, const void* B,
+                          const float* A, const float* d_dH, float* dX, float* dB, float* dA,
+                          void* workspace, size_t workspace_bytes, void* stream);
+size_t dart_chunk_states_bwd_workspace_bytes(const dart_dims_t* dims);
 
 const char* dart_status_string(int status);
 /* Message for this thread's last failing call ("" if none). */

@@ -273,4 +273,92 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
                     "dart_sma_decode");
 }
 
+size_t dart_sma_bwd_workspace_bytes(const dart_dims_t* dims) {
+  t_err[0] = '\0';
+  if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;
+  const dart::Shape s = make_shape(dims);
+  if (prod({2, s.b, s.H, s.M, s.L}) < 0 || prod({s.b, s.L, s.H, 2 * s.N + s.P}) < 0) return 0;
+  return dart::sma_bwd_workspace_bytes(s);
+}
+
+int dart_sma_bwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
+                 const void* dH, const void* gate, int gate_per_channel, const float* R,
+                 const float* lse, const void* dout, float* dQ, float* dC, float* dE, float* d_dH,
+                 float* dgate, void* workspace, size_t workspace_bytes, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const int gpc = gate_per_channel ? 1 : 0;
+  const Buf bq{Q, prod({s.b, s.L, s.G, s.N}) * es, "Q"};
+  const Buf bc{C, prod({s.b, s.L, s.G, s.N}) * es, "C"};
+  const Buf be{E, prod({s.b, s.L, s.G, s.P}) * es, "E"};
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf bg{gate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * es, "gate"};
+  const Buf br{R, prod({s.b, s.L, s.H, s.P}) * 4, "R"};
+  const Buf bl{lse, prod({s.b, s.H, s.L}) * 4, "lse"};
+  const Buf bo{dout, prod({s.b, s.L, s.H, s.P}) * es, "dout"};
+  const Buf gq{dQ, prod({s.b, s.L, s.G, s.N}) * 4, "dQ"};
+  const Buf gc{dC, prod({s.b, s.L, s.G, s.N}) * 4, "dC"};
+  const Buf ge{dE, prod({s.b, s.L, s.G, s.P}) * 4, "dE"};
+  const Buf gd{d_dH, prod({s.b, s.H, s.M, s.P, s.N}) * 4, "d_dH"};
+  const Buf gg{dgate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * 4, "dgate"};
+  const size_t need = dart::sma_bwd_workspace_bytes(s);
+  const Buf bw{workspace, (int64_t)need, "workspace"};
+  if ((st = check_ptrs({bq, bc, be, bd, bg, br, bl, bo, gq, gc, ge, gd}))) return st;
+  if ((st = check_opt_align(dgate, "dgate"))) return st;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((st = check_opt_align(workspace, "workspace"))) return st;
+  if ((st = check_alias({gq, gc, ge, gd, gg, bw}, {bq, bc, be, bd, bg, br, bl, bo}, nullptr, nullptr)))
+    return st;
+  if (prod({s.b, s.H, s.M, (s.N * s.P + 255) / 256}) >= kMaxIndex || prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "b * H * M or b * H * L is too large for one launch");
+  hipStream_t strm = (hipStream_t)stream;
+  return hip_status(dart::launch_sma_bwd_general(s, dtype == DART_BF16, Q, C, E, dH, gate, gpc, R, lse,
+                                                 dout, dQ, dC, dE, d_dH, dgate, (float*)workspace, strm),
+                    "dart_sma_bwd");
+}
+
+size_t dart_chunk_states_bwd_workspace_bytes(const dart_dims_t* dims) {
+  t_err[0] = '\0';
+  if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;
+  const dart::Shape s = make_shape(dims);
+  if (prod({2, s.b, s.H, s.L}) < 0 || prod({s.b, s.L, s.H, s.N}) < 0) return 0;
+  return dart::chunk_states_bwd_workspace_bytes(s);
+}
+
+int dart_chunk_states_bwd(const dart_dims_t* dims, int dtype, const void* X, const void* B,
+                          const float* A, const float* d_dH, float* dX, float* dB, float* dA,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const Buf bx{X, prod({s.b, s.L, s.H, s.P}) * es, "X"};
+  const Buf bb{B, prod({s.b, s.L, s.G, s.N}) * es, "B"};
+  const Buf ba{A, prod({s.b, s.L, s.H}) * 4, "A"};
+  const Buf bd{d_dH, prod({s.b, s.H, s.M, s.P, s.N}) * 4, "d_dH"};
+  const Buf gx{dX, prod({s.b, s.L, s.H, s.P}) * 4, "dX"};
+  const Buf gb{dB, prod({s.b, s.L, s.G, s.N}) * 4, "dB"};
+  const Buf ga{dA, prod({s.b, s.L, s.H}) * 4, "dA"};
+  const size_t need = dart::chunk_states_bwd_workspace_bytes(s);
+  const Buf bw{workspace, (int64_t)need, "workspace"};
+  if ((st = check_ptrs({bx, bb, ba, bd, gx, gb, ga}))) return st;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((st = check_opt_align(workspace, "workspace"))) return st;
+  if ((st = check_alias({gx, gb, ga, bw}, {bx, bb, ba, bd}, nullptr, nullptr))) return st;
+  if (prod({s.b, s.H, s.M}) >= kMaxIndex || prod({s.b, s.L, s.G, s.N}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "problem is too large for one launch");
+  hipStream_t strm = (hipStream_t)stream;
+  return hip_status(dart::launch_chunk_states_bwd_general(s, dtype == DART_BF16, X, B, A, d_dH, dX, dB,
+                                                          dA, (float*)workspace, strm),
+                    "dart_chunk_states_bwd");
+}
+
 }  // extern "C"

@@ -23,6 +23,18 @@ hipError_t launch_sma_decode_general(const Shape& s, bool bf16, int64_t max_chun
                                      const int32_t* n_chunks, const void* y, const void* gate,
                                      int gate_pc, void* out, float* R, float* lse, hipStream_t st);
 
+// ---- backward, general kernels -------------------------------------------
+size_t sma_bwd_workspace_bytes(const Shape& s);
+hipError_t launch_sma_bwd_general(const Shape& s, bool bf16, const void* Q, const void* C,
+                                  const void* E, const void* dH, const void* gate, int gate_pc,
+                                  const float* R, const float* lse, const void* dout, float* dQ,
+                                  float* dC, float* dE, float* ddH, float* dgate, float* ws,
+                                  hipStream_t st);
+size_t chunk_states_bwd_workspace_bytes(const Shape& s);
+hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, const void* X, const void* B,
+                                           const float* A, const float* ddH, float* dX, float* dB,
+                                           float* dA, float* ws, hipStream_t st);
+
 // ---- MFMA kernels (bfloat16, N = 128, P = 64) -----------------------------
 hipError_t launch_chunk_states_mfma(const Shape& s, const void* X, const void* B, const float* A,
                                     void* dH, hipStream_t st);

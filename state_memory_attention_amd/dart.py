@@ -28,8 +28,9 @@ STATUS = {0: "DART_OK", -1: "DART_ERR_NULL", -2: "DART_ERR_SHAPE", -3: "DART_ERR
           -4: "DART_ERR_WORKSPACE", -5: "DART_ERR_HIP", -6: "DART_ERR_ALIGN"}
 
 ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
-                "dart_sma_decode_workspace_bytes", "dart_status_string", "dart_last_error",
-                "dart_abi_version", "dart_set_path")
+                "dart_sma_decode_workspace_bytes", "dart_sma_bwd", "dart_sma_bwd_workspace_bytes",
+                "dart_chunk_states_bwd", "dart_chunk_states_bwd_workspace_bytes",
+                "dart_status_string", "dart_last_error", "dart_abi_version", "dart_set_path")
 
 
 class DartError(RuntimeError):
@@ -67,6 +68,15 @@ def lib() -> ctypes.CDLL:
     L.dart_sma_decode.restype = i32
     L.dart_sma_decode_workspace_bytes.argtypes = [dp, i64]
     L.dart_sma_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.dart_sma_bwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                               vp, ctypes.c_size_t, vp]
+    L.dart_sma_bwd.restype = i32
+    L.dart_sma_bwd_workspace_bytes.argtypes = [dp]
+    L.dart_sma_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.dart_chunk_states_bwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dart_chunk_states_bwd.restype = i32
+    L.dart_chunk_states_bwd_workspace_bytes.argtypes = [dp]
+    L.dart_chunk_states_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.dart_status_string.argtypes = [i32]
     L.dart_status_string.restype = ctypes.c_char_p
     L.dart_last_error.argtypes = []
@@ -223,3 +233,70 @@ def dart_sma_decode(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: to
                                  _ptr(out), _ptr(R), _ptr(lse), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
     return out, R, lse
+
+
+def _workspace(need: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def dart_sma_bwd(Q: torch.Tensor, C: torch.Tensor, E: torch.Tensor, dH: torch.Tensor,
+                 gate: torch.Tensor, R: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                 chunk: int, want_dgate: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Gradients of out = Y + gate * R(Q, C, E, dH) for dout (b, L, H, P),
+    from the forward's R and lse.  Returns float32 (dQ, dC, dE, d_dH, dgate);
+    dQ, dC, dE are summed over the heads of a group, d_dH has the dH layout
+    (b, H, M, P, N), dgate is None unless want_dgate.  The gradient of Y is
+    dout itself."""
+    b, L, G, N = Q.shape
+    H, P = dout.shape[2], dout.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = Q.device, Q.dtype
+    f32 = torch.float32
+    _need(C, "C", (b, L, G, N), dt, dev)
+    _need(E, "E", (b, L, G, P), dt, dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    gpc = gate.dim() == 4
+    _need(gate, "gate", (b, L, H, P) if gpc else (b, L, H), dt, dev)
+    _need(R, "R", (b, L, H, P), f32, dev)
+    _need(lse, "lse", (b, H, L), f32, dev)
+    _need(dout, "dout", (b, L, H, P), dt, dev)
+    dQ = torch.empty((b, L, G, N), dtype=f32, device=dev)
+    dC = torch.empty((b, L, G, N), dtype=f32, device=dev)
+    dE = torch.empty((b, L, G, P), dtype=f32, device=dev)
+    ddH = torch.empty((b, H, M, P, N), dtype=f32, device=dev)
+    dgate = torch.empty(gate.shape, dtype=f32, device=dev) if want_dgate else None
+    dims = Dims(b, L, H, G, N, P, chunk)
+    need = int(lib().dart_sma_bwd_workspace_bytes(ctypes.byref(dims)))
+    workspace = _workspace(need, dev, workspace)
+    _check(lib().dart_sma_bwd(ctypes.byref(dims), _code(dt), _ptr(Q), _ptr(C), _ptr(E), _ptr(dH),
+                              _ptr(gate), int(gpc), _ptr(R), _ptr(lse), _ptr(dout), _ptr(dQ),
+                              _ptr(dC), _ptr(dE), _ptr(ddH), _ptr(dgate), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(Q)))
+    return dQ, dC, dE, ddH, dgate
+
+
+def dart_chunk_states_bwd(X: torch.Tensor, B: torch.Tensor, A: torch.Tensor, ddH: torch.Tensor,
+                          chunk: int, workspace: Optional[torch.Tensor] = None):
+    """Gradients of dH = chunk_states(X, B, A) for d_dH (b, H, M, P, N)
+    float32.  Returns float32 (dX, dB, dA); dB is summed over the heads of a
+    group."""
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = X.device, X.dtype
+    f32 = torch.float32
+    _need(B, "B", (b, L, G, N), dt, dev)
+    _need(A, "A", (b, L, H), f32, dev)
+    _need(ddH, "d_dH", (b, H, M, P, N), f32, dev)
+    dX = torch.empty((b, L, H, P), dtype=f32, device=dev)
+    dB = torch.empty((b, L, G, N), dtype=f32, device=dev)
+    dA = torch.empty((b, L, H), dtype=f32, device=dev)
+    dims = Dims(b, L, H, G, N, P, chunk)
+    need = int(lib().dart_chunk_states_bwd_workspace_bytes(ctypes.byref(dims)))
+    workspace = _workspace(need, dev, workspace)
+    _check(lib().dart_chunk_states_bwd(ctypes.byref(dims), _code(dt), _ptr(X), _ptr(B), _ptr(A),
+                                       _ptr(ddH), _ptr(dX), _ptr(dB), _ptr(dA), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(X)))
+    return dX, dB, dA

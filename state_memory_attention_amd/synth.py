@@ -194,3 +194,20 @@ def draw_memories(batch, nheads, n_chunks, d_state, d_head, dtype="bf16", std=1.
     m = rng.standard_normal((batch, nheads, n_chunks, d_head, d_state), dtype=np.float32)
     m *= np.float32(std)
     return round_bf16(m) if dtype == "bf16" else m
+
+
+def draw_grad(shape, dtype="bf16", seed=0) -> np.ndarray:
+    """Loss gradient dout ~ N(0, 1) of the given shape (numpy float32,
+    bf16-valued when dtype='bf16'), for the backward pass."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal(shape, dtype=np.float32)
+    return round_bf16(g) if dtype == "bf16" else g
+
+
+def draw_grad_torch(shape, dtype="bf16", seed=0):
+    """GPU draw of a loss gradient of the given shape, N(0, 1)."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    t = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)

@@ -150,3 +150,56 @@ def test_path_selection_round_trips():
     prev = D.set_path(D.DART_PATH_GENERAL)
     assert D.set_path(D.DART_PATH_AUTO) == D.DART_PATH_GENERAL
     D.set_path(prev)
+
+
+def bwd(d, dtype=1, ws=ADDR[15], ws_bytes=1 << 40, dgate=None, over=None):
+    p = list(ADDR[:13])
+    for k, v in (over or {}).items():
+        p[k] = v
+    # Q C E dH gate R lse dout | dQ dC dE d_dH
+    return D.lib().dart_sma_bwd(ctypes.byref(d), dtype, p[0], p[1], p[2], p[3], p[4], 1, p[5], p[6],
+                                p[7], p[8], p[9], p[10], p[11], dgate, ws, ws_bytes, None)
+
+
+def csb(d, dtype=1, ws=ADDR[15], ws_bytes=1 << 40, over=None):
+    p = list(ADDR[:7])
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_chunk_states_bwd(ctypes.byref(d), dtype, p[0], p[1], p[2], p[3], p[4], p[5],
+                                         p[6], ws, ws_bytes, None)
+
+
+def test_backward_validation():
+    d = dims()
+    need = D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(d))
+    b, L, H, G, N, P, S = 2, 512, 4, 2, 128, 64, 256
+    M = 2
+    # (p, dl) per (chunk, token) and head, plus per-head partials (grouped)
+    assert need == 4 * (2 * b * H * M * L + b * L * H * (2 * N + P))
+    assert bwd(d, ws=None) == -4 and "workspace" in last()
+    assert bwd(d, ws_bytes=need - 1) == -4
+    assert bwd(d, over={0: None}) == -1 and "Q" in last()
+    assert bwd(d, over={5: None}) == -1 and "R" in last()
+    assert bwd(d, over={11: None}) == -1 and "d_dH" in last()
+    assert bwd(d, over={8: ctypes.c_void_p(ADDR[8].value + 4)}) == -6
+    assert bwd(d, dgate=ctypes.c_void_p((14 << 40) + 8)) == -6
+    # a gradient overlapping an input
+    assert bwd(d, over={8: ctypes.c_void_p(ADDR[0].value)}) == -2 and "overlaps" in last()
+    assert bwd(dims(L=0)) == 0 and bwd(dims(b=0)) == 0
+    assert bwd(d, dtype=3) == -3
+    # ungrouped heads need no per-head partials
+    d1 = dims(G=4)
+    assert D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(d1)) == 4 * 2 * b * H * M * L
+    assert D.lib().dart_sma_bwd_workspace_bytes(None) == 0
+
+
+def test_chunk_states_backward_validation():
+    d = dims()
+    need = D.lib().dart_chunk_states_bwd_workspace_bytes(ctypes.byref(d))
+    assert need == 4 * (2 * 2 * 4 * 512 + 2 * 512 * 4 * 128)
+    assert csb(d, ws=None) == -4
+    assert csb(d, ws_bytes=need - 1) == -4
+    assert csb(d, over={3: None}) == -1 and "d_dH" in last()
+    assert csb(d, over={6: ctypes.c_void_p(ADDR[6].value + 2)}) == -6
+    assert csb(d, over={4: ctypes.c_void_p(ADDR[1].value)}) == -2
+    assert csb(dims(b=0)) == 0

@@ -1,0 +1,128 @@
+"""GPU parity of dart_sma_bwd and dart_chunk_states_bwd against the fp64
+oracle's backward [§3 Eq. 5, 8-11 differentiated; App. C Eq. 33-35].
+
+* same-input: chunk memories drawn directly; the GPU backward gets the GPU
+  forward's R and lse, the oracle its own; every gradient (dQ, dC, dE, d_dH,
+  dgate) is compared entry by entry;
+* end to end: X, B, A -> chunk states -> forward -> backward -> chunk-state
+  backward on the GPU against the same chain in the oracle (dX, dB, dA too);
+* shapes cover grouped heads (summed gradients), a ragged last chunk, a
+  chunk longer than the sequence, the scalar gate, and fp32 and bf16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import state_memory_attention_amd as dart
+from state_memory_attention_amd import synth
+
+from gpu_helpers import TOL, TOL_SAME_INPUT, dev, err, host, say, to_oracle_mem
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_fwd_bwd(d, mem, cfg, dout, gate_pc):
+    dt = cfg["dtype"]
+    Q, C, E = dev(d["Q"], dt), dev(d["C"], dt), dev(d["E"], dt)
+    Y, g = dev(d["Y"], dt), dev(d["gate"], dt)
+    dH = mem if torch.is_tensor(mem) else dev(mem, dt)
+    _, R, lse = dart.dart_sma_fwd(Q, C, E, dH, Y, g, cfg["chunk"], want_R=True, want_lse=True)
+    go = dev(dout, dt)
+    dQ, dC, dE, ddH, dg = dart.dart_sma_bwd(Q, C, E, dH, g, R, lse, go, cfg["chunk"])
+    torch.cuda.synchronize()
+    return dict(Q=host(dQ), C=host(dC), E=host(dE), dH=host(ddH), gate=host(dg)), ddH
+
+
+def oracle_bwd(d, mem_oracle, cfg, dout, gate_pc):
+    R, lse = O.sma_forward(d["Q"], d["C"], d["E"], mem_oracle, cfg["chunk"])
+    _, dR, dg = O.gated_residual_backward(dout, d["gate"], R, gate_pc)
+    dQ, dC, dE, ddH = O.sma_backward(d["Q"], d["C"], d["E"], mem_oracle, cfg["chunk"], dR, lse)
+    return dict(Q=dQ, C=dC, E=dE, dH=np.swapaxes(ddH, -1, -2), gate=dg)
+
+
+def compare(got, ref, tol, label):
+    errs = {k: err(got[k], ref[k]) for k in ref}
+    say(f"  {label}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert not np.isnan(got[k]).any(), k
+        assert v <= tol, (k, v)
+
+
+CASES = [
+    # fp32, grouped heads, ragged last chunk
+    dict(batch=1, nheads=2, ngroups=1, seqlen=300, chunk=64, d_state=16, d_head=16, dtype="f32"),
+    # bf16 at the MFMA shapes, scalar gate in one case
+    dict(batch=1, nheads=2, ngroups=2, seqlen=700, chunk=128, d_state=128, d_head=64, dtype="bf16"),
+    # odd sizes and a chunk that does not divide L
+    dict(batch=2, nheads=3, ngroups=3, seqlen=97, chunk=20, d_state=40, d_head=24, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+@pytest.mark.parametrize("gate_pc", [True, False])
+def test_sma_bwd_same_input(ci, gate_pc):
+    cfg = CASES[ci]
+    say("sma_bwd same-input", cfg, "gate_pc", gate_pc)
+    d = synth.draw_fwd(**cfg, seed=11, gate_per_channel=gate_pc)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, cfg["d_state"], cfg["d_head"],
+                              cfg["dtype"], std=1.0, seed=12)
+    dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["d_head"]), cfg["dtype"], 13)
+    got, _ = gpu_fwd_bwd(d, mem, cfg, dout, gate_pc)
+    ref = oracle_bwd(d, to_oracle_mem(mem), cfg, dout, gate_pc)
+    compare(got, ref, TOL_SAME_INPUT[cfg["dtype"]], "same-input")
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_backward_end_to_end(ci):
+    cfg = CASES[ci]
+    say("backward end-to-end", cfg)
+    dt = cfg["dtype"]
+    d = synth.draw_fwd(**cfg, seed=21)
+    dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["d_head"]), dt, 22)
+    X, B = dev(d["X"], dt), dev(d["B"], dt)
+    A = dev(d["A"], "f32")
+    dH = dart.dart_chunk_states(X, B, A, cfg["chunk"])
+    got, ddH = gpu_fwd_bwd(d, dH, cfg, dout, True)
+    dX, dB, dA = dart.dart_chunk_states_bwd(X, B, A, ddH, cfg["chunk"])
+    torch.cuda.synchronize()
+    got.update(X=host(dX), B=host(dB), A=host(dA))
+
+    memo = O.chunk_states(d["X"], d["B"], d["A"], cfg["chunk"])
+    ref = oracle_bwd(d, memo, cfg, dout, True)
+    ddH_o = np.swapaxes(ref["dH"], -1, -2)
+    rX, rB, rA = O.chunk_states_backward(d["X"], d["B"], d["A"], cfg["chunk"], ddH_o)
+    ref.update(X=rX, B=rB, A=rA)
+    compare(got, ref, TOL[dt], "end-to-end")
+
+
+def test_chunk_states_bwd_same_input_and_edges():
+    # d_dH given directly: the chunk-state backward alone, fp32, grouped
+    # heads, a chunk longer than the sequence and a zero decay
+    for cfg in (dict(batch=1, nheads=4, ngroups=2, seqlen=70, chunk=32, d_state=24, d_head=12),
+                dict(batch=2, nheads=2, ngroups=2, seqlen=50, chunk=64, d_state=8, d_head=8)):
+        say("chunk_states_bwd same-input", cfg)
+        d = synth.draw_fwd(**cfg, dtype="f32", seed=31)
+        d["A"][0, 5, 0] = 0.0
+        S = min(cfg["chunk"], cfg["seqlen"])
+        M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+        g = synth.draw_memories(cfg["batch"], cfg["nheads"], M, cfg["d_state"], cfg["d_head"], "f32",
+                                seed=32)
+        dX, dB, dA = dart.dart_chunk_states_bwd(dev(d["X"]), dev(d["B"]), dev(d["A"]), dev(g),
+                                                cfg["chunk"])
+        torch.cuda.synchronize()
+        rX, rB, rA = O.chunk_states_backward(d["X"], d["B"], d["A"], S, to_oracle_mem(g))
+        compare(dict(X=host(dX), B=host(dB), A=host(dA)), dict(X=rX, B=rB, A=rA), TOL["f32"], "cs-bwd")
+
+
+def test_bwd_deterministic():
+    cfg = CASES[1]
+    d = synth.draw_fwd(**cfg, seed=41)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, 128, 64, "bf16", seed=42)
+    dout = synth.draw_grad((1, cfg["seqlen"], 2, 64), "bf16", 43)
+    a, _ = gpu_fwd_bwd(d, mem, cfg, dout, True)
+    b, _ = gpu_fwd_bwd(d, mem, cfg, dout, True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
