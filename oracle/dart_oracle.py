@@ -66,6 +66,8 @@ __all__ = [
     "gated_residual_backward",
     "chunk_states_head_backward",
     "chunk_states_backward",
+    "decode_state_update",
+    "decode_stream",
 ]
 
 
@@ -279,6 +281,38 @@ def cache_ratio(N: int, S: int) -> float:
     """Chunk-memory cache over the matched token-level KV cache, per head
     [§4 Eq. 14]: (L N P / S) / (2 L P) = N / (2 S)."""
     return N / (2.0 * S)
+
+
+def decode_state_update(state, x, B_t, a_t, pos: int, S: int):
+    """One decode step of the in-progress chunk memory  [§2 Eq. 2 restricted
+    to the current chunk; App. A Eq. 20; §4 "Inference Cache"]:
+
+        state <- a_t state + B_t^T x_t          (N x P, zero at a chunk's start)
+
+    The token at absolute position ``pos`` closes its chunk when
+    pos % S == S - 1; the closed chunk's memory is then returned and the state
+    restarts from zero.  Returns (new_state, closed_memory_or_None)."""
+    state, x, B_t = _f64(state), _f64(x), _f64(B_t)
+    new = float(a_t) * state + np.outer(B_t, x)
+    if pos % S == S - 1:
+        return np.zeros_like(new), new
+    return new, None
+
+
+def decode_stream(X, B, a, S: int):
+    """Run decode_state_update over a whole sequence of one head:
+    X (L, P), B (L, N), a (L,)  ->  (cache of the closed chunks (L // S, N, P),
+    in-progress state after the last token (N, P))."""
+    X, B, a = _f64(X), _f64(B), _f64(a)
+    L, P = X.shape
+    N = B.shape[1]
+    state = np.zeros((N, P))
+    cache = []
+    for t in range(L):
+        state, closed = decode_state_update(state, X[t], B[t], a[t], t, S)
+        if closed is not None:
+            cache.append(closed)
+    return (np.stack(cache) if cache else np.zeros((0, N, P))), state
 
 
 # ---------------------------------------------------------------------------

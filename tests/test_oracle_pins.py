@@ -304,3 +304,41 @@ def test_cache_ratio_matches_paper():
     chunk_cache = np.zeros((O.num_chunks(L, S), N, P), dtype=np.float16)
     kv_cache = np.zeros((L, 2, P), dtype=np.float16)
     assert chunk_cache.nbytes / kv_cache.nbytes == r
+
+
+# ---- decode-side cache maintenance --------------------------------------------
+
+
+def test_decode_stream_reproduces_chunk_states():
+    """Streaming the in-progress chunk update token by token closes every
+    complete chunk with exactly the Eq. 5 memory, and the state after a
+    partial last chunk is that chunk's Eq. 5 memory too (it decays to its
+    last present token)."""
+    rng = np.random.default_rng(17)
+    for L, S in ((40, 8), (37, 8), (16, 16), (5, 8)):
+        X, B = rng.standard_normal((L, 3)), rng.standard_normal((L, 4))
+        a = np.exp(-rng.uniform(0.0, 1.0, L))
+        cache, state = O.decode_stream(X, B, a, S)
+        ref = O.chunk_states_head(X, B, a, S)
+        assert cache.shape[0] == L // S
+        np.testing.assert_allclose(cache, ref[: L // S], rtol=1e-12, atol=1e-12)
+        if L % S:
+            np.testing.assert_allclose(state, ref[-1], rtol=1e-12, atol=1e-12)
+        else:
+            assert np.abs(state).max() == 0
+
+
+def test_decode_state_matches_step_recurrence_from_chunk_start():
+    """Within a chunk the state is the Eq. 2 recurrence restarted from zero at
+    the chunk's first token."""
+    rng = np.random.default_rng(19)
+    L, S = 29, 10
+    X, B = rng.standard_normal((L, 2)), rng.standard_normal((L, 3))
+    a = np.exp(-rng.uniform(0.0, 2.0, L))
+    state = np.zeros((3, 2))
+    for t in range(L):
+        state, closed = O.decode_state_update(state, X[t], B[t], a[t], t, S)
+        s0 = (t // S) * S
+        want = O.ssm_recurrence(X[s0:t + 1], B[s0:t + 1], a[s0:t + 1])[-1]
+        got = closed if closed is not None else state
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
