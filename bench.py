@@ -125,9 +125,43 @@ def time_decode(torch, dart, synth, steps=20, warmup=3):
     res = {"workload": cfg["name"], "us_per_call": t * 1e6, "bytes_per_call": nbytes,
            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
            "traffic": traffic_record("decode", cfg["name"])}
+    res["state_update"] = time_state_update(torch, dart, synth, cfg, d["cache"], steps, warmup)
     del d, ws, out
     torch.cuda.empty_cache()
     return res
+
+
+def time_state_update(torch, dart, synth, cfg, cache, steps, warmup):
+    """dart_decode_state_update on the decode workload: one token per row
+    absorbed into the float32 in-progress chunk memories (b, H, P, N).  The
+    positions are mid-chunk, so every call reads and writes the whole state
+    and writes no cache row (the per-token steady state; a chunk close writes
+    the dtype row instead of the state, fewer bytes)."""
+    b, H, G, N, P = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["d_state"], cfg["d_head"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    x = torch.randn((b, H, P), generator=gen, device="cuda").to(torch.bfloat16)
+    Bt = (torch.randn((b, G, N), generator=gen, device="cuda") / N ** 0.5).to(torch.bfloat16)
+    a = torch.rand((b, H), generator=gen, device="cuda") * 0.5 + 0.5
+    state = torch.zeros((b, H, P, N), device="cuda")
+    pos = torch.full((b,), 256 * 100 + 7, dtype=torch.int32, device="cuda")
+    nch = torch.zeros((b,), dtype=torch.int32, device="cuda")
+    S = 256
+    for _ in range(warmup):
+        dart.dart_decode_state_update(x, Bt, a, state, pos, cache, S, n_chunks=nch)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        dart.dart_decode_state_update(x, Bt, a, state, pos, cache, S, n_chunks=nch)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = 2 * state.numel() * 4 + (x.numel() + Bt.numel()) * 2 + a.numel() * 4
+    gbs = nbytes / t / 1e9
+    return {"kernel": "dart_decode_state_update", "us_per_call": t * 1e6, "bytes_per_call": nbytes,
+            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
 
 
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written

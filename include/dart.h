@@ -9,6 +9,7 @@
  *     with the gated residual
  *   - SMA for one new token against   dart_sma_decode     [§4 "Inference Cache"]
  *     a cache of chunk memories
+ *   - decode-side cache maintenance   dart_decode_state_update  [§2 Eq. 2; §4]
  *   - gradients of the SMA branch     dart_sma_bwd        [§4 "Efficient Training";
  *     and of the chunk states         dart_chunk_states_bwd   App. C Eq. 33-35]
  *
@@ -40,7 +41,8 @@
  *   - Inputs are read only.  Outputs (including the optional R and lse) are
  *     fully overwritten.  `out` may alias `Y_ssm` (same pointer, same layout);
  *     no other aliasing is allowed.
- *   - Every pointer must be 16-byte aligned.
+ *   - Every pointer must be 16-byte aligned (dart_decode_state_update
+ *     relaxes this for its per-token inputs, see there).
  *
  * Errors:
  *   - Calls return DART_OK (0) or a negative dart_status_t.  On failure the
@@ -139,6 +141,28 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
 /* Workspace bytes dart_sma_decode needs for these dims and max_chunks
  * (0 on invalid dims; dtype does not matter). */
 size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chunks);
+
+/* Decode-side cache maintenance, one new token per batch row [§2 Eq. 2
+ * restricted to the current chunk; §3 Eq. 5 / App. A Eq. 20; §4 "Inference
+ * Cache"].  For the token at absolute position pos[b] (chunk size S =
+ * dims->chunk; dims->seqlen is ignored), every head of row b updates its
+ * in-progress chunk memory
+ *   state <- a * state + B^T x
+ * and, when the token closes its chunk (pos % S == S - 1), writes the state,
+ * rounded to dtype, to cache chunk pos / S and restarts the state from zero.
+ * After the update n_chunks[b] = min((pos + 1) / S, max_chunks): the number of
+ * complete chunks the next token's dart_sma_decode sees.
+ *   x [b][H][P] (dtype)          B [b][G][N] (dtype)          a [b][H] float32
+ *   state [b][H][P][N] float32   in/out; zero before a sequence's first token
+ *   pos [b] int32 (device)       rows with pos < 0 are left untouched
+ *   cache [b][H][max_chunks][P][N] (dtype)   written only at a chunk close;
+ *                                a chunk index >= max_chunks is not written
+ *   n_chunks [b] int32 (device)  written; NULL skips it
+ * Alignment: state and cache 16 bytes; x, B, a, pos and n_chunks only their
+ * element size (per-token slices of larger tensors are accepted). */
+int dart_decode_state_update(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* x,
+                             const void* B, const float* a, float* state, const int32_t* pos,
+                             void* cache, int32_t* n_chunks, void* stream);
 
 /* SMA backward with the gated residual [§3 Eq. 8-11 differentiated; §4
  * "Efficient Training"; App. C "Recomputation", Eq. 33-35].  For the loss

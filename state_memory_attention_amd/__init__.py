@@ -7,6 +7,7 @@ if it is missing: there is no fallback path.
 """
 from .dart import (  # noqa: F401
     DART_BF16, DART_F32, DART_PATH_AUTO, DART_PATH_GENERAL, DartError, abi_version,
-    dart_chunk_states, dart_chunk_states_bwd, dart_sma_bwd, dart_sma_decode, dart_sma_fwd,
+    dart_chunk_states, dart_chunk_states_bwd, dart_decode_state_update, dart_sma_bwd,
+    dart_sma_decode, dart_sma_fwd,
     decode_workspace_bytes, num_chunks, set_path,
 )

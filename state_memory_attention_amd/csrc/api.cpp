@@ -273,6 +273,49 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
                     "dart_sma_decode");
 }
 
+int dart_decode_state_update(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* x,
+                             const void* B, const float* a, float* state, const int32_t* pos,
+                             void* cache, int32_t* n_chunks, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, false);
+  if (st) return st;
+  if (dims->chunk <= 0) return fail(DART_ERR_SHAPE, "chunk = %lld must be > 0", (long long)dims->chunk);
+  if (max_chunks < 0) return fail(DART_ERR_SHAPE, "max_chunks = %lld < 0", (long long)max_chunks);
+  if (max_chunks >= kMaxIndex) return fail(DART_ERR_SHAPE, "max_chunks must be < 2^31");
+  dart::Shape s = make_shape(dims);
+  s.L = 1;
+  s.S = dims->chunk;
+  s.M = max_chunks;
+  if (s.b == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const Buf bx{x, prod({s.b, s.H, s.P}) * es, "x"};
+  const Buf bb{B, prod({s.b, s.G, s.N}) * es, "B"};
+  const Buf ba{a, prod({s.b, s.H}) * 4, "a"};
+  const Buf bs{state, prod({s.b, s.H, s.P, s.N}) * 4, "state"};
+  const Buf bp{pos, s.b * 4, "pos"};
+  const Buf bk{cache, prod({s.b, s.H, max_chunks, s.P, s.N}) * es, "cache"};
+  const Buf bn{n_chunks, s.b * 4, "n_chunks"};
+  // x, B, a, pos are read element by element: per-token slices of larger
+  // tensors are accepted at element alignment; state and cache are accessed
+  // in 16-byte vectors.
+  for (const Buf& e : {bx, bb, ba, bp}) {
+    if (e.p == nullptr) return fail(DART_ERR_NULL, "%s is NULL", e.name);
+    const uintptr_t al = (e.p == x || e.p == B) ? (uintptr_t)es : 4u;
+    if (((uintptr_t)e.p & (al - 1)) != 0)
+      return fail(DART_ERR_ALIGN, "%s is not %d-byte aligned", e.name, (int)al);
+  }
+  if ((st = check_ptrs({bs}))) return st;
+  if (max_chunks > 0 && cache == nullptr) return fail(DART_ERR_NULL, "cache is NULL");
+  if ((st = check_opt_align(cache, "cache"))) return st;
+  if (n_chunks != nullptr && ((uintptr_t)n_chunks & 3u) != 0)
+    return fail(DART_ERR_ALIGN, "n_chunks is not 4-byte aligned");
+  if ((st = check_alias({bs, bk, bn}, {bx, bb, ba, bp}, nullptr, nullptr))) return st;
+  if (prod({s.b, s.H}) >= kMaxIndex) return fail(DART_ERR_SHAPE, "b * H is too large for one launch");
+  return hip_status(dart::launch_decode_update(s, dtype == DART_BF16, max_chunks, x, B, a, state, pos,
+                                               cache, n_chunks, (hipStream_t)stream),
+                    "dart_decode_state_update");
+}
+
 size_t dart_sma_bwd_workspace_bytes(const dart_dims_t* dims) {
   t_err[0] = '\0';
   if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;

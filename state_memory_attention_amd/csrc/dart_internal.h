@@ -23,6 +23,11 @@ hipError_t launch_sma_decode_general(const Shape& s, bool bf16, int64_t max_chun
                                      const int32_t* n_chunks, const void* y, const void* gate,
                                      int gate_pc, void* out, float* R, float* lse, hipStream_t st);
 
+// ---- decode-side cache maintenance (any N, P) -----------------------------
+hipError_t launch_decode_update(const Shape& s, bool bf16, int64_t max_chunks, const void* x,
+                                const void* B, const float* a, float* state, const int32_t* pos,
+                                void* cache, int32_t* n_chunks, hipStream_t st);
+
 // ---- backward, general kernels -------------------------------------------
 size_t sma_bwd_workspace_bytes(const Shape& s);
 hipError_t launch_sma_bwd_general(const Shape& s, bool bf16, const void* Q, const void* C,

@@ -1,0 +1,99 @@
+// Decode-side cache maintenance: the in-progress chunk memory of every
+// (batch row, head) absorbs one new token, and a chunk that the token closes
+// is appended to the chunk-memory cache.
+//
+// Paper: "DART: Decoded Attention over Recurrent States for Efficient
+// Long-Context Sequence Modeling" (arXiv 2608.02032).  The cache holds one
+// memory per complete chunk [§4 "Inference Cache"]; the memory of chunk c is
+// the chunk's zero-initial-state contribution dH_[c] [§3 Eq. 5; App. A
+// Eq. 20], which is the step recurrence of §2 Eq. 2 restarted from zero at
+// the chunk's first token:
+//     state <- a_t state + B_t^T X_t,
+// so after the chunk's last token the state equals dH_[c].
+//
+// Memory bound: the float32 state (N x P per head) is read and written once
+// per token, the dtype cache row is written only when a chunk closes.  One
+// block per (b, h); every thread owns 8 consecutive entries (one 16- or
+// 32-byte vector) of rows p of the [P][N] state at a time.
+#include "dart_internal.h"
+#include "dev_common.h"
+
+namespace dart {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void decode_update_kernel(
+    int64_t H, int64_t G, int N, int P, int64_t S, int64_t max_chunks, const T* __restrict__ x,
+    const T* __restrict__ B, const float* __restrict__ a, float* __restrict__ state,
+    const int32_t* __restrict__ pos, T* __restrict__ cache, int32_t* __restrict__ n_chunks) {
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / H, h = bh % H, g = h / (H / G);
+  const int64_t t = pos[b];
+  if (t < 0) return;  // padding row: untouched
+  const int64_t c = t / S;
+  const bool closes = (t % S) == S - 1;
+  if (h == 0 && threadIdx.x == 0 && n_chunks) {
+    const int64_t done = (t + 1) / S;
+    n_chunks[b] = (int32_t)(done < max_chunks ? done : max_chunks);
+  }
+  const float at = a[bh];
+  const T* xr = x + bh * P;
+  const T* br = B + (b * G + g) * N;
+  float* st = state + bh * (int64_t)P * N;
+  T* dst = (closes && c < max_chunks) ? cache + (bh * max_chunks + c) * (int64_t)P * N : nullptr;
+  const int64_t total = (int64_t)P * N;
+  if ((N & 7) == 0) {
+    // 8 entries of one row per step: state as 2 float4, cache as 8 elements
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < total; i += (int64_t)kThreads * 8) {
+      const int p = (int)(i / N), n = (int)(i % N);
+      const float xp = Elem<T>::ld(xr, p);
+      float4 s0 = *(const float4*)(st + i), s1 = *(const float4*)(st + i + 4);
+      float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = fmaf(at, v[k], Elem<T>::ld(br, n + k) * xp);
+      if (closes) {
+        if (dst)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) Elem<T>::st(dst, i + k, v[k]);
+        *(float4*)(st + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *(float4*)(st + i + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        *(float4*)(st + i) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)(st + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < total; i += kThreads) {
+      const int p = (int)(i / N), n = (int)(i % N);
+      const float v = fmaf(at, st[i], Elem<T>::ld(br, n) * Elem<T>::ld(xr, p));
+      if (closes) {
+        if (dst) Elem<T>::st(dst, i, v);
+        st[i] = 0.f;
+      } else {
+        st[i] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_update(const Shape& s, bool bf16, int64_t max_chunks, const void* x,
+                                const void* B, const float* a, float* state, const int32_t* pos,
+                                void* cache, int32_t* n_chunks, hipStream_t st) {
+  const int64_t blocks = s.b * s.H;
+  if (blocks == 0) return hipSuccess;
+  if (bf16)
+    decode_update_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
+        s.H, s.G, (int)s.N, (int)s.P, s.S, max_chunks, (const bf16_t*)x, (const bf16_t*)B, a, state,
+        pos, (bf16_t*)cache, n_chunks);
+  else
+    decode_update_kernel<float><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
+        s.H, s.G, (int)s.N, (int)s.P, s.S, max_chunks, (const float*)x, (const float*)B, a, state, pos,
+        (float*)cache, n_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace dart

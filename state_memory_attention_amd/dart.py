@@ -30,6 +30,7 @@ STATUS = {0: "DART_OK", -1: "DART_ERR_NULL", -2: "DART_ERR_SHAPE", -3: "DART_ERR
 ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
                 "dart_sma_decode_workspace_bytes", "dart_sma_bwd", "dart_sma_bwd_workspace_bytes",
                 "dart_chunk_states_bwd", "dart_chunk_states_bwd_workspace_bytes",
+                "dart_decode_state_update",
                 "dart_status_string", "dart_last_error", "dart_abi_version", "dart_set_path")
 
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.dart_chunk_states_bwd.restype = i32
     L.dart_chunk_states_bwd_workspace_bytes.argtypes = [dp]
     L.dart_chunk_states_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.dart_decode_state_update.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dart_decode_state_update.restype = i32
     L.dart_status_string.argtypes = [i32]
     L.dart_status_string.restype = ctypes.c_char_p
     L.dart_last_error.argtypes = []
@@ -300,3 +303,28 @@ def dart_chunk_states_bwd(X: torch.Tensor, B: torch.Tensor, A: torch.Tensor, ddH
                                        _ptr(ddH), _ptr(dX), _ptr(dB), _ptr(dA), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(X)))
     return dX, dB, dA
+
+
+def dart_decode_state_update(x: torch.Tensor, B: torch.Tensor, a: torch.Tensor,
+                             state: torch.Tensor, pos: torch.Tensor, cache: torch.Tensor,
+                             chunk: int, n_chunks: Optional[torch.Tensor] = None) -> None:
+    """Absorb one new token per batch row into the in-progress chunk memory
+    state (b, H, P, N) float32; a chunk the token closes is written to cache
+    (b, H, Mmax, P, N).  x (b, H, P), B (b, G, N), a (b, H) float32, pos (b,)
+    int32 absolute token positions; n_chunks (b,) int32 receives the number of
+    complete chunks.  Updates state, cache and n_chunks in place."""
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    Mx = cache.shape[2]
+    dev, dt = x.device, x.dtype
+    _need(B, "B", (b, G, N), dt, dev)
+    _need(a, "a", (b, H), torch.float32, dev)
+    _need(state, "state", (b, H, P, N), torch.float32, dev)
+    _need(pos, "pos", (b,), torch.int32, dev)
+    _need(cache, "cache", (b, H, Mx, P, N), dt, dev)
+    if n_chunks is not None:
+        _need(n_chunks, "n_chunks", (b,), torch.int32, dev)
+    dims = Dims(b, 1, H, G, N, P, chunk)
+    _check(lib().dart_decode_state_update(ctypes.byref(dims), _code(dt), Mx, _ptr(x), _ptr(B),
+                                          _ptr(a), _ptr(state), _ptr(pos), _ptr(cache),
+                                          _ptr(n_chunks), _stream(x)))

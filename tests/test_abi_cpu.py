@@ -203,3 +203,26 @@ def test_chunk_states_backward_validation():
     assert csb(d, over={6: ctypes.c_void_p(ADDR[6].value + 2)}) == -6
     assert csb(d, over={4: ctypes.c_void_p(ADDR[1].value)}) == -2
     assert csb(dims(b=0)) == 0
+
+
+def upd(d, max_chunks=4, dtype=1, over=None):
+    p = [ADDR[0], ADDR[1], ADDR[2], ADDR[3], ADDR[4], ADDR[5], ADDR[6]]  # x B a state pos cache n
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_decode_state_update(ctypes.byref(d), dtype, max_chunks, *p, None)
+
+
+def test_decode_update_validation():
+    d = dims()
+    assert upd(d, over={3: None}) == -1 and "state" in last()
+    assert upd(d, over={4: None}) == -1 and "pos" in last()
+    assert upd(d, over={5: None}) == -1 and "cache" in last()
+    assert upd(d, over={6: ctypes.c_void_p(ADDR[6].value + 2)}) == -6
+    assert upd(d, over={3: ctypes.c_void_p(ADDR[3].value + 4)}) == -6 and "state" in last()
+    assert upd(d, over={2: ctypes.c_void_p(ADDR[2].value + 1)}) == -6 and "a" in last()
+    assert upd(d, over={0: ctypes.c_void_p(ADDR[0].value + 1)}) == -6 and "x" in last()
+    assert upd(d, over={3: ctypes.c_void_p(ADDR[0].value)}) == -2 and "overlaps" in last()
+    assert upd(d, max_chunks=-1) == -2
+    bad = dims(S=0)
+    assert upd(bad) == -2
+    assert upd(dims(b=0)) == 0
