@@ -29,6 +29,7 @@ SOURCES = [
     "sma_decode_mfma.hip",
     "backward_general.hip",
     "decode_update.hip",
+    "sma_bwd_mfma.hip",
 ]
 # A plain 16-byte-vector copy kernel in its own library, used only to
 # calibrate hardware memory-traffic counters (bench.py --profile-kernels).

@@ -123,6 +123,11 @@ dart::Shape make_shape(const dart_dims_t* d) {
   return s;
 }
 
+size_t bwd_workspace(const dart::Shape& s) {
+  const size_t g = dart::sma_bwd_workspace_bytes(s), m = dart::sma_bwd_mfma_workspace_bytes(s);
+  return g > m ? g : m;
+}
+
 bool use_mfma(int dtype, const dart_dims_t* d) {
   return t_path == DART_PATH_AUTO && dtype == DART_BF16 && d->d_state == 128 && d->d_head == 64;
 }
@@ -321,7 +326,7 @@ size_t dart_sma_bwd_workspace_bytes(const dart_dims_t* dims) {
   if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;
   const dart::Shape s = make_shape(dims);
   if (prod({2, s.b, s.H, s.M, s.L}) < 0 || prod({s.b, s.L, s.H, 2 * s.N + s.P}) < 0) return 0;
-  return dart::sma_bwd_workspace_bytes(s);
+  return bwd_workspace(s);
 }
 
 int dart_sma_bwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
@@ -348,7 +353,7 @@ int dart_sma_bwd(const dart_dims_t* dims, int dtype, const void* Q, const void* 
   const Buf ge{dE, prod({s.b, s.L, s.G, s.P}) * 4, "dE"};
   const Buf gd{d_dH, prod({s.b, s.H, s.M, s.P, s.N}) * 4, "d_dH"};
   const Buf gg{dgate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * 4, "dgate"};
-  const size_t need = dart::sma_bwd_workspace_bytes(s);
+  const size_t need = bwd_workspace(s);
   const Buf bw{workspace, (int64_t)need, "workspace"};
   if ((st = check_ptrs({bq, bc, be, bd, bg, br, bl, bo, gq, gc, ge, gd}))) return st;
   if ((st = check_opt_align(dgate, "dgate"))) return st;
@@ -360,6 +365,10 @@ int dart_sma_bwd(const dart_dims_t* dims, int dtype, const void* Q, const void* 
   if (prod({s.b, s.H, s.M, (s.N * s.P + 255) / 256}) >= kMaxIndex || prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "b * H * M or b * H * L is too large for one launch");
   hipStream_t strm = (hipStream_t)stream;
+  if (use_mfma(dtype, dims))
+    return hip_status(dart::launch_sma_bwd_mfma(s, Q, C, E, dH, gate, gpc, R, lse, dout, dQ, dC, dE, d_dH,
+                                                dgate, workspace, strm),
+                      "dart_sma_bwd");
   return hip_status(dart::launch_sma_bwd_general(s, dtype == DART_BF16, Q, C, E, dH, gate, gpc, R, lse,
                                                  dout, dQ, dC, dE, d_dH, dgate, (float*)workspace, strm),
                     "dart_sma_bwd");

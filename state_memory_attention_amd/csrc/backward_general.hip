@@ -305,6 +305,12 @@ inline unsigned grid1(int64_t n) { return (unsigned)((n + kThreads - 1) / kThrea
 
 }  // namespace
 
+hipError_t launch_group_sum(const float* in, float* out, int64_t rows, int64_t G, int64_t hpg,
+                            int64_t K, hipStream_t st) {
+  group_sum_kernel<<<grid1(rows * G * K), dim3(kThreads), 0, st>>>(in, out, rows, G, hpg, K);
+  return hipGetLastError();
+}
+
 size_t sma_bwd_workspace_bytes(const Shape& s) {
   const int64_t pd = 2 * s.b * s.H * s.M * s.L;
   const int64_t heads = (s.H != s.G) ? s.b * s.L * s.H * (2 * s.N + s.P) : 0;

@@ -47,6 +47,26 @@ hipError_t launch_sma_fwd_mfma(const Shape& s, const void* Q, const void* C, con
                                const void* dH, const void* Y, const void* gate, int gate_pc,
                                void* out, float* R, float* lse, hipStream_t st);
 
+// Backward on the matrix core: pass A (recompute, p and dl, dE, dgate, dR),
+// pass BC (dQ, dC), pass D (d_dH); per-head partials summed over groups.
+size_t sma_bwd_mfma_workspace_bytes(const Shape& s);
+hipError_t launch_sma_bwd_a_mfma(const Shape& s, const void* Q, const void* C, const void* E,
+                                 const void* dH, const void* gate, int gate_pc, const void* dout,
+                                 const float* R, const float* lse, float* dE, int dE_heads,
+                                 float* pd, void* dR, float* dgate, hipStream_t st);
+hipError_t launch_sma_bwd_bc_mfma(const Shape& s, const void* E, const void* dR, const void* dH,
+                                  const float* pd, float* dQ, float* dC, int out_heads,
+                                  hipStream_t st);
+hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, const void* C,
+                                 const void* Q, const float* pd, float* ddH, hipStream_t st);
+hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, const void* E,
+                               const void* dH, const void* gate, int gate_pc, const float* R,
+                               const float* lse, const void* dout, float* dQ, float* dC, float* dE,
+                               float* ddH, float* dgate, void* ws, hipStream_t st);
+// out[r][g][k] = sum over the hpg heads of group g of in[r][h][k]
+hipError_t launch_group_sum(const float* in, float* out, int64_t rows, int64_t G, int64_t hpg,
+                            int64_t K, hipStream_t st);
+
 // Split-chunk decode: per (b, h, split) partial softmax states in the
 // workspace, then a fixed-order combine.
 struct DecodePlan {

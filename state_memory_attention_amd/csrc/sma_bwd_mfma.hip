@@ -1,0 +1,825 @@
+// State-memory attention backward on gfx950 MFMA: bfloat16 inputs, N = 128,
+// P = 64, float32 arithmetic and gradients.
+//
+// Paper: "DART: Decoded Attention over Recurrent States for Efficient
+// Long-Context Sequence Modeling" (arXiv 2608.02032).  Training keeps only R
+// and lse from the forward and recomputes every logit; the chunk weights come
+// back as p = exp(l - lse) [§4 "Efficient Training"; App. C "Recomputation",
+// Eq. 33-35].  The chain rule through §3 Eq. 8-11 gives, with dR = g * dout,
+// D_t = dR_t . R_t, W = Q_t dH_c, V = C_t dH_c and dl = p (dR_t . V - D_t):
+//     dE_t = sum_c dl W / sqrt(N)
+//     dQ_t = sum_c dl dH_c E_t / sqrt(N),      dC_t = sum_c p dH_c dR_t
+//     d_dH_c = sum_{t: chunk(t) > c} p C_t^T dR_t + dl Q_t^T E_t / sqrt(N).
+//
+// Three passes, each sized to the register file (two waves per SIMD):
+//   A  token tiles x chunks: recompute W and V on the matrix core exactly as
+//      the forward does, then p, dl (stored per (chunk, token)), dE, dgate
+//      and dR (stored in bfloat16 for pass D);
+//   BC token tiles x chunks: dQ^T += dH_c (E * dl/sqrt(N))^T and
+//      dC^T += dH_c (dR * p)^T, the chunk memory as the A operand read with
+//      the transposing LDS read;
+//   D  chunks x later token tiles: the two token contractions of d_dH, the
+//      per-token weights scaling one operand (the chunk-state kernel's form).
+#include "dart_internal.h"
+#include "dev_common.h"
+#include "lds_dma.h"
+
+namespace dart {
+namespace {
+
+constexpr int kN = 128;
+constexpr int kP = 64;
+constexpr int kTile = 128;       // tokens per block in the token-major passes
+constexpr int kThreads = 256;
+constexpr int kMemBytes = kP * kN * 2;
+constexpr int kRing = 4;         // LDS buffers for chunk memories (3 in flight)
+
+// ---------------------------------------------------------------------------
+// Pass A
+// ---------------------------------------------------------------------------
+
+struct BwdAArgs {
+  const bf16_t* Q;
+  const bf16_t* C;
+  const bf16_t* E;
+  const bf16_t* dH;
+  const bf16_t* gate;
+  const bf16_t* dout;
+  const float* R;
+  const float* lse;
+  float* dE;        // [b][L][dE_heads][P]
+  float* pd;        // [b][H][M][2][L]: row of p then row of dl per chunk
+  bf16_t* dR;       // [b][L][H][P]
+  float* dgate;     // nullable
+  int64_t L;
+  int H, G, hpg, S, M, gate_pc, dE_heads;
+  int BH, BHp, n_tiles;
+  float e_scale;    // log2(e) / sqrt(N)
+  float inv_sqrt_n;
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sma_bwd_a_kernel(BwdAArgs a) {
+  // The forward's LDS plan: a 64 KB ring of chunk memories (first used to
+  // stage the Q and C tiles) and a 16 KB area that takes chunk 0.
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kRing * kMemBytes + kMemBytes];
+  uint8_t* const s_mem = s_lds;
+  uint8_t* const s_e = s_lds + kRing * kMemBytes;
+
+  const int blk = blockIdx.x;
+  const int bh = blk % a.BHp;
+  if (bh >= a.BH) return;
+  const int tile = a.n_tiles - 1 - blk / a.BHp;
+  const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int64_t t0 = (int64_t)tile * kTile;
+  const int64_t t_last = (t0 + kTile < a.L ? t0 + kTile : a.L) - 1;
+  const int n_hist = (int)(t_last / a.S);
+  const int64_t t = t0 + wave * 32 + col;  // this lane's token
+  const bool tok_ok = t < a.L;
+  const int64_t tc = tok_ok ? t : a.L - 1;
+  const int my_hist = tok_ok ? (int)(t / a.S) : 0;
+  const int64_t row0 = (int64_t)b * a.L;
+
+  // chunk slots: chunk 0 in the 16 KB area, chunk s >= 1 in ring buffer
+  // (s - 1) % 4; every wave loads rows 16w .. 16w+15 of each (4 loads).
+  const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
+  const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
+  auto slot_buf = [&](int s) -> uint8_t* { return s == 0 ? s_e : s_mem + ((s - 1) % kRing) * kMemBytes; };
+  auto issue_mem = [&](int s) {
+    const auto rs = buf_rsrc(mem_head + (int64_t)s * kMemBytes, kMemBytes);
+    uint8_t* dst = slot_buf(s) + wave * 16 * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      buf_dma16(rs, mem_dma + i * 1024 + (((lane & 15) ^ (row & 15)) << 4), dst + i * 4 * 256);
+    }
+  };
+
+  // ---- token operands (see the forward kernel): Q, C staged as whole rows;
+  // E and dR kept as bfloat16 pairs in the accumulator layout (register r of
+  // row block rb holds p = 32 rb + 8 (r / 4) + 4 half + r % 4).  dR = g * dout
+  // is rounded to bfloat16 once, and D = dR . R and every dR . V use the
+  // rounded values: the gradients are then exactly those of a dout perturbed
+  // by at most one bfloat16 rounding, with no cancellation error in dp - D.
+  bf16x8_t qf[8], cf[8];
+  uint2 ev[2][4], drv[2][4];
+  float D, lse2;
+  {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 32 * wave + 4 * k + (lane >> 4);
+      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
+      const int64_t off = ((row0 + tok) * a.G + g) * kN + (((lane & 15) ^ (r & 15)) << 3);
+      dma16(a.Q + off, s_mem + (32 * wave + 4 * k) * 256);
+      dma16(a.C + off, s_mem + 32768 + (32 * wave + 4 * k) * 256);
+    }
+    if (n_hist > 0) issue_mem(0);
+    const bf16_t* ep = a.E + ((row0 + tc) * a.G + g) * kP + 4 * half;
+    const int64_t orow = (row0 + tc) * a.H + h;
+    const bf16_t* dop = a.dout + orow * kP + 4 * half;
+    const float* rp = a.R + orow * kP + 4 * half;
+    const float gs = a.gate_pc ? 0.f : bf16_to_f32(a.gate[orow]);
+    float part = 0.f, gpart = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int po = 32 * rb + 8 * gq;
+        ev[rb][gq] = *(const uint2*)(ep + po);
+        const uint2 dv = *(const uint2*)(dop + po);
+        const float4 rv = *(const float4*)(rp + po);
+        float g0 = gs, g1 = gs, g2 = gs, g3 = gs;
+        if (a.gate_pc) {
+          const uint2 gv = *(const uint2*)(a.gate + orow * kP + 4 * half + po);
+          g0 = bf16lo(gv.x); g1 = bf16hi(gv.x); g2 = bf16lo(gv.y); g3 = bf16hi(gv.y);
+        }
+        const float d0 = bf16lo(dv.x), d1 = bf16hi(dv.x), d2 = bf16lo(dv.y), d3 = bf16hi(dv.y);
+        uint2 pk;
+        pk.x = pack_bf16x2(g0 * d0, g1 * d1);
+        pk.y = pack_bf16x2(g2 * d2, g3 * d3);
+        drv[rb][gq] = pk;
+        part = fmaf(bf16lo(pk.x), rv.x, part);
+        part = fmaf(bf16hi(pk.x), rv.y, part);
+        part = fmaf(bf16lo(pk.y), rv.z, part);
+        part = fmaf(bf16hi(pk.y), rv.w, part);
+        if (tok_ok) {
+          // dR for pass D, dgate = dout * R (per channel) [§3 Eq. 11]
+          *(uint2*)(a.dR + orow * kP + 4 * half + po) = pk;
+          if (a.dgate && a.gate_pc)
+            *(float4*)(a.dgate + orow * kP + 4 * half + po) =
+                make_float4(d0 * rv.x, d1 * rv.y, d2 * rv.z, d3 * rv.w);
+        }
+        gpart += d0 * rv.x + d1 * rv.y + d2 * rv.z + d3 * rv.w;
+      }
+    D = halves_sum(part);
+    gpart = halves_sum(gpart);
+    if (a.dgate && !a.gate_pc && half == 0 && tok_ok) a.dgate[orow] = gpart;
+    lse2 = a.lse[(int64_t)bh * a.L + tc] * kLog2e;
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    // keep the E pairs from being waited for inside the loop
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        asm volatile("" : "+v"(ev[rb][gq].x), "+v"(ev[rb][gq].y));
+        asm volatile("" : "+v"(drv[rb][gq].x), "+v"(drv[rb][gq].y));
+      }
+    const int r = 32 * wave + col;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
+      qf[ks] = *(const bf16x8_t*)(s_mem + o);
+      cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
+    }
+  }
+
+  float de[2][16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) de[0][r] = de[1][r] = 0.f;
+
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  for (int s = 1; s < kRing - 1 && s < n_hist; ++s) issue_mem(s);
+
+  // (p, dl) rows of this wave's 32 tokens: a uniform base per chunk plus the lane
+  const int64_t pd_base = (int64_t)bh * a.M * 2 * a.L + t0 + 32 * wave;
+  for (int j = 0; j < n_hist; ++j) {
+    // chunk j landed everywhere, chunk j-1 free (see the forward kernel)
+    if (j > 0) {
+      if (n_hist - 1 - j >= 2)
+        __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
+      else if (n_hist - 1 - j == 1)
+        __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0 & kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t w0 = {}, w1 = {}, v0 = {}, v1 = {};
+    const uint8_t* sm = slot_buf(j);
+    // dH_j^T operands one k-step ahead of their MFMAs (the forward's schedule)
+    bf16x8_t n0 = *(const bf16x8_t*)(sm + mem_off(col, half));
+    bf16x8_t n1 = *(const bf16x8_t*)(sm + mem_off(32 + col, half));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t a0 = n0, a1 = n1;
+      if (ks < 7) {
+        n0 = *(const bf16x8_t*)(sm + mem_off(col, 2 * ks + 2 + half));
+        n1 = *(const bf16x8_t*)(sm + mem_off(32 + col, 2 * ks + 2 + half));
+      }
+      w0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], w0, 0, 0, 0);
+      w1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], w1, 0, 0, 0);
+      v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cf[ks], v0, 0, 0, 0);
+      v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cf[ks], v1, 0, 0, 0);
+      if (ks == 1 && j + kRing - 1 < n_hist) issue_mem(j + kRing - 1);
+      if (ks == 0) __builtin_amdgcn_s_setprio(2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);              // MFMA
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    // logit (base 2) and dR . V, each over this half-wave's 32 p then both.
+    // The bfloat16 pairs are unpacked here, every iteration: the empty asm
+    // keeps the compiler from hoisting 64 unpacked floats out of the loop.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      asm volatile("" : "+v"(ev[rb][0].x), "+v"(ev[rb][0].y), "+v"(ev[rb][1].x), "+v"(ev[rb][1].y),
+                   "+v"(ev[rb][2].x), "+v"(ev[rb][2].y), "+v"(ev[rb][3].x), "+v"(ev[rb][3].y),
+                   "+v"(drv[rb][0].x), "+v"(drv[rb][0].y), "+v"(drv[rb][1].x), "+v"(drv[rb][1].y),
+                   "+v"(drv[rb][2].x), "+v"(drv[rb][2].y), "+v"(drv[rb][3].x), "+v"(drv[rb][3].y));
+    float pl = 0.f, pv = 0.f;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      pl = fmaf(w0[4 * gq + 0], bf16lo(ev[0][gq].x), pl);
+      pl = fmaf(w0[4 * gq + 1], bf16hi(ev[0][gq].x), pl);
+      pl = fmaf(w0[4 * gq + 2], bf16lo(ev[0][gq].y), pl);
+      pl = fmaf(w0[4 * gq + 3], bf16hi(ev[0][gq].y), pl);
+      pl = fmaf(w1[4 * gq + 0], bf16lo(ev[1][gq].x), pl);
+      pl = fmaf(w1[4 * gq + 1], bf16hi(ev[1][gq].x), pl);
+      pl = fmaf(w1[4 * gq + 2], bf16lo(ev[1][gq].y), pl);
+      pl = fmaf(w1[4 * gq + 3], bf16hi(ev[1][gq].y), pl);
+    }
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      pv = fmaf(v0[4 * gq + 0], bf16lo(drv[0][gq].x), pv);
+      pv = fmaf(v0[4 * gq + 1], bf16hi(drv[0][gq].x), pv);
+      pv = fmaf(v0[4 * gq + 2], bf16lo(drv[0][gq].y), pv);
+      pv = fmaf(v0[4 * gq + 3], bf16hi(drv[0][gq].y), pv);
+      pv = fmaf(v1[4 * gq + 0], bf16lo(drv[1][gq].x), pv);
+      pv = fmaf(v1[4 * gq + 1], bf16hi(drv[1][gq].x), pv);
+      pv = fmaf(v1[4 * gq + 2], bf16lo(drv[1][gq].y), pv);
+      pv = fmaf(v1[4 * gq + 3], bf16hi(drv[1][gq].y), pv);
+    }
+    const float l2 = halves_sum(pl) * a.e_scale;
+    const float dp = halves_sum(pv);
+    const bool valid = j < my_hist;
+    const float pj = valid ? fast_exp2(l2 - lse2) : 0.f;
+    const float dl = pj * (dp - D);
+    const float dls = dl * a.inv_sqrt_n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      de[0][r] = fmaf(dls, w0[r], de[0][r]);
+      de[1][r] = fmaf(dls, w1[r], de[1][r]);
+    }
+    if (half == 0 && tok_ok) {
+      const int64_t rowj = pd_base + (int64_t)j * 2 * a.L;
+      a.pd[rowj + col] = pj;
+      a.pd[rowj + a.L + col] = dl;
+    }
+  }
+
+  if (tok_ok) {
+    float* dp = a.dE + (((row0 + t) * a.dE_heads) + (a.dE_heads == a.H ? h : g)) * kP + 4 * half;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        *(float4*)(dp + 32 * rb + 8 * gq) =
+            make_float4(de[rb][4 * gq + 0], de[rb][4 * gq + 1], de[rb][4 * gq + 2], de[rb][4 * gq + 3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sma_bwd_a_mfma(const Shape& s, const void* Q, const void* C, const void* E,
+                                 const void* dH, const void* gate, int gate_pc, const void* dout,
+                                 const float* R, const float* lse, float* dE, int dE_heads,
+                                 float* pd, void* dR, float* dgate, hipStream_t st) {
+  BwdAArgs a;
+  a.Q = (const bf16_t*)Q;
+  a.C = (const bf16_t*)C;
+  a.E = (const bf16_t*)E;
+  a.dH = (const bf16_t*)dH;
+  a.gate = (const bf16_t*)gate;
+  a.dout = (const bf16_t*)dout;
+  a.R = R;
+  a.lse = lse;
+  a.dE = dE;
+  a.pd = pd;
+  a.dR = (bf16_t*)dR;
+  a.dgate = dgate;
+  a.L = s.L;
+  a.H = (int)s.H;
+  a.G = (int)s.G;
+  a.hpg = (int)(s.H / s.G);
+  a.S = (int)s.S;
+  a.M = (int)s.M;
+  a.gate_pc = gate_pc;
+  a.dE_heads = dE_heads;
+  a.BH = (int)(s.b * s.H);
+  a.BHp = (a.BH + 7) / 8 * 8;
+  a.n_tiles = (int)((s.L + kTile - 1) / kTile);
+  a.e_scale = kLog2e / sqrtf((float)kN);
+  a.inv_sqrt_n = 1.f / sqrtf((float)kN);
+  const int64_t blocks = (int64_t)a.BHp * a.n_tiles;
+  if (blocks == 0) return hipSuccess;
+  sma_bwd_a_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Pass BC: dQ^T += dH_c (E * dl / sqrt(N))^T,  dC^T += dH_c (dR * p)^T
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kPdBytes = 4 * 2 * 32 * 4;          // (p, dl) of 4 waves x 32 tokens
+constexpr int kSlotBC = kMemBytes + kPdBytes;     // one chunk memory + its weights
+
+struct BwdBCArgs {
+  const bf16_t* E;
+  const bf16_t* dR;    // [b][L][H][P], from pass A
+  const bf16_t* dH;
+  const float* pd;     // [b][H][M][2][L], from pass A
+  float* dQ;           // [b][L][out_heads][N]
+  float* dC;
+  int64_t L;
+  int H, G, hpg, S, M, out_heads;
+  int BH, BHp, n_tiles;
+  float inv_sqrt_n;
+};
+
+// Byte offset of bf16 entry (row p, column n) of a chunk memory staged for the
+// transposing reads: 256-byte rows of 16-byte pieces, piece ^ ((p & 3) << 2).
+__device__ __forceinline__ uint32_t tr_off(int p, int n) {
+  return (uint32_t)(p * 256 + ((((n >> 3) ^ ((p & 3) << 2))) << 4) + (n & 7) * 2);
+}
+
+// Eight transposing reads (4 bf16 = 8 bytes each) that return together; the
+// tiles read are complete by construction (explicit wait + barrier), and the
+// asm waits for its own results (the compiler's form of this read would drain
+// every direct-to-LDS load in flight first).
+__device__ __forceinline__ void ld_tr8(uint64_t (&o)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+        "=&v"(o[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+      : "memory");
+}
+
+// 8 bf16 scaled by s in float32 and rounded back.
+__device__ __forceinline__ bf16x8_t scale8(bf16x8_t x, float s) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  uint4 r;
+  r.x = pack_bf16x2(bf16lo(u.x) * s, bf16hi(u.x) * s);
+  r.y = pack_bf16x2(bf16lo(u.y) * s, bf16hi(u.y) * s);
+  r.z = pack_bf16x2(bf16lo(u.z) * s, bf16hi(u.z) * s);
+  r.w = pack_bf16x2(bf16lo(u.w) * s, bf16hi(u.w) * s);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sma_bwd_bc_kernel(BwdBCArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing * kSlotBC];
+
+  const int blk = blockIdx.x;
+  const int bh = blk % a.BHp;
+  if (bh >= a.BH) return;
+  const int tile = a.n_tiles - 1 - blk / a.BHp;
+  const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int grp16 = (lane >> 4) & 1, j16 = lane & 15;
+  const int64_t t0 = (int64_t)tile * kTile;
+  const int64_t t_last = (t0 + kTile < a.L ? t0 + kTile : a.L) - 1;
+  const int n_hist = (int)(t_last / a.S);
+  const int64_t t = t0 + wave * 32 + col;
+  const bool tok_ok = t < a.L;
+  const int64_t tc = tok_ok ? t : a.L - 1;
+  const int64_t row0 = (int64_t)b * a.L;
+
+  // Slot s = chunk s in ring buffer s % 4: the memory (rows p = 16w .. 16w+15
+  // loaded by wave w, 4 loads) and the (p, dl) pair of the wave's 32 tokens
+  // (one 4-byte-per-lane load: lanes 0-31 p, lanes 32-63 dl).  Five loads per
+  // wave per slot.
+  const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
+  const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
+  const uint32_t pd_lane = (uint32_t)((half ? a.L : 0) + t0 + 32 * wave + col) * 4;
+  auto issue = [&](int s) {
+    uint8_t* dst = s_ring + (s % kRing) * kSlotBC;
+    const auto rs = buf_rsrc(mem_head + (int64_t)s * kMemBytes, kMemBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      buf_dma16(rs, mem_dma + i * 1024 + (((lane & 15) ^ ((row & 3) << 2)) << 4),
+                dst + wave * 16 * 256 + i * 4 * 256);
+    }
+    const auto rp = buf_rsrc(a.pd + ((int64_t)bh * a.M + s) * 2 * a.L, (uint32_t)(2 * a.L * 4));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rp, (__attribute__((address_space(3))) void*)(dst + kMemBytes + wave * 256), 4, pd_lane, 0, 0, 0);
+  };
+
+  // B operands: lane holds token `col`, p = 16 ks + 8 half + 0..7
+  bf16x8_t eop[4], rop[4];
+  {
+    const bf16_t* ep = a.E + ((row0 + tc) * a.G + g) * kP + 8 * half;
+    const bf16_t* rp = a.dR + ((row0 + tc) * a.H + h) * kP + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      eop[ks] = *(const bf16x8_t*)(ep + 16 * ks);
+      rop[ks] = *(const bf16x8_t*)(rp + 16 * ks);
+    }
+  }
+  for (int s = 0; s < kRing - 1 && s < n_hist; ++s) issue(s);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);  // operands and the first slots
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    asm volatile("" : "+v"(eop[ks]));
+    asm volatile("" : "+v"(rop[ks]));
+  }
+
+  // A operand (dH: rows n, k = p): lane (column j16 + 16 grp16 of row block
+  // rb, k-octet `half`) addresses row p = 16 ks + 8 half + 4 hh + j16/4 at
+  // column n = 32 rb + 16 grp16 + 4 (j16 % 4).  The swizzle term depends only
+  // on p & 3 = (j16 / 4) & 3, so each row block has one per-lane base.
+  uint32_t abase[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) abase[rb] = tr_off(8 * half + (j16 >> 2), 32 * rb + 16 * grp16 + 4 * (j16 & 3));
+
+  f32x16_t dq[4], dc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) dq[rb] = dc[rb] = f32x16_t{};
+
+  for (int j = 0; j < n_hist; ++j) {
+    // slot j landed (its 5 loads) in every wave's part; slot j-1 free
+    asm volatile("" ::: "memory");
+    if (n_hist - 1 - j >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0f7a);      // vmcnt(10)
+    else if (n_hist - 1 - j == 1)
+      __builtin_amdgcn_s_waitcnt(0x0f75);      // vmcnt(5)
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + kRing - 1 < n_hist) issue(j + kRing - 1);
+
+    const uint8_t* slot = s_ring + (j % kRing) * kSlotBC;
+    const float* wpd = (const float*)(slot + kMemBytes + wave * 256);
+    const float ps = wpd[col], dls = wpd[32 + col] * a.inv_sqrt_n;
+    const uint32_t sb = lds_addr(slot);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {           // two k-steps per read batch
+      uint32_t ad[8];
+      uint64_t rd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ks = 2 * kp + (i >> 2), rb = i & 3;
+        ad[i] = sb + abase[rb] + (uint32_t)(16 * ks) * 256;  // hh = 0 half of the fragment
+      }
+      ld_tr8(rd, ad);
+      uint32_t ad2[8];
+      uint64_t rd2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ad2[i] = ad[i] + 4 * 256;   // hh = 1: rows + 4
+      ld_tr8(rd2, ad2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ks = 2 * kp + q;
+        const bf16x8_t be = scale8(eop[ks], dls);
+        const bf16x8_t br = scale8(rop[ks], ps);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int i = 4 * q + rb;
+          const bf16x8_t af = __builtin_bit_cast(
+              bf16x8_t, make_uint4((uint32_t)rd[i], (uint32_t)(rd[i] >> 32), (uint32_t)rd2[i],
+                                   (uint32_t)(rd2[i] >> 32)));
+          dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, be, dq[rb], 0, 0, 0);
+          dc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, br, dc[rb], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // dQ^T, dC^T: lane column = token, register r of row block rb is
+  // n = 32 rb + 8 (r / 4) + 4 half + r % 4
+  if (tok_ok) {
+    const int64_t orow = ((row0 + t) * a.out_heads + (a.out_heads == a.H ? h : g)) * kN + 4 * half;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = 32 * rb + 8 * q;
+        *(float4*)(a.dQ + orow + n) = make_float4(dq[rb][4 * q], dq[rb][4 * q + 1], dq[rb][4 * q + 2], dq[rb][4 * q + 3]);
+        *(float4*)(a.dC + orow + n) = make_float4(dc[rb][4 * q], dc[rb][4 * q + 1], dc[rb][4 * q + 2], dc[rb][4 * q + 3]);
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sma_bwd_bc_mfma(const Shape& s, const void* E, const void* dR, const void* dH,
+                                  const float* pd, float* dQ, float* dC, int out_heads,
+                                  hipStream_t st) {
+  BwdBCArgs a;
+  a.E = (const bf16_t*)E;
+  a.dR = (const bf16_t*)dR;
+  a.dH = (const bf16_t*)dH;
+  a.pd = pd;
+  a.dQ = dQ;
+  a.dC = dC;
+  a.L = s.L;
+  a.H = (int)s.H;
+  a.G = (int)s.G;
+  a.hpg = (int)(s.H / s.G);
+  a.S = (int)s.S;
+  a.M = (int)s.M;
+  a.out_heads = out_heads;
+  a.BH = (int)(s.b * s.H);
+  a.BHp = (a.BH + 7) / 8 * 8;
+  a.n_tiles = (int)((s.L + kTile - 1) / kTile);
+  a.inv_sqrt_n = 1.f / sqrtf((float)kN);
+  const int64_t blocks = (int64_t)a.BHp * a.n_tiles;
+  if (blocks == 0) return hipSuccess;
+  sma_bwd_bc_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Pass D: d_dH_c^T[p][n] = sum_{t >= (c+1)S} p_tc dR_t[p] C_t[n] + dl_tc/sqrt(N) E_t[p] Q_t[n]
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kSB = 64;                      // tokens per sub-block
+constexpr int kChunksD = 4;                  // chunks per block (one per wave's weight row)
+constexpr int kStagesD = 3;
+constexpr int kATile = kSB * kP * 2;         // dR or E: 64 rows of 128 B
+constexpr int kBTile = kSB * kN * 2;         // C or Q: 64 rows of 256 B
+constexpr int kWBytes = kChunksD * kSB * 4;  // weights of the block's chunks
+constexpr int kStageD = kATile + kBTile + kWBytes;
+
+struct BwdDArgs {
+  const bf16_t* dR;   // [b][L][H][P]
+  const bf16_t* E;    // [b][L][G][P]
+  const bf16_t* C;    // [b][L][G][N]
+  const bf16_t* Q;
+  const float* pd;    // [b][H][M][2][L]
+  float* ddH;         // [b][H][M][P][N]
+  int64_t L;
+  int H, G, hpg, S, M, n_groups, BH, BHp;
+  float inv_sqrt_n;
+};
+
+__device__ __forceinline__ int swz_x(int row) { return (row & 3) << 1; }
+__device__ __forceinline__ int swz_b(int row) { return (row & 3) << 2; }
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+// Six transposing reads plus eight 16-byte reads (the weights of the block's
+// chunks), returned together like ld_tr6: the compiler would otherwise drain
+// the loads in flight before reading the weights of the staged slot.
+__device__ __forceinline__ void ld_tr6_w8(uint64_t (&o)[6], f32x4v_t (&w)[8], const uint32_t (&ad)[6],
+                                          uint32_t wad) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %14\n\t"
+      "ds_read_b64_tr_b16 %1, %15\n\t"
+      "ds_read_b64_tr_b16 %2, %16\n\t"
+      "ds_read_b64_tr_b16 %3, %17\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %19\n\t"
+      "ds_read_b128 %6, %20\n\t"
+      "ds_read_b128 %7, %20 offset:16\n\t"
+      "ds_read_b128 %8, %20 offset:256\n\t"
+      "ds_read_b128 %9, %20 offset:272\n\t"
+      "ds_read_b128 %10, %20 offset:512\n\t"
+      "ds_read_b128 %11, %20 offset:528\n\t"
+      "ds_read_b128 %12, %20 offset:768\n\t"
+      "ds_read_b128 %13, %20 offset:784\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(w[0]),
+        "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(wad)
+      : "memory");
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sma_bwd_d_kernel(BwdDArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kStagesD * kStageD];
+
+  // heads fastest, chunk groups from the first (longest token stream) on
+  const int blk = blockIdx.x;
+  const int bh = blk % a.BHp;
+  if (bh >= a.BH) return;
+  const int cg = blk / a.BHp;
+  const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int half = lane >> 5, grp16 = (lane >> 4) & 1, j16 = lane & 15;
+  const int c0 = cg * kChunksD;
+  const int64_t row0 = (int64_t)b * a.L;
+  const int64_t ts = (int64_t)(c0 + 1) * a.S;          // first token any chunk of the block sees
+  const int64_t n_tok = ts < a.L ? a.L - ts : 0;
+  const int nsb = (int)((n_tok + kSB - 1) / kSB);
+  const int n_steps = 2 * nsb;                          // term 1 sub-blocks, then term 2
+
+  // Step q: term = q / nsb, sub-block q % nsb.  Wave w loads rows 16w..16w+15
+  // of both tiles (2 + 4 loads) and the weights of chunk c0 + w (1 load).
+  auto issue = [&](int q) {
+    const bool live = q < n_steps;
+    const int term = live ? q / nsb : 0;
+    const int sbk = live ? q % nsb : 0;
+    const int64_t sb = ts + (int64_t)sbk * kSB;
+    const int cnt = live ? (int)((a.L - sb) < kSB ? (a.L - sb) : kSB) : 1;
+    uint8_t* st = s_lds + (q % kStagesD) * kStageD;
+    const bf16_t* abase = term == 0 ? a.dR + ((row0 + sb) * a.H + h) * kP : a.E + ((row0 + sb) * a.G + g) * kP;
+    const int astride = term == 0 ? a.H * kP : a.G * kP;
+    const auto ra = buf_rsrc(abase, live ? (uint32_t)((cnt - 1) * astride + kP) * 2 : 0u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * wave + 8 * i + (lane >> 3);
+      const int piece = (lane & 7) ^ swz_x(r);
+      buf_dma16(ra, (uint32_t)(r * astride + piece * 8) * 2, st + (16 * wave + 8 * i) * 128);
+    }
+    const bf16_t* bbase = (term == 0 ? a.C : a.Q) + ((row0 + sb) * a.G + g) * kN;
+    const auto rbr = buf_rsrc(bbase, live ? (uint32_t)((cnt - 1) * a.G * kN + kN) * 2 : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
+      const int piece = (lane & 15) ^ swz_b(r);
+      buf_dma16(rbr, (uint32_t)(r * a.G * kN + piece * 8) * 2, st + kATile + (16 * wave + 4 * i) * 256);
+    }
+    // weights of chunk c0 + wave for tokens sb .. sb+63 (p row or dl row)
+    const int c = c0 + wave;
+    const bool wl = live && c < a.M;
+    const float* wrow = a.pd + ((int64_t)bh * a.M + (c < a.M ? c : 0)) * 2 * a.L + (term ? a.L : 0);
+    const auto rw = buf_rsrc(wrow, wl ? (uint32_t)(a.L * 4) : 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rw, (__attribute__((address_space(3))) void*)(st + kATile + kBTile + wave * kSB * 4), 4,
+        (uint32_t)((sb - 0) + lane) * 4, 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int q = 0; q < kStagesD; ++q) issue(q);
+
+  f32x16_t acc[kChunksD][2];
+#pragma unroll
+  for (int k = 0; k < kChunksD; ++k) acc[k][0] = acc[k][1] = f32x16_t{};
+
+  for (int q = 0; q < n_steps; ++q) {
+    const int after = n_steps - 1 - q;
+    asm volatile("" ::: "memory");
+    if (after >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0f7e);      // vmcnt(14): steps q+1, q+2 in flight
+    else if (after == 1)
+      __builtin_amdgcn_s_waitcnt(0x0f77);      // vmcnt(7)
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (q >= 1 && q + 2 < n_steps) issue(q + 2);
+
+    const int term = q / nsb;
+    const int64_t sb = ts + (int64_t)(q % nsb) * kSB;
+    const uint8_t* st = s_lds + (q % kStagesD) * kStageD;
+    const uint32_t sa = lds_addr(st), sbb = sa + kATile;
+    const uint32_t swt = sa + kATile + kBTile;  // weights: chunk k at + 256 k
+    const float wscale = term ? a.inv_sqrt_n : 1.f;
+    // chunks that see some token of this sub-block (uniform); a chunk whose
+    // first visible token lies inside the sub-block is masked per token
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < kSB / 16; ++ks) {
+      uint32_t ad[6];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = 16 * ks + 8 * half + 4 * hh + (j16 >> 2);
+        const int cb = 16 * grp16 + 4 * (j16 & 3);
+        const int nb = 32 * wave + cb;
+        ad[hh] = sbb + r * 256 + (((nb >> 3) ^ swz_b(r)) << 4) + ((nb & 7) >> 2) * 8;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int pb = 32 * f + cb;
+          ad[2 + 2 * f + hh] = sa + r * 128 + (((pb >> 3) ^ swz_x(r)) << 4) + ((pb & 7) >> 2) * 8;
+        }
+      }
+      uint64_t rd[6];
+      f32x4v_t wv[8];  // chunk k: tokens 16 ks + 8 half + 0..3 (2k), + 4..7 (2k+1)
+      ld_tr6_w8(rd, wv, ad, swt + (16 * ks + 8 * half) * 4);
+      const uint2 b0 = __builtin_bit_cast(uint2, rd[0]), b1 = __builtin_bit_cast(uint2, rd[1]);
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
+                                                                  (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[4], (uint32_t)(rd[4] >> 32),
+                                                                  (uint32_t)rd[5], (uint32_t)(rd[5] >> 32)));
+      const int64_t tk = sb + 16 * ks + 8 * half;  // this lane's first token of the k-step
+#pragma unroll
+      for (int k = 0; k < kChunksD; ++k) {
+        const int64_t first = (int64_t)(c0 + k + 1) * a.S;  // chunk c0+k sees tokens >= first
+        if (c0 + k >= a.M || sb + kSB <= first) continue;    // uniform: nothing to add
+        float4 w0 = make_float4(wv[2 * k][0], wv[2 * k][1], wv[2 * k][2], wv[2 * k][3]);
+        float4 w1 = make_float4(wv[2 * k + 1][0], wv[2 * k + 1][1], wv[2 * k + 1][2], wv[2 * k + 1][3]);
+        if (sb < first) {  // straddling sub-block: drop the tokens before `first`
+          w0.x = tk + 0 >= first ? w0.x : 0.f; w0.y = tk + 1 >= first ? w0.y : 0.f;
+          w0.z = tk + 2 >= first ? w0.z : 0.f; w0.w = tk + 3 >= first ? w0.w : 0.f;
+          w1.x = tk + 4 >= first ? w1.x : 0.f; w1.y = tk + 5 >= first ? w1.y : 0.f;
+          w1.z = tk + 6 >= first ? w1.z : 0.f; w1.w = tk + 7 >= first ? w1.w : 0.f;
+        }
+        uint4 bs;
+        bs.x = pack_bf16x2(bf16lo(b0.x) * (w0.x * wscale), bf16hi(b0.x) * (w0.y * wscale));
+        bs.y = pack_bf16x2(bf16lo(b0.y) * (w0.z * wscale), bf16hi(b0.y) * (w0.w * wscale));
+        bs.z = pack_bf16x2(bf16lo(b1.x) * (w1.x * wscale), bf16hi(b1.x) * (w1.y * wscale));
+        bs.w = pack_bf16x2(bf16lo(b1.y) * (w1.z * wscale), bf16hi(b1.y) * (w1.w * wscale));
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bs);
+        acc[k][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, acc[k][0], 0, 0, 0);
+        acc[k][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, acc[k][1], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // a block with no token to stream still issued its (zero-length) prologue
+  // loads into LDS: let them land before the block ends
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // d_dH_c^T[p][n]: register r of row block rb is p = 32 rb + 8 (r/4) + 4 half + r%4
+#pragma unroll
+  for (int k = 0; k < kChunksD; ++k) {
+    if (c0 + k >= a.M) continue;
+    float* outp = a.ddH + ((int64_t)bh * a.M + c0 + k) * (kP * kN) + 32 * wave + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = 8 * (r >> 2) + 4 * half + (r & 3);
+      outp[p * kN] = acc[k][0][r];
+      outp[(32 + p) * kN] = acc[k][1][r];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, const void* C,
+                                 const void* Q, const float* pd, float* ddH, hipStream_t st) {
+  BwdDArgs a;
+  a.dR = (const bf16_t*)dR;
+  a.E = (const bf16_t*)E;
+  a.C = (const bf16_t*)C;
+  a.Q = (const bf16_t*)Q;
+  a.pd = pd;
+  a.ddH = ddH;
+  a.L = s.L;
+  a.H = (int)s.H;
+  a.G = (int)s.G;
+  a.hpg = (int)(s.H / s.G);
+  a.S = (int)s.S;
+  a.M = (int)s.M;
+  a.n_groups = (int)((s.M + kChunksD - 1) / kChunksD);
+  a.BH = (int)(s.b * s.H);
+  a.BHp = (a.BH + 7) / 8 * 8;
+  a.inv_sqrt_n = 1.f / sqrtf((float)kN);
+  const int64_t blocks = (int64_t)a.BHp * a.n_groups;
+  if (blocks == 0) return hipSuccess;
+  sma_bwd_d_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// Workspace of the MFMA backward: (p, dl) rows [b][H][M][2][L] float32, dR
+// [b][L][H][P] bfloat16 and, for grouped heads, per-head dQ, dC [b][L][H][N]
+// and dE [b][L][H][P] float32 (summed over the group at the end).
+size_t sma_bwd_mfma_workspace_bytes(const Shape& s) {
+  size_t bytes = (size_t)(2 * s.b * s.H * s.M * s.L) * 4 + (size_t)(s.b * s.L * s.H * s.P) * 2;
+  bytes = (bytes + 255) / 256 * 256;
+  if (s.H != s.G) bytes += (size_t)(s.b * s.L * s.H * (2 * s.N + s.P)) * 4;
+  return bytes;
+}
+
+hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, const void* E,
+                               const void* dH, const void* gate, int gate_pc, const float* R,
+                               const float* lse, const void* dout, float* dQ, float* dC, float* dE,
+                               float* ddH, float* dgate, void* ws, hipStream_t st) {
+  uint8_t* w = (uint8_t*)ws;
+  float* pd = (float*)w;
+  void* dR = w + (size_t)(2 * s.b * s.H * s.M * s.L) * 4;
+  const bool grouped = s.H != s.G;
+  size_t off = ((size_t)(2 * s.b * s.H * s.M * s.L) * 4 + (size_t)(s.b * s.L * s.H * s.P) * 2 + 255) / 256 * 256;
+  float* hq = grouped ? (float*)(w + off) : dQ;
+  float* hc = grouped ? hq + s.b * s.L * s.H * s.N : dC;
+  float* he = grouped ? hc + s.b * s.L * s.H * s.N : dE;
+  const int heads = grouped ? (int)s.H : (int)s.G;
+  hipError_t e = launch_sma_bwd_a_mfma(s, Q, C, E, dH, gate, gate_pc, dout, R, lse, he, heads, pd, dR,
+                                       dgate, st);
+  if (e != hipSuccess) return e;
+  e = launch_sma_bwd_bc_mfma(s, E, dR, dH, pd, hq, hc, heads, st);
+  if (e != hipSuccess) return e;
+  e = launch_sma_bwd_d_mfma(s, dR, E, C, Q, pd, ddH, st);
+  if (e != hipSuccess || !grouped) return e;
+  const int64_t rows = s.b * s.L, hpg = s.H / s.G;
+  if ((e = launch_group_sum(hq, dQ, rows, s.G, hpg, s.N, st)) != hipSuccess) return e;
+  if ((e = launch_group_sum(hc, dC, rows, s.G, hpg, s.N, st)) != hipSuccess) return e;
+  return launch_group_sum(he, dE, rows, s.G, hpg, s.P, st);
+}
+
+}  // namespace dart

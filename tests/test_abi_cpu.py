@@ -174,8 +174,12 @@ def test_backward_validation():
     need = D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(d))
     b, L, H, G, N, P, S = 2, 512, 4, 2, 128, 64, 256
     M = 2
-    # (p, dl) per (chunk, token) and head, plus per-head partials (grouped)
-    assert need == 4 * (2 * b * H * M * L + b * L * H * (2 * N + P))
+    # the larger of the two layouts: (p, dl) per (chunk, token) and head, plus
+    # per-head partials when heads are grouped; the MFMA path also keeps dR
+    # in bfloat16 (a 256-byte aligned section)
+    general = 4 * (2 * b * H * M * L + b * L * H * (2 * N + P))
+    mfma = -(-(4 * 2 * b * H * M * L + 2 * b * L * H * P) // 256) * 256 + 4 * b * L * H * (2 * N + P)
+    assert need == max(general, mfma)
     assert bwd(d, ws=None) == -4 and "workspace" in last()
     assert bwd(d, ws_bytes=need - 1) == -4
     assert bwd(d, over={0: None}) == -1 and "Q" in last()
@@ -189,7 +193,8 @@ def test_backward_validation():
     assert bwd(d, dtype=3) == -3
     # ungrouped heads need no per-head partials
     d1 = dims(G=4)
-    assert D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(d1)) == 4 * 2 * b * H * M * L
+    assert D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(d1)) == max(
+        4 * 2 * b * H * M * L, -(-(4 * 2 * b * H * M * L + 2 * b * L * H * P) // 256) * 256)
     assert D.lib().dart_sma_bwd_workspace_bytes(None) == 0
 
 

@@ -34,6 +34,15 @@ def gpu_fwd_bwd(d, mem, cfg, dout, gate_pc):
     return dict(Q=host(dQ), C=host(dC), E=host(dE), dH=host(ddH), gate=host(dg)), ddH
 
 
+def run_bwd_path(d, mem, cfg, dout, gate_pc, path):
+    prev = dart.set_path(path)
+    try:
+        got, _ = gpu_fwd_bwd(d, mem, cfg, dout, gate_pc)
+    finally:
+        dart.set_path(prev)
+    return got
+
+
 def oracle_bwd(d, mem_oracle, cfg, dout, gate_pc):
     R, lse = O.sma_forward(d["Q"], d["C"], d["E"], mem_oracle, cfg["chunk"])
     _, dR, dg = O.gated_residual_backward(dout, d["gate"], R, gate_pc)
@@ -69,9 +78,14 @@ def test_sma_bwd_same_input(ci, gate_pc):
     mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, cfg["d_state"], cfg["d_head"],
                               cfg["dtype"], std=1.0, seed=12)
     dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["d_head"]), cfg["dtype"], 13)
-    got, _ = gpu_fwd_bwd(d, mem, cfg, dout, gate_pc)
     ref = oracle_bwd(d, to_oracle_mem(mem), cfg, dout, gate_pc)
-    compare(got, ref, TOL_SAME_INPUT[cfg["dtype"]], "same-input")
+    # general kernels: float32 arithmetic on the exact inputs
+    got = run_bwd_path(d, mem, cfg, dout, gate_pc, dart.DART_PATH_GENERAL)
+    compare(got, ref, TOL_SAME_INPUT[cfg["dtype"]], "same-input general")
+    # default path (the matrix core for bf16, N = 128, P = 64): dR and the
+    # weighted MFMA operands are rounded to bf16 once each, ~2^-9 relative
+    got = run_bwd_path(d, mem, cfg, dout, gate_pc, dart.DART_PATH_AUTO)
+    compare(got, ref, TOL[cfg["dtype"]], "same-input default")
 
 
 @pytest.mark.parametrize("ci", [0, 1])
@@ -126,3 +140,45 @@ def test_bwd_deterministic():
     b, _ = gpu_fwd_bwd(d, mem, cfg, dout, True)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+# bf16, N = 128, P = 64: the matrix-core backward.  Shapes chosen to exercise
+# tiles spanning several chunks (S < 128), chunk starts inside a 64-token
+# sub-block of the d_dH pass (S % 64 != 0), grouped heads, a ragged tail,
+# one chunk group per block boundary (M > 4) and the scalar gate.
+MFMA_CASES = [
+    dict(batch=1, nheads=4, ngroups=2, seqlen=1000, chunk=96, d_state=128, d_head=64, dtype="bf16"),
+    dict(batch=2, nheads=2, ngroups=2, seqlen=777, chunk=64, d_state=128, d_head=64, dtype="bf16"),
+    dict(batch=1, nheads=2, ngroups=1, seqlen=1300, chunk=256, d_state=128, d_head=64, dtype="bf16"),
+    dict(batch=1, nheads=3, ngroups=3, seqlen=200, chunk=50, d_state=128, d_head=64, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(MFMA_CASES)))
+def test_mfma_bwd_against_oracle_and_general(ci):
+    cfg = MFMA_CASES[ci]
+    gate_pc = ci != 1
+    say("mfma bwd", cfg, "gate_pc", gate_pc)
+    d = synth.draw_fwd(**cfg, seed=51 + ci, gate_per_channel=gate_pc)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, 128, 64, "bf16", std=1.0, seed=61 + ci)
+    dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], 64), "bf16", 71 + ci)
+    got = run_bwd_path(d, mem, cfg, dout, gate_pc, dart.DART_PATH_AUTO)
+    gen = run_bwd_path(d, mem, cfg, dout, gate_pc, dart.DART_PATH_GENERAL)
+    ref = oracle_bwd(d, to_oracle_mem(mem), cfg, dout, gate_pc)
+    compare(got, ref, TOL["bf16"], "mfma vs oracle")
+    compare(got, gen, TOL["bf16"], "mfma vs general")
+
+
+def test_mfma_bwd_sharp_weights():
+    """Logits scaled up so the chunk weights are far from uniform (the
+    graded draw gives nearly uniform weights, under which a misrouted chunk
+    or a wrong p would hide)."""
+    cfg = MFMA_CASES[2]
+    d = synth.draw_fwd(**cfg, seed=81, gains={"Q": 8.0 * 11.3})
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(1, 2, M, 128, 64, "bf16", std=1.0, seed=82)
+    dout = synth.draw_grad((1, cfg["seqlen"], 2, 64), "bf16", 83)
+    got = run_bwd_path(d, mem, cfg, dout, True, dart.DART_PATH_AUTO)
+    ref = oracle_bwd(d, to_oracle_mem(mem), cfg, dout, True)
+    compare(got, ref, TOL["bf16"], "mfma sharp vs oracle")
