@@ -53,6 +53,55 @@ def fwd_flops(cfg):
     return 4 * N * P * fwd_pairs(b, H, L, S), 2 * N * P * b * H * L
 
 
+def time_backward(torch, dart, synth, cfg, steps=5, warmup=1):
+    """The backward of the hot path on the same workload: dart_sma_bwd (the
+    three matrix-core passes) from the forward's R and lse and a synthetic
+    loss gradient, then dart_chunk_states_bwd.  Algorithmic flops of the SMA
+    backward: 12NP per (token, visible chunk) pair (the recomputed W and V
+    products 4NP, dQ and dC 4NP, the two d_dH contractions 4NP)."""
+    b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)
+    _, R, lse = dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S, want_R=True, want_lse=True)
+    dout = synth.draw_grad_torch((b, L, H, cfg["d_head"]), "bf16", seed=3)
+    import ctypes
+
+    from state_memory_attention_amd import dart as D
+    dims = D.Dims(b, L, H, cfg["ngroups"], cfg["d_state"], cfg["d_head"], S)
+    ws = torch.empty(int(D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8,
+                     device="cuda")
+    ws2 = torch.empty(int(D.lib().dart_chunk_states_bwd_workspace_bytes(ctypes.byref(dims))),
+                      dtype=torch.uint8, device="cuda")
+
+    def run():
+        g = dart.dart_sma_bwd(d["Q"], d["C"], d["E"], dH, d["gate"], R, lse, dout, S, workspace=ws)
+        return g
+
+    for _ in range(warmup):
+        g = run()
+        dart.dart_chunk_states_bwd(d["X"], d["B"], d["A"], g[3], S, workspace=ws2)
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record(st)
+        g = run()
+        ev[k][1].record(st)
+        dart.dart_chunk_states_bwd(d["X"], d["B"], d["A"], g[3], S, workspace=ws2)
+        ev[k][2].record(st)
+    torch.cuda.synchronize()
+    t_bwd = sum(e[0].elapsed_time(e[1]) for e in ev) / steps / 1e3
+    t_csb = sum(e[1].elapsed_time(e[2]) for e in ev) / steps / 1e3
+    flops = 12 * cfg["d_state"] * cfg["d_head"] * fwd_pairs(b, H, L, S)
+    res = {"workload": cfg["name"], "kernel": "dart_sma_bwd", "us_per_call": t_bwd * 1e6,
+           "flop_per_call": flops, "achieved_TFLOPs": flops / t_bwd / 1e12,
+           "peak_TFLOPs": PEAK_BF16_TFLOPS, "frac": flops / t_bwd / 1e12 / PEAK_BF16_TFLOPS,
+           "chunk_states_bwd_us": t_csb * 1e6, "grad_dtype": "f32"}
+    del d, dH, R, lse, dout, ws, ws2, g
+    torch.cuda.empty_cache()
+    return res
+
+
 def traffic_record(kernel, workload):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; else None."""
@@ -274,6 +323,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run each hot kernel a few times for a hardware-counter pass, then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -351,6 +401,8 @@ def main():
     }
     del d, dH, out
     torch.cuda.empty_cache()
+    if not args.no_backward:
+        result["backward"] = time_backward(torch, dart, synth, cfg)
     if not args.no_decode:
         result["decode"] = time_decode(torch, dart, synth)
     if not args.no_cpu_baseline:

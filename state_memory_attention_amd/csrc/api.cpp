@@ -408,8 +408,8 @@ int dart_chunk_states_bwd(const dart_dims_t* dims, int dtype, const void* X, con
   if (prod({s.b, s.H, s.M}) >= kMaxIndex || prod({s.b, s.L, s.G, s.N}) >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "problem is too large for one launch");
   hipStream_t strm = (hipStream_t)stream;
-  return hip_status(dart::launch_chunk_states_bwd_general(s, dtype == DART_BF16, X, B, A, d_dH, dX, dB,
-                                                          dA, (float*)workspace, strm),
+  return hip_status(dart::launch_chunk_states_bwd_general(s, dtype == DART_BF16, use_mfma(dtype, dims), X, B,
+                                                          A, d_dH, dX, dB, dA, (float*)workspace, strm),
                     "dart_chunk_states_bwd");
 }
 

@@ -362,16 +362,19 @@ size_t chunk_states_bwd_workspace_bytes(const Shape& s) {
   return (size_t)(wdw + heads) * sizeof(float);
 }
 
-hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, const void* X, const void* B,
-                                           const float* A, const float* ddH, float* dX, float* dB,
-                                           float* dA, float* ws, hipStream_t st) {
+hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, bool mfma, const void* X,
+                                           const void* B, const float* A, const float* ddH, float* dX,
+                                           float* dB, float* dA, float* ws, hipStream_t st) {
   float* wsw = ws;
   float* wsdw = ws + s.b * s.H * s.L;
   const bool grouped = s.H != s.G;
   float* hb = grouped ? wsdw + s.b * s.H * s.L : dB;
   const int64_t hs = grouped ? s.H : s.G;
   const unsigned blocks = (unsigned)(s.b * s.H * s.M);
-  if (bf16)
+  if (mfma) {
+    hipError_t e = launch_chunk_states_bwd_mfma(s, X, B, A, ddH, dX, hb, (int)hs, wsw, wsdw, st);
+    if (e != hipSuccess) return e;
+  } else if (bf16)
     chunk_states_bwd_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(
         s, (const bf16_t*)X, (const bf16_t*)B, A, ddH, dX, hb, hs, wsw, wsdw);
   else

@@ -36,9 +36,14 @@ hipError_t launch_sma_bwd_general(const Shape& s, bool bf16, const void* Q, cons
                                   float* dC, float* dE, float* ddH, float* dgate, float* ws,
                                   hipStream_t st);
 size_t chunk_states_bwd_workspace_bytes(const Shape& s);
-hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, const void* X, const void* B,
-                                           const float* A, const float* ddH, float* dX, float* dB,
-                                           float* dA, float* ws, hipStream_t st);
+// mfma: dX, dB and dw on the matrix core (bfloat16, N = 128, P = 64); the
+// decay recurrence and the group sums are shared.
+hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, bool mfma, const void* X,
+                                           const void* B, const float* A, const float* ddH, float* dX,
+                                           float* dB, float* dA, float* ws, hipStream_t st);
+hipError_t launch_chunk_states_bwd_mfma(const Shape& s, const void* X, const void* B, const float* A,
+                                        const float* ddH, float* dX, float* dB, int db_heads,
+                                        float* wsw, float* wsdw, hipStream_t st);
 
 // ---- MFMA kernels (bfloat16, N = 128, P = 64) -----------------------------
 hipError_t launch_chunk_states_mfma(const Shape& s, const void* X, const void* B, const float* A,

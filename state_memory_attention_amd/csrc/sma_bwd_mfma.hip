@@ -822,4 +822,196 @@ hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, con
   return launch_group_sum(he, dE, rows, s.G, hpg, s.P, st);
 }
 
+// ---------------------------------------------------------------------------
+// Chunk-state backward: for the chunk's d_dH (G, staged as bf16 G^T[p][n])
+//   T^T = G^T B_c^T  (P x S tokens):  dX_s = w_s T_s,  dw_s = X_s . T_s
+//   dB^T = G X_c^T   (N x S tokens):  dB_s = w_s (dB^T)_s
+// [§3 Eq. 5 differentiated]; dw goes to the decay recurrence kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kGroupCS = 256;   // tokens per decay-weight group (one per thread)
+
+struct CsBwdArgs {
+  const bf16_t* X;
+  const bf16_t* B;
+  const float* A;
+  const float* ddH;    // [b][H][M][P][N] float32
+  float* dX;           // [b][L][H][P]
+  float* dB;           // [b][L][db_heads][N]
+  float* wsw;          // [b][H][L]: w_s
+  float* wsdw;         // [b][H][L]: dw_s
+  int64_t L;
+  int H, G, hpg, S, M, db_heads;
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void chunk_states_bwd_mfma_kernel(CsBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_g[kMemBytes];   // G^T, tr-read swizzle
+  __shared__ float s_w[kGroupCS + 4];
+
+  const int nh = a.H;
+  const int bb = blockIdx.x / (a.M * nh);
+  const int rem = blockIdx.x - bb * (a.M * nh);
+  const int c = rem / nh;
+  const int bh = bb * nh + rem % nh;
+  const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int grp16 = (lane >> 4) & 1, j16 = lane & 15;
+  const int64_t s0 = (int64_t)c * a.S;
+  const int64_t s1 = (s0 + a.S < a.L) ? s0 + a.S : a.L;
+  const int64_t row0 = (int64_t)b * a.L;
+
+  // stage G^T (float32 in HBM) as bfloat16 for the matrix core
+  {
+    const float* gp = a.ddH + ((int64_t)bh * a.M + c) * (kP * kN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (tid + 256 * i) * 8;  // 8 consecutive n of one row p
+      const int p = e / kN, n = e % kN;
+      const float4 v0 = *(const float4*)(gp + e), v1 = *(const float4*)(gp + e + 4);
+      uint4 pk;
+      pk.x = pack_bf16x2(v0.x, v0.y);
+      pk.y = pack_bf16x2(v0.z, v0.w);
+      pk.z = pack_bf16x2(v1.x, v1.y);
+      pk.w = pack_bf16x2(v1.z, v1.w);
+      *(uint4*)(s_g + tr_off(p, n)) = pk;
+    }
+  }
+  // A operand of T^T: G^T rows p (k = n), read in 16-byte pieces
+  auto gt_frag = [&](int prow, int ks) -> bf16x8_t {
+    return *(const bf16x8_t*)(s_g + tr_off(prow, 16 * ks + 8 * half));
+  };
+  // A operand of dB^T: G rows n (k = p) by transposing reads (see pass BC)
+  uint32_t abase[4];
+  const uint32_t sgb = lds_addr(s_g);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    abase[rb] = sgb + tr_off(8 * half + (j16 >> 2), 32 * rb + 16 * grp16 + 4 * (j16 & 3));
+
+  float carry = 1.f;
+  const int64_t n_tok = s1 - s0;
+  for (int64_t gend = n_tok; gend > 0; gend -= kGroupCS) {   // groups from the chunk end
+    const int64_t g0 = gend - kGroupCS > 0 ? gend - kGroupCS : 0;
+    // weights of the group: in-wave suffix scan, then later waves and groups
+    {
+      const int64_t tg = s0 + g0 + tid;
+      float v = (g0 + tid < gend) ? a.A[(row0 + tg) * a.H + h] : 1.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float u = __shfl_down(v, off);
+        if (lane + off < 64) v *= u;
+      }
+      float nxt = __shfl_down(v, 1);
+      if (lane == 63) nxt = 1.f;
+      __syncthreads();  // previous group's weights are read; G staged
+      if (lane == 0) s_w[kGroupCS + wave] = v;
+      __syncthreads();
+      float later = carry;
+      for (int w2 = wave + 1; w2 < 4; ++w2) later *= s_w[kGroupCS + w2];
+      const float wv = (g0 + tid < gend) ? later * nxt : 0.f;
+      carry *= s_w[kGroupCS] * s_w[kGroupCS + 1] * s_w[kGroupCS + 2] * s_w[kGroupCS + 3];
+      __syncthreads();
+      s_w[tid] = wv;
+      __syncthreads();
+    }
+    for (int64_t pb = g0; pb < gend; pb += kTile) {           // 128-token passes
+      const int64_t sl = pb + 32 * wave + col;                // chunk-local token of this lane
+      const bool ok = sl < gend;
+      const int64_t tok = row0 + s0 + (ok ? sl : gend - 1);
+      // B operands: B_c^T (k = n, 8 per lane per step) and X_c^T (k = p)
+      const bf16_t* brow = a.B + (tok * a.G + g) * kN + 8 * half;
+      const bf16_t* xrow = a.X + (tok * a.H + h) * kP + 8 * half;
+      f32x16_t t0 = {}, t1 = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t bv = *(const bf16x8_t*)(brow + 16 * ks);
+        t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt_frag(col, ks), bv, t0, 0, 0, 0);
+        t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt_frag(32 + col, ks), bv, t1, 0, 0, 0);
+      }
+      f32x16_t db[4] = {{}, {}, {}, {}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t xv = *(const bf16x8_t*)(xrow + 16 * ks);
+        uint32_t ad[8];
+        uint64_t rd[8];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          ad[2 * rb] = abase[rb] + (uint32_t)(16 * ks) * 256;
+          ad[2 * rb + 1] = ad[2 * rb] + 4 * 256;
+        }
+        ld_tr8(rd, ad);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const bf16x8_t af = __builtin_bit_cast(
+              bf16x8_t, make_uint4((uint32_t)rd[2 * rb], (uint32_t)(rd[2 * rb] >> 32),
+                                   (uint32_t)rd[2 * rb + 1], (uint32_t)(rd[2 * rb + 1] >> 32)));
+          db[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xv, db[rb], 0, 0, 0);
+        }
+      }
+      // epilogue: lane column = token; T rows p = 32 rb + 8 (r/4) + 4 half + r%4
+      const float w = s_w[(int)(pb - g0) + 32 * wave + col];
+      const bf16_t* xa = a.X + (tok * a.H + h) * kP + 4 * half;
+      float part = 0.f;
+      float* dxp = a.dX + (tok * a.H + h) * kP + 4 * half;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16_t& tt = rb ? t1 : t0;
+          const uint2 xv = *(const uint2*)(xa + 32 * rb + 8 * q);
+          part = fmaf(bf16lo(xv.x), tt[4 * q + 0], part);
+          part = fmaf(bf16hi(xv.x), tt[4 * q + 1], part);
+          part = fmaf(bf16lo(xv.y), tt[4 * q + 2], part);
+          part = fmaf(bf16hi(xv.y), tt[4 * q + 3], part);
+          if (ok)
+            *(float4*)(dxp + 32 * rb + 8 * q) =
+                make_float4(w * tt[4 * q + 0], w * tt[4 * q + 1], w * tt[4 * q + 2], w * tt[4 * q + 3]);
+        }
+      const float dw = halves_sum(part);
+      if (ok && half == 0) {
+        a.wsw[(int64_t)bh * a.L + s0 + sl] = w;
+        a.wsdw[(int64_t)bh * a.L + s0 + sl] = dw;
+      }
+      if (ok) {
+        float* dbp = a.dB + (tok * a.db_heads + (a.db_heads == a.H ? h : g)) * kN + 4 * half;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(float4*)(dbp + 32 * rb + 8 * q) = make_float4(w * db[rb][4 * q + 0], w * db[rb][4 * q + 1],
+                                                            w * db[rb][4 * q + 2], w * db[rb][4 * q + 3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_states_bwd_mfma(const Shape& s, const void* X, const void* B, const float* A,
+                                        const float* ddH, float* dX, float* dB, int db_heads,
+                                        float* wsw, float* wsdw, hipStream_t st) {
+  CsBwdArgs a;
+  a.X = (const bf16_t*)X;
+  a.B = (const bf16_t*)B;
+  a.A = A;
+  a.ddH = ddH;
+  a.dX = dX;
+  a.dB = dB;
+  a.wsw = wsw;
+  a.wsdw = wsdw;
+  a.L = s.L;
+  a.H = (int)s.H;
+  a.G = (int)s.G;
+  a.hpg = (int)(s.H / s.G);
+  a.S = (int)s.S;
+  a.M = (int)s.M;
+  a.db_heads = db_heads;
+  const int64_t blocks = s.b * s.H * s.M;
+  if (blocks == 0) return hipSuccess;
+  chunk_states_bwd_mfma_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace dart

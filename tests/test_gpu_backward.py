@@ -182,3 +182,32 @@ def test_mfma_bwd_sharp_weights():
     got = run_bwd_path(d, mem, cfg, dout, True, dart.DART_PATH_AUTO)
     ref = oracle_bwd(d, to_oracle_mem(mem), cfg, dout, True)
     compare(got, ref, TOL["bf16"], "mfma sharp vs oracle")
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(batch=1, nheads=4, ngroups=2, seqlen=900, chunk=300, d_state=128, d_head=64),  # 2 weight groups
+    dict(batch=2, nheads=2, ngroups=2, seqlen=333, chunk=100, d_state=128, d_head=64),
+    dict(batch=1, nheads=2, ngroups=1, seqlen=512, chunk=256, d_state=128, d_head=64),
+])
+def test_chunk_states_bwd_mfma(cfg):
+    """dX, dB, dA on the matrix core (d_dH rounded to bf16 as its operand)
+    against the oracle and the general kernels."""
+    say("chunk_states_bwd mfma", cfg)
+    d = synth.draw_fwd(**cfg, dtype="bf16", seed=91)
+    d["A"][0, 7, 0] = 0.0
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    gmem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, 128, 64, "f32", seed=92)
+    X, B, A, G = dev(d["X"], "bf16"), dev(d["B"], "bf16"), dev(d["A"]), dev(gmem)
+    out = {}
+    for path in (dart.DART_PATH_AUTO, dart.DART_PATH_GENERAL):
+        prev = dart.set_path(path)
+        try:
+            dX, dB, dA = dart.dart_chunk_states_bwd(X, B, A, G, cfg["chunk"])
+        finally:
+            dart.set_path(prev)
+        torch.cuda.synchronize()
+        out[path] = dict(X=host(dX), B=host(dB), A=host(dA))
+    rX, rB, rA = O.chunk_states_backward(d["X"], d["B"], d["A"], cfg["chunk"], to_oracle_mem(gmem))
+    ref = dict(X=rX, B=rB, A=rA)
+    compare(out[dart.DART_PATH_GENERAL], ref, TOL_SAME_INPUT["bf16"], "cs-bwd general")
+    compare(out[dart.DART_PATH_AUTO], ref, TOL["bf16"], "cs-bwd mfma")
