@@ -48,7 +48,7 @@ struct BwdAArgs {
   const float* R;
   const float* lse;
   float* dE;        // [b][L][dE_heads][P]
-  float* pd;        // [b][H][M][2][L]: row of p then row of dl per chunk
+  float* pd;        // [b][H][M][2][L]: row of p then row of dl / sqrt(N) per chunk
   bf16_t* dR;       // [b][L][H][P]
   float* dgate;     // nullable
   int64_t L;
@@ -270,7 +270,7 @@ void sma_bwd_a_kernel(BwdAArgs a) {
     if (half == 0 && tok_ok) {
       const int64_t rowj = pd_base + (int64_t)j * 2 * a.L;
       a.pd[rowj + col] = pj;
-      a.pd[rowj + a.L + col] = dl;
+      a.pd[rowj + a.L + col] = dls;
     }
   }
 
@@ -335,7 +335,7 @@ struct BwdBCArgs {
   const bf16_t* E;
   const bf16_t* dR;    // [b][L][H][P], from pass A
   const bf16_t* dH;
-  const float* pd;     // [b][H][M][2][L], from pass A
+  const float* pd;     // [b][H][M][2][L], from pass A (p, dl / sqrt(N))
   float* dQ;           // [b][L][out_heads][N]
   float* dC;
   int64_t L;
@@ -469,7 +469,7 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
 
     const uint8_t* slot = s_ring + (j % kRing) * kSlotBC;
     const float* wpd = (const float*)(slot + kMemBytes + wave * 256);
-    const float ps = wpd[col], dls = wpd[32 + col] * a.inv_sqrt_n;
+    const float ps = wpd[col], dls = wpd[32 + col];
     const uint32_t sb = lds_addr(slot);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -568,7 +568,7 @@ struct BwdDArgs {
   const bf16_t* E;    // [b][L][G][P]
   const bf16_t* C;    // [b][L][G][N]
   const bf16_t* Q;
-  const float* pd;    // [b][H][M][2][L]
+  const float* pd;    // [b][H][M][2][L]: p, dl / sqrt(N)
   float* ddH;         // [b][H][M][P][N]
   int64_t L;
   int H, G, hpg, S, M, n_groups, BH, BHp;
@@ -688,7 +688,6 @@ void sma_bwd_d_kernel(BwdDArgs a) {
     const uint8_t* st = s_lds + (q % kStagesD) * kStageD;
     const uint32_t sa = lds_addr(st), sbb = sa + kATile;
     const uint32_t swt = sa + kATile + kBTile;  // weights: chunk k at + 256 k
-    const float wscale = term ? a.inv_sqrt_n : 1.f;
     // chunks that see some token of this sub-block (uniform); a chunk whose
     // first visible token lies inside the sub-block is masked per token
     __builtin_amdgcn_s_setprio(1);
@@ -729,10 +728,10 @@ void sma_bwd_d_kernel(BwdDArgs a) {
           w1.z = tk + 6 >= first ? w1.z : 0.f; w1.w = tk + 7 >= first ? w1.w : 0.f;
         }
         uint4 bs;
-        bs.x = pack_bf16x2(bf16lo(b0.x) * (w0.x * wscale), bf16hi(b0.x) * (w0.y * wscale));
-        bs.y = pack_bf16x2(bf16lo(b0.y) * (w0.z * wscale), bf16hi(b0.y) * (w0.w * wscale));
-        bs.z = pack_bf16x2(bf16lo(b1.x) * (w1.x * wscale), bf16hi(b1.x) * (w1.y * wscale));
-        bs.w = pack_bf16x2(bf16lo(b1.y) * (w1.z * wscale), bf16hi(b1.y) * (w1.w * wscale));
+        bs.x = pack_bf16x2(bf16lo(b0.x) * w0.x, bf16hi(b0.x) * w0.y);
+        bs.y = pack_bf16x2(bf16lo(b0.y) * w0.z, bf16hi(b0.y) * w0.w);
+        bs.z = pack_bf16x2(bf16lo(b1.x) * w1.x, bf16hi(b1.x) * w1.y);
+        bs.w = pack_bf16x2(bf16lo(b1.y) * w1.z, bf16hi(b1.y) * w1.w);
         const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bs);
         acc[k][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, acc[k][0], 0, 0, 0);
         acc[k][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, acc[k][1], 0, 0, 0);
