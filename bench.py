@@ -26,16 +26,25 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "SMA+chunk-state fwd tokens/s at L=16K,N=128,P=64,S=256; % bf16 MFMA peak"
+_CSRC = "state_memory_attention_amd/csrc/"
+# the source files (kernel file and the device headers it includes) whose
+# hash keys a committed counter summary to the code it was taken on
 KERNEL_SOURCES = {
-    "sma_fwd": "state_memory_attention_amd/csrc/sma_fwd_mfma.hip",
-    "chunk_states": "state_memory_attention_amd/csrc/chunk_states_mfma.hip",
-    "decode": "state_memory_attention_amd/csrc/sma_decode_mfma.hip",
+    "sma_fwd": [_CSRC + "sma_fwd_mfma.hip", _CSRC + "dev_common.h"],
+    "chunk_states": [_CSRC + "chunk_states_mfma.hip", _CSRC + "dev_common.h"],
+    "decode": [_CSRC + "sma_decode_mfma.hip", _CSRC + "dev_common.h"],
+    "sma_bwd": [_CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
+    "chunk_states_bwd": [_CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
+    "state_update": [_CSRC + "decode_update.hip", _CSRC + "dev_common.h"],
 }
 
 
-def source_hash(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def fwd_pairs(b, H, L, S):
@@ -96,13 +105,15 @@ def time_backward(torch, dart, synth, cfg, steps=5, warmup=1):
     res = {"workload": cfg["name"], "kernel": "dart_sma_bwd", "us_per_call": t_bwd * 1e6,
            "flop_per_call": flops, "achieved_TFLOPs": flops / t_bwd / 1e12,
            "peak_TFLOPs": PEAK_BF16_TFLOPS, "frac": flops / t_bwd / 1e12 / PEAK_BF16_TFLOPS,
-           "chunk_states_bwd_us": t_csb * 1e6, "grad_dtype": "f32"}
+           "chunk_states_bwd_us": t_csb * 1e6, "grad_dtype": "f32",
+           "traffic": {k: traffic_record(k, cfg["name"], "sma_bwd") for k in ("sma_bwd_a", "sma_bwd_bc", "sma_bwd_d")}}
+    res["traffic"]["chunk_states_bwd"] = traffic_record("chunk_states_bwd", cfg["name"])
     del d, dH, R, lse, dout, ws, ws2, g
     torch.cuda.empty_cache()
     return res
 
 
-def traffic_record(kernel, workload):
+def traffic_record(kernel, workload, sources=None):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
@@ -110,7 +121,7 @@ def traffic_record(kernel, workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[sources or kernel]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -180,12 +191,10 @@ def time_decode(torch, dart, synth, steps=20, warmup=3):
     return res
 
 
-def time_state_update(torch, dart, synth, cfg, cache, steps, warmup):
-    """dart_decode_state_update on the decode workload: one token per row
-    absorbed into the float32 in-progress chunk memories (b, H, P, N).  The
-    positions are mid-chunk, so every call reads and writes the whole state
-    and writes no cache row (the per-token steady state; a chunk close writes
-    the dtype row instead of the state, fewer bytes)."""
+def _state_update_inputs(torch, cfg):
+    """One new token per batch row of the decode workload: x (b, H, P) and
+    B (b, G, N) in bf16, decay a (b, H), a float32 in-progress state
+    (b, H, P, N) and positions in the middle of chunk 100 (S = 256)."""
     b, H, G, N, P = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["d_state"], cfg["d_head"]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1)
@@ -194,7 +203,17 @@ def time_state_update(torch, dart, synth, cfg, cache, steps, warmup):
     a = torch.rand((b, H), generator=gen, device="cuda") * 0.5 + 0.5
     state = torch.zeros((b, H, P, N), device="cuda")
     pos = torch.full((b,), 256 * 100 + 7, dtype=torch.int32, device="cuda")
-    nch = torch.zeros((b,), dtype=torch.int32, device="cuda")
+    return x, Bt, a, state, pos
+
+
+def time_state_update(torch, dart, synth, cfg, cache, steps, warmup):
+    """dart_decode_state_update on the decode workload: one token per row
+    absorbed into the float32 in-progress chunk memories (b, H, P, N).  The
+    positions are mid-chunk, so every call reads and writes the whole state
+    and writes no cache row (the per-token steady state; a chunk close writes
+    the dtype row instead of the state, fewer bytes)."""
+    x, Bt, a, state, pos = _state_update_inputs(torch, cfg)
+    nch = torch.zeros((cfg["batch"],), dtype=torch.int32, device="cuda")
     S = 256
     for _ in range(warmup):
         dart.dart_decode_state_update(x, Bt, a, state, pos, cache, S, n_chunks=nch)
@@ -210,7 +229,8 @@ def time_state_update(torch, dart, synth, cfg, cache, steps, warmup):
     nbytes = 2 * state.numel() * 4 + (x.numel() + Bt.numel()) * 2 + a.numel() * 4
     gbs = nbytes / t / 1e9
     return {"kernel": "dart_decode_state_update", "us_per_call": t * 1e6, "bytes_per_call": nbytes,
-            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
+            "traffic": traffic_record("state_update", cfg["name"])}
 
 
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
@@ -254,6 +274,26 @@ def profile_kernels(launches=3):
     for _ in range(launches):
         dart.dart_sma_decode(d["q"], d["c"], d["e"], d["cache"], d["y"], d["gate"])
     torch.cuda.synchronize()
+    upd = _state_update_inputs(torch, cfg)
+    for _ in range(launches):
+        dart.dart_decode_state_update(*upd, d["cache"], 256, n_chunks=None)
+    torch.cuda.synchronize()
+    del d, upd
+    torch.cuda.empty_cache()
+    # backward of the long-context workload: the forward's R and lse first
+    cfg = dict(synth.CONFIGS[2])
+    S = cfg["chunk"]
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)
+    _, R, lse = dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S, want_R=True, want_lse=True)
+    dout = synth.draw_grad_torch((cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["d_head"]), "bf16", seed=3)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        g = dart.dart_sma_bwd(d["Q"], d["C"], d["E"], dH, d["gate"], R, lse, dout, S)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        dart.dart_chunk_states_bwd(d["X"], d["B"], d["A"], g[3], S)
+    torch.cuda.synchronize()
     print("profile-kernels done", flush=True)
 
 
@@ -296,19 +336,27 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
         return (sum(sel_f) / len(sel_f) * 1024 * f_scale, sum(sel_w) / len(sel_w) * 1024 * w_scale)
 
     out = []
-    plan = [("chunk_states", "chunk_states_mfma_kernel", synth.CONFIGS[2]["name"], 1),
-            ("sma_fwd", "sma_fwd_mfma_kernel", synth.CONFIGS[2]["name"], 0),
-            ("chunk_states", "chunk_states_mfma_kernel", synth.CONFIGS[3]["name"], 1 + launches + 1),
-            ("sma_fwd", "sma_fwd_mfma_kernel", synth.CONFIGS[3]["name"], launches),
-            ("decode", "sma_decode_partial_kernel", synth.CONFIGS[4]["name"], 0)]
-    for kernel, sym, workload, first in plan:
+    w2, w3, w4 = (synth.CONFIGS[i]["name"] for i in (2, 3, 4))
+    # (file label, source set, kernel symbol, workload, index of the first
+    # counted dispatch of that symbol in the --profile-kernels program)
+    plan = [("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w2, 1),
+            ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w2, 0),
+            ("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w3, 1 + launches + 1),
+            ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w3, launches),
+            ("decode", "decode", "sma_decode_partial_kernel", w4, 0),
+            ("state_update", "state_update", "decode_update_kernel", w4, 0),
+            ("sma_bwd_a", "sma_bwd", "sma_bwd_a_kernel", w2, 0),
+            ("sma_bwd_bc", "sma_bwd", "sma_bwd_bc_kernel", w2, 0),
+            ("sma_bwd_d", "sma_bwd", "sma_bwd_d_kernel", w2, 0),
+            ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w2, 0)]
+    for label, kernel, sym, workload, first in plan:
         rd, wr = per_kernel(sym, first, launches)
         rec = {"kernel": sym, "workload": workload, "source_sha256_16": source_hash(KERNEL_SOURCES[kernel]),
                "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
                "hbm_bytes_per_launch": rd + wr, "fetch_scale": f_scale, "write_scale": w_scale,
                "calibration": f"plain 16-byte-vector copy (libdart_probe.so) of {COPY_BYTES} bytes: FETCH_SIZE and WRITE_SIZE (KiB) "
                               "scaled so that the copy reads and writes exactly its size"}
-        path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+        path = os.path.join(ROOT, "profiles", f"traffic_{label}_{workload}.json")
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         out.append(rec)
@@ -389,7 +437,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded torch generator on the GPU; recipe in DESIGN.md)",
+        "data": "synthetic (seeded torch generator on the GPU; recipe in state_memory_attention_amd/synth.py)",
         "config": {"workload": cfg["name"], "batch": b, "nheads": H, "ngroups": cfg["ngroups"],
                    "seqlen": L, "chunk": S, "d_state": cfg["d_state"], "d_head": cfg["d_head"]},
         "roofline": {"bound": "mfma", "kernel": "dart_sma_fwd", "achieved": achieved,
