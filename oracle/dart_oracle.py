@@ -31,6 +31,9 @@ design notes):
   * a partial last chunk decays to its own last token (e(c) is the last index
     actually in the chunk) [§3 text under Eq. 5].
 
+  * the RMS-normalised score branch [App. B.1 Eq. 25-27] uses one eps for
+    both RMSNorms and for r_c, and an optional per-channel RMSNorm weight
+    applied after the normalisation;
   * the backward pass takes the loss gradient of ``out`` (or of R) and the
     forward's saved lse, and recovers the chunk weights as p = exp(l - lse)
     [App. C Eq. 33-35]; gradients of projections shared by a group of heads
@@ -68,6 +71,12 @@ __all__ = [
     "chunk_states_backward",
     "decode_state_update",
     "decode_stream",
+    "rms_norm",
+    "chunk_inv_rms",
+    "sma_token_rms",
+    "sma_head_rms",
+    "sma_forward_rms",
+    "sma_decode_rms",
 ]
 
 
@@ -455,3 +464,119 @@ def chunk_states_backward(X, B, A, S: int, d_dH):
             dB[bi, :, h // hpg] += bb
             dA[bi, :, h] = aa
     return dX, dB, dA
+
+
+# ---------------------------------------------------------------------------
+# RMS-normalised score branch  [§3 text after Eq. 10; App. B.1 Eq. 25-27].
+# Only the logits change: the query and the key readout vector are
+# RMS-normalised per token, and the key readout of chunk c is rescaled along
+# the key axis N by the inverse RMS of dH_c taken over the value axis P.  The
+# value readout V_c = C_t dH_c is the plain one of §3 Eq. 8.
+# Readings: one eps serves the two RMSNorms and r_c; each RMSNorm may carry a
+# per-channel weight applied after the normalisation (None = 1).
+# ---------------------------------------------------------------------------
+
+
+def rms_norm(x, eps: float, weight=None):
+    """RMSNorm over the last axis  [App. B.1 Eq. 25]:
+    x / sqrt(mean(x^2) + eps), then times ``weight`` (per channel) if given."""
+    x = _f64(x)
+    y = x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return y if weight is None else y * _f64(weight)
+
+
+def chunk_inv_rms(dH, eps: float):
+    """r_c of App. B.1 Eq. 26: the inverse RMS of each chunk memory along
+    the value axis, r_{c,n} = (mean_p dH_c[n, p]^2 + eps)^(-1/2).
+    dH (..., N, P)  ->  r (..., N)."""
+    dH = _f64(dH)
+    return 1.0 / np.sqrt((dH * dH).mean(axis=-1) + eps)
+
+
+def sma_token_rms(q, c, e, dH_visible, eps: float, wq=None, we=None):
+    """The normalised score branch for one token  [App. B.1 Eq. 25-27]:
+
+        qn = RMSNorm(Q_t), en = RMSNorm(E_t)                      [Eq. 25]
+        K_c = r_c * (dH_c en),  l_c = qn . K_c / sqrt(N)           [Eq. 26-27]
+        g = softmax_c(l),  V_c = C_t dH_c,  R_t = sum_c g_c V_c    [Eq. 27]
+
+    q, c (N,), e (P,), dH_visible (n, N, P).  Returns (R (P,), lse)."""
+    c, dH = _f64(c), _f64(dH_visible)
+    N, P = dH.shape[1], dH.shape[2]
+    n = dH.shape[0]
+    if n == 0:
+        return np.zeros(P), -math.inf
+    qn = rms_norm(q, eps, wq)
+    en = rms_norm(e, eps, we)
+    r = chunk_inv_rms(dH, eps)                               # (n, N)  [Eq. 26]
+    K = r * np.einsum("cnp,p->cn", dH, en)                   # [Eq. 26]
+    logits = (K @ qn) / math.sqrt(N)                         # [Eq. 27]
+    V = np.einsum("n,cnp->cp", c, dH)                        # [§3 Eq. 8]
+    m = logits.max()
+    p = np.exp(logits - m)
+    d = p.sum()
+    return (p[:, None] * V).sum(axis=0) / d, m + math.log(d)
+
+
+def sma_head_rms(Q, C, E, dH, S: int, eps: float, wq=None, we=None):
+    """sma_token_rms for every token of one head, batched per target chunk
+    as in ``sma_head``:  Q, C (L, N), E (L, P), dH (M, N, P)
+    ->  R (L, P), lse (L,)."""
+    C, dH = _f64(C), _f64(dH)
+    L, N = C.shape
+    P = dH.shape[2]
+    M = num_chunks(L, S)
+    Qn = rms_norm(Q, eps, wq)                                # [Eq. 25]
+    En = rms_norm(E, eps, we)
+    r = chunk_inv_rms(dH, eps)                               # (M, N)  [Eq. 26]
+    R = np.zeros((L, P))
+    lse = np.full(L, -math.inf)
+    scale = 1.0 / math.sqrt(N)
+    for i in range(1, M):
+        s0, s1 = chunk_bounds(i, L, S)
+        hist = dH[:i]
+        V = np.einsum("tn,cnp->tcp", C[s0:s1], hist, optimize=True)
+        K = r[:i][None] * np.einsum("cnp,tp->tcn", hist, En[s0:s1], optimize=True)
+        logits = np.einsum("tn,tcn->tc", Qn[s0:s1], K) * scale
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        d = p.sum(axis=1, keepdims=True)
+        R[s0:s1] = np.einsum("tc,tcp->tp", p, V, optimize=True) / d
+        lse[s0:s1] = (m + np.log(d))[:, 0]
+    return R, lse
+
+
+def sma_forward_rms(Q, C, E, dH, S: int, eps: float, wq=None, we=None):
+    """Batched sma_head_rms (layouts as ``sma_forward``); wq (N,) and we (P,)
+    are the RMSNorm weights shared by every head, or None."""
+    Q, C, E = _f64(Q), _f64(C), _f64(E)
+    b, L, G, N = Q.shape
+    H = dH.shape[1]
+    P = E.shape[3]
+    hpg = H // G
+    R = np.zeros((b, L, H, P))
+    lse = np.zeros((b, H, L))
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            R[bi, :, h], lse[bi, h] = sma_head_rms(Q[bi, :, g], C[bi, :, g], E[bi, :, g], dH[bi, h], S,
+                                                   eps, wq, we)
+    return R, lse
+
+
+def sma_decode_rms(q, c, e, cache, n_chunks, eps: float, hpg: int = 1, wq=None, we=None):
+    """Decode with the normalised score branch (layouts as ``sma_decode``):
+    every cached chunk 0..n_b-1 is visible; r_c is the inverse RMS of the
+    cached memory [App. B.1 Eq. 26]."""
+    q, c, e, cache = _f64(q), _f64(c), _f64(e), _f64(cache)
+    b, H = cache.shape[0], cache.shape[1]
+    P = cache.shape[4]
+    R = np.zeros((b, H, P))
+    lse = np.zeros((b, H))
+    for bi in range(b):
+        nb = int(n_chunks[bi])
+        for h in range(H):
+            g = h // hpg
+            R[bi, h], lse[bi, h] = sma_token_rms(q[bi, g], c[bi, g], e[bi, g], cache[bi, h, :nb], eps,
+                                                 wq, we)
+    return R, lse
