@@ -113,6 +113,50 @@ def time_backward(torch, dart, synth, cfg, steps=5, warmup=1):
     return res
 
 
+def time_rms(torch, dart, synth, cfg, steps=10, warmup=2, eps=1e-6):
+    """The hot path with the RMS-normalised score branch on the same
+    workload: dart_chunk_states_rms (chunk memories plus the float16 score
+    memory) and dart_sma_fwd_rms.  Same algorithmic flops as the plain
+    forward (4NP per pair; the normalisation is O(L (N + P)) per head)."""
+    b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
+    N, P = cfg["d_state"], cfg["d_head"]
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    M = dart.num_chunks(L, S)
+    dH = torch.empty((b, H, M, P, N), dtype=torch.bfloat16, device="cuda")
+    dHs = torch.empty((b, H, M, P, N), dtype=torch.float16, device="cuda")
+    out = torch.empty_like(d["Y"])
+
+    def cs():
+        dart.dart_chunk_states_rms(d["X"], d["B"], d["A"], S, eps, dH=dH, dH_score=dHs, want_r=False)
+
+    def fwd():
+        dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["Y"], d["gate"], S, eps, out=out)
+
+    for _ in range(warmup):
+        cs()
+        fwd()
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record(st)
+        cs()
+        ev[k][1].record(st)
+        fwd()
+        ev[k][2].record(st)
+    torch.cuda.synchronize()
+    t_cs = sum(e[0].elapsed_time(e[1]) for e in ev) / steps / 1e3
+    t_fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps / 1e3
+    f_sma, _ = fwd_flops(cfg)
+    res = {"workload": cfg["name"], "kernel": "dart_sma_fwd_rms", "us_per_call": t_fwd * 1e6,
+           "achieved_TFLOPs": f_sma / t_fwd / 1e12, "peak_TFLOPs": PEAK_BF16_TFLOPS,
+           "frac": f_sma / t_fwd / 1e12 / PEAK_BF16_TFLOPS, "chunk_states_rms_us": t_cs * 1e6,
+           "tokens_per_s": b * L / (t_cs + t_fwd)}
+    del d, dH, dHs, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def traffic_record(kernel, workload, sources=None):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; else None."""
@@ -372,6 +416,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-rms", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run each hot kernel a few times for a hardware-counter pass, then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -449,6 +494,8 @@ def main():
     }
     del d, dH, out
     torch.cuda.empty_cache()
+    if not args.no_rms:
+        result["rms"] = time_rms(torch, dart, synth, cfg)
     if not args.no_backward:
         result["backward"] = time_backward(torch, dart, synth, cfg)
     if not args.no_decode:

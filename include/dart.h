@@ -12,6 +12,10 @@
  *   - decode-side cache maintenance   dart_decode_state_update  [§2 Eq. 2; §4]
  *   - gradients of the SMA branch     dart_sma_bwd        [§4 "Efficient Training";
  *     and of the chunk states         dart_chunk_states_bwd   App. C Eq. 33-35]
+ *   - the RMS-normalised score        dart_chunk_states_rms, dart_chunk_rms,
+ *     branch                          dart_sma_fwd_rms, dart_sma_decode_rms,
+ *                                     dart_decode_state_update_rms
+ *                                     [§3 text after Eq. 10; App. B.1 Eq. 25-27]
  *
  * Notation: b = batch, L = sequence length, H = heads, G = projection groups
  * (B, C, Q, E are shared by the H/G consecutive heads of a group; head h reads
@@ -200,6 +204,69 @@ int dart_chunk_states_bwd(const dart_dims_t* dims, int dtype, const void* X, con
                           const float* A, const float* d_dH, float* dX, float* dB, float* dA,
                           void* workspace, size_t workspace_bytes, void* stream);
 size_t dart_chunk_states_bwd_workspace_bytes(const dart_dims_t* dims);
+
+/* ---- RMS-normalised score branch [§3 text after Eq. 10; App. B.1 Eq. 25-27].
+ * Only the logits change:
+ *   l_tc = RMSNorm(Q_t) . (r_c * (dH_c RMSNorm(E_t))) / sqrt(N),
+ *   RMSNorm(x) = x / sqrt(mean(x^2) + eps) * w   (w: optional per-channel
+ *                weight, w_q [N] for Q and w_e [P] for E, float32; NULL = 1),
+ *   r_c[n] = (mean_p dH_c[n][p]^2 + eps)^(-1/2)   (inverse RMS of each key
+ *                row of a chunk memory along the value axis, Eq. 26);
+ * V = C_t dH_c, the softmax over chunks, lse and the gated residual are those
+ * of dart_sma_fwd / dart_sma_decode.  One eps serves the two RMSNorms and r_c
+ * (eps >= 0; with eps = 0 an all-zero key row gives r = inf).
+ *
+ * The forward consumes the chunk side of the normalisation precomputed once
+ * per chunk, the score memory
+ *   dHs_c[p][n] = w_e[p] * dH_c[p][n] * r_c[n] * w_q[n]    (dH layout),
+ * stored in float16 for bfloat16 inputs (|entries| <= sqrt(P) max|w_q| max|w_e|,
+ * and float16 keeps three more mantissa bits than bfloat16) and in float32
+ * for float32 inputs.  Decode reads r_c from the cache instead. */
+
+/* Chunk state memories as dart_chunk_states, plus r [b][H][M][N] float32 and
+ * the score memory dH_score [b][H][M][P][N] (float16 or float32, see above),
+ * both computed from dH as stored (after its rounding to dtype).  r and
+ * dH_score are optional (NULL skips them); w_q [N] and w_e [P] are the
+ * RMSNorm weights folded into dH_score (NULL = 1; 4-byte alignment). */
+int dart_chunk_states_rms(const dart_dims_t* dims, int dtype, const void* X, const void* B,
+                          const float* A, float eps, const float* w_q, const float* w_e, void* dH,
+                          float* r, void* dH_score, void* stream);
+
+/* r and the score memory of given chunk memories (any source, e.g. a cache
+ * filled elsewhere): dims->seqlen and dims->chunk give M = ceil(L/S) memories
+ * per (b, h) as for dart_chunk_states.  dH [b][H][M][P][N] (dtype) in,
+ * r [b][H][M][N] float32 and dH_score out (either may be NULL). */
+int dart_chunk_rms(const dart_dims_t* dims, int dtype, const void* dH, float eps, const float* w_q,
+                   const float* w_e, float* r, void* dH_score, void* stream);
+
+/* SMA forward with the normalised score branch and the gated residual.
+ * Arguments as dart_sma_fwd, plus dH_score from dart_chunk_states_rms (with
+ * the RMSNorm weights already folded in) and eps for the RMSNorm of Q_t and
+ * E_t. */
+int dart_sma_fwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const void* C,
+                     const void* E, const void* dH, const void* dH_score, const void* Y_ssm,
+                     const void* gate, int gate_per_channel, float eps, void* out, float* R,
+                     float* lse, void* stream);
+
+/* Decode with the normalised score branch.  Arguments as dart_sma_decode,
+ * plus r_cache [b][H][max_chunks][N] float32 (r_c of every cached chunk, as
+ * written by dart_decode_state_update_rms or dart_chunk_states_rms), eps and
+ * the RMSNorm weights w_q [N], w_e [P] (NULL = 1; 4-byte alignment).  The
+ * workspace is sized by dart_sma_decode_workspace_bytes. */
+int dart_sma_decode_rms(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                        const void* c, const void* e, const void* cache, const float* r_cache,
+                        const int32_t* n_chunks, const void* y_ssm, const void* gate,
+                        int gate_per_channel, float eps, const float* w_q, const float* w_e,
+                        void* out, float* R, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* dart_decode_state_update, and for every chunk it closes also
+ * r_cache[b][h][chunk][n] = r_c[n] of the memory as cached (float32,
+ * [b][H][max_chunks][N], 16-byte aligned). */
+int dart_decode_state_update_rms(const dart_dims_t* dims, int dtype, int64_t max_chunks, float eps,
+                                 const void* x, const void* B, const float* a, float* state,
+                                 const int32_t* pos, void* cache, float* r_cache, int32_t* n_chunks,
+                                 void* stream);
 
 const char* dart_status_string(int status);
 /* Message for this thread's last failing call ("" if none). */

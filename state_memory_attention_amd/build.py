@@ -30,6 +30,8 @@ SOURCES = [
     "backward_general.hip",
     "decode_update.hip",
     "sma_bwd_mfma.hip",
+    "rms_general.hip",
+    "sma_fwd_rms_mfma.hip",
 ]
 # A plain 16-byte-vector copy kernel in its own library, used only to
 # calibrate hardware memory-traffic counters (bench.py --profile-kernels).

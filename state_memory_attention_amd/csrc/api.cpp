@@ -5,6 +5,7 @@
 
 #include <stdarg.h>
 #include <stdint.h>
+#include <math.h>
 #include <stdio.h>
 
 #include <initializer_list>
@@ -188,12 +189,18 @@ int dart_chunk_states(const dart_dims_t* dims, int dtype, const void* X, const v
                     "dart_chunk_states");
 }
 
-int dart_sma_fwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
-                 const void* dH, const void* Y_ssm, const void* gate, int gate_per_channel,
-                 void* out, float* R, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// dart_sma_fwd and dart_sma_fwd_rms (rms: dHs is the score memory).
+int sma_fwd_impl(const dart_dims_t* dims, int dtype, bool rms, float eps, const void* Q, const void* C,
+                 const void* E, const void* dH, const void* dHs, const void* Y_ssm, const void* gate,
+                 int gate_per_channel, void* out, float* R, float* lse, void* stream) {
   t_err[0] = '\0';
   int st = check_dims(dims, dtype, true);
   if (st) return st;
+  if (rms && !(eps >= 0.f && eps < INFINITY)) return fail(DART_ERR_SHAPE, "eps must be finite and >= 0");
   const dart::Shape s = make_shape(dims);
   if (s.b == 0 || s.L == 0) return DART_OK;
   const int64_t es = dtype == DART_BF16 ? 2 : 4;
@@ -202,23 +209,120 @@ int dart_sma_fwd(const dart_dims_t* dims, int dtype, const void* Q, const void* 
   const Buf bc{C, prod({s.b, s.L, s.G, s.N}) * es, "C"};
   const Buf be{E, prod({s.b, s.L, s.G, s.P}) * es, "E"};
   const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf bs{dHs, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH_score"};
   const Buf by{Y_ssm, prod({s.b, s.L, s.H, s.P}) * es, "Y_ssm"};
   const Buf bg{gate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * es, "gate"};
   const Buf bo{out, prod({s.b, s.L, s.H, s.P}) * es, "out"};
   const Buf br{R, prod({s.b, s.L, s.H, s.P}) * 4, "R"};
   const Buf bl{lse, prod({s.b, s.H, s.L}) * 4, "lse"};
   if ((st = check_ptrs({bq, bc, be, bd, by, bg, bo}))) return st;
+  if (rms && (st = check_ptrs({bs}))) return st;
   if ((st = check_opt_align(R, "R")) || (st = check_opt_align(lse, "lse"))) return st;
-  if ((st = check_alias({bo, br, bl}, {bq, bc, be, bd, by, bg}, out, Y_ssm))) return st;
+  if ((st = check_alias({bo, br, bl}, {bq, bc, be, bd, by, bg, rms ? bs : Buf{nullptr, 0, ""}}, out, Y_ssm)))
+    return st;
   if (prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "b * H * L is too large for one launch");
   hipStream_t strm = (hipStream_t)stream;
+  const bool bf16 = dtype == DART_BF16;
+  if (rms && use_mfma(dtype, dims))
+    return hip_status(dart::launch_sma_fwd_rms_mfma(s, eps, Q, C, E, dH, dHs, Y_ssm, gate, gpc, out, R, lse,
+                                                    strm),
+                      "dart_sma_fwd_rms");
+  if (rms)
+    return hip_status(dart::launch_sma_fwd_rms_general(s, bf16, eps, Q, C, E, dH, dHs, Y_ssm, gate, gpc, out,
+                                                       R, lse, strm),
+                      "dart_sma_fwd_rms");
   if (use_mfma(dtype, dims))
     return hip_status(dart::launch_sma_fwd_mfma(s, Q, C, E, dH, Y_ssm, gate, gpc, out, R, lse, strm),
                       "dart_sma_fwd");
-  return hip_status(dart::launch_sma_fwd_general(s, dtype == DART_BF16, Q, C, E, dH, Y_ssm, gate, gpc,
-                                                 out, R, lse, strm),
+  return hip_status(dart::launch_sma_fwd_general(s, bf16, Q, C, E, dH, Y_ssm, gate, gpc, out, R, lse, strm),
                     "dart_sma_fwd");
+}
+
+// Weights of an RMSNorm: NULL or n float32 values at 4-byte alignment.
+int check_weight(const float* w, const char* name) {
+  if (w != nullptr && ((uintptr_t)w & 3u) != 0) return fail(DART_ERR_ALIGN, "%s is not 4-byte aligned", name);
+  return DART_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dart_sma_fwd(const dart_dims_t* dims, int dtype, const void* Q, const void* C, const void* E,
+                 const void* dH, const void* Y_ssm, const void* gate, int gate_per_channel,
+                 void* out, float* R, float* lse, void* stream) {
+  return sma_fwd_impl(dims, dtype, false, 0.f, Q, C, E, dH, nullptr, Y_ssm, gate, gate_per_channel, out, R,
+                      lse, stream);
+}
+
+int dart_sma_fwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const void* C,
+                     const void* E, const void* dH, const void* dH_score, const void* Y_ssm,
+                     const void* gate, int gate_per_channel, float eps, void* out, float* R,
+                     float* lse, void* stream) {
+  return sma_fwd_impl(dims, dtype, true, eps, Q, C, E, dH, dH_score, Y_ssm, gate, gate_per_channel, out, R,
+                      lse, stream);
+}
+
+int dart_chunk_rms(const dart_dims_t* dims, int dtype, const void* dH, float eps, const float* w_q,
+                   const float* w_e, float* r, void* dH_score, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  if (!(eps >= 0.f && eps < INFINITY)) return fail(DART_ERR_SHAPE, "eps must be finite and >= 0");
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf bwq{w_q, s.N * 4, "w_q"};
+  const Buf bwe{w_e, s.P * 4, "w_e"};
+  const Buf br{r, prod({s.b, s.H, s.M, s.N}) * 4, "r"};
+  const Buf bs{dH_score, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH_score"};
+  if ((st = check_ptrs({bd}))) return st;
+  if ((st = check_weight(w_q, "w_q")) || (st = check_weight(w_e, "w_e"))) return st;
+  if ((st = check_opt_align(r, "r")) || (st = check_opt_align(dH_score, "dH_score"))) return st;
+  if ((st = check_alias({br, bs}, {bd, bwq, bwe}, nullptr, nullptr))) return st;
+  if (prod({s.b, s.H, s.M}) >= kMaxIndex) return fail(DART_ERR_SHAPE, "b * H * M is too large for one launch");
+  if (r == nullptr && dH_score == nullptr) return DART_OK;
+  return hip_status(dart::launch_chunk_rms(s, dtype == DART_BF16, eps, dH, w_q, w_e, r, dH_score,
+                                           (hipStream_t)stream),
+                    "dart_chunk_rms");
+}
+
+int dart_chunk_states_rms(const dart_dims_t* dims, int dtype, const void* X, const void* B,
+                          const float* A, float eps, const float* w_q, const float* w_e, void* dH,
+                          float* r, void* dH_score, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  if (!(eps >= 0.f && eps < INFINITY)) return fail(DART_ERR_SHAPE, "eps must be finite and >= 0");
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const Buf bx{X, prod({s.b, s.L, s.H, s.P}) * es, "X"};
+  const Buf bb{B, prod({s.b, s.L, s.G, s.N}) * es, "B"};
+  const Buf ba{A, prod({s.b, s.L, s.H}) * 4, "A"};
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf bwq{w_q, s.N * 4, "w_q"};
+  const Buf bwe{w_e, s.P * 4, "w_e"};
+  const Buf br{r, prod({s.b, s.H, s.M, s.N}) * 4, "r"};
+  const Buf bs{dH_score, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH_score"};
+  if ((st = check_ptrs({bx, bb, ba, bd}))) return st;
+  if ((st = check_weight(w_q, "w_q")) || (st = check_weight(w_e, "w_e"))) return st;
+  if ((st = check_opt_align(r, "r")) || (st = check_opt_align(dH_score, "dH_score"))) return st;
+  if ((st = check_alias({bd, br, bs}, {bx, bb, ba, bwq, bwe}, nullptr, nullptr))) return st;
+  const int64_t tiles = (s.N * s.P + 255) / 256;
+  if (prod({s.b, s.H, s.M, tiles}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "b * H * M is too large for one launch");
+  hipStream_t strm = (hipStream_t)stream;
+  const bool bf16 = dtype == DART_BF16;
+  if (use_mfma(dtype, dims))  // r and the score memory come from the same kernel's epilogue
+    return hip_status(dart::launch_chunk_states_mfma(s, X, B, A, dH, strm, eps, w_q, w_e, r, dH_score),
+                      "dart_chunk_states_rms");
+  st = hip_status(dart::launch_chunk_states_general(s, bf16, X, B, A, dH, strm), "dart_chunk_states_rms");
+  if (st || (r == nullptr && dH_score == nullptr)) return st;
+  return hip_status(dart::launch_chunk_rms(s, bf16, eps, dH, w_q, w_e, r, dH_score, strm),
+                    "dart_chunk_states_rms");
 }
 
 size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chunks) {
@@ -228,13 +332,20 @@ size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chun
   return dart::decode_plan(dims->batch, dims->nheads, dims->d_head, max_chunks).workspace_bytes;
 }
 
-int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
-                    const void* c, const void* e, const void* cache, const int32_t* n_chunks,
-                    const void* y_ssm, const void* gate, int gate_per_channel, void* out,
-                    float* R, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// dart_sma_decode and dart_sma_decode_rms (rms: r_cache and the weights).
+int sma_decode_impl(const dart_dims_t* dims, int dtype, int64_t max_chunks, bool rms, float eps,
+                    const void* q, const void* c, const void* e, const void* cache, const float* r_cache,
+                    const int32_t* n_chunks, const float* w_q, const float* w_e, const void* y_ssm,
+                    const void* gate, int gate_per_channel, void* out, float* R, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   t_err[0] = '\0';
   int st = check_dims(dims, dtype, false);
   if (st) return st;
+  if (rms && !(eps >= 0.f && eps < INFINITY)) return fail(DART_ERR_SHAPE, "eps must be finite and >= 0");
   if (max_chunks < 0) return fail(DART_ERR_SHAPE, "max_chunks = %lld < 0", (long long)max_chunks);
   if (max_chunks >= kMaxIndex) return fail(DART_ERR_SHAPE, "max_chunks must be < 2^31");
   dart::Shape s = make_shape(dims);
@@ -255,7 +366,14 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
   const Buf bl{lse, prod({s.b, s.H}) * 4, "lse"};
   const dart::DecodePlan plan = dart::decode_plan(s.b, s.H, s.P, max_chunks);
   const Buf bw{workspace, (int64_t)plan.workspace_bytes, "workspace"};
+  const Buf brc{r_cache, prod({s.b, s.H, max_chunks, s.N}) * 4, "r_cache"};
+  const Buf bwq{w_q, s.N * 4, "w_q"};
+  const Buf bwe{w_e, s.P * 4, "w_e"};
   if (max_chunks > 0 && cache == nullptr) return fail(DART_ERR_NULL, "cache is NULL");
+  if (rms && max_chunks > 0 && r_cache == nullptr) return fail(DART_ERR_NULL, "r_cache is NULL");
+  if (rms && ((st = check_opt_align(r_cache, "r_cache")) || (st = check_weight(w_q, "w_q")) ||
+              (st = check_weight(w_e, "w_e"))))
+    return st;
   if ((st = check_ptrs({bq, bc, be, by, bg, bo}))) return st;
   if ((st = check_opt_align(cache, "cache")) || (st = check_opt_align(R, "R")) ||
       (st = check_opt_align(lse, "lse")) || (st = check_opt_align(n_chunks, "n_chunks")))
@@ -265,25 +383,64 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
                 plan.workspace_bytes);
   if ((st = check_opt_align(workspace, "workspace"))) return st;
   const Buf bn{n_chunks, s.b * 4, "n_chunks"};
-  if ((st = check_alias({bo, br, bl, bw}, {bq, bc, be, bk, by, bg, bn}, out, y_ssm))) return st;
+  if ((st = check_alias({bo, br, bl, bw}, {bq, bc, be, bk, by, bg, bn, brc, bwq, bwe}, out, y_ssm))) return st;
   if (prod({s.b, s.H, plan.splits}) >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "b * H is too large for one launch");
   hipStream_t strm = (hipStream_t)stream;
+  if (rms && use_mfma(dtype, dims))
+    return hip_status(dart::launch_sma_decode_mfma(s, max_chunks, plan, q, c, e, cache, n_chunks, y_ssm, gate,
+                                                   gpc, out, R, lse, (float*)workspace, r_cache, w_q, w_e,
+                                                   eps, strm),
+                      "dart_sma_decode_rms");
+  if (rms)
+    return hip_status(dart::launch_sma_decode_rms_general(s, dtype == DART_BF16, max_chunks, eps, q, c, e,
+                                                          cache, r_cache, n_chunks, w_q, w_e, y_ssm, gate,
+                                                          gpc, out, R, lse, strm),
+                      "dart_sma_decode_rms");
   if (use_mfma(dtype, dims))
     return hip_status(dart::launch_sma_decode_mfma(s, max_chunks, plan, q, c, e, cache, n_chunks, y_ssm,
-                                                   gate, gpc, out, R, lse, (float*)workspace, strm),
+                                                   gate, gpc, out, R, lse, (float*)workspace, nullptr,
+                                                   nullptr, nullptr, 0.f, strm),
                       "dart_sma_decode");
   return hip_status(dart::launch_sma_decode_general(s, dtype == DART_BF16, max_chunks, q, c, e, cache,
                                                     n_chunks, y_ssm, gate, gpc, out, R, lse, strm),
                     "dart_sma_decode");
 }
 
-int dart_decode_state_update(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* x,
-                             const void* B, const float* a, float* state, const int32_t* pos,
-                             void* cache, int32_t* n_chunks, void* stream) {
+}  // namespace
+
+extern "C" {
+
+int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                    const void* c, const void* e, const void* cache, const int32_t* n_chunks,
+                    const void* y_ssm, const void* gate, int gate_per_channel, void* out,
+                    float* R, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return sma_decode_impl(dims, dtype, max_chunks, false, 0.f, q, c, e, cache, nullptr, n_chunks, nullptr,
+                         nullptr, y_ssm, gate, gate_per_channel, out, R, lse, workspace, workspace_bytes,
+                         stream);
+}
+
+int dart_sma_decode_rms(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                        const void* c, const void* e, const void* cache, const float* r_cache,
+                        const int32_t* n_chunks, const void* y_ssm, const void* gate,
+                        int gate_per_channel, float eps, const float* w_q, const float* w_e,
+                        void* out, float* R, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return sma_decode_impl(dims, dtype, max_chunks, true, eps, q, c, e, cache, r_cache, n_chunks, w_q, w_e,
+                         y_ssm, gate, gate_per_channel, out, R, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_update_impl(const dart_dims_t* dims, int dtype, int64_t max_chunks, bool rms, float eps,
+                       const void* x, const void* B, const float* a, float* state, const int32_t* pos,
+                       void* cache, float* r_cache, int32_t* n_chunks, void* stream) {
   t_err[0] = '\0';
   int st = check_dims(dims, dtype, false);
   if (st) return st;
+  if (rms && !(eps >= 0.f && eps < INFINITY)) return fail(DART_ERR_SHAPE, "eps must be finite and >= 0");
   if (dims->chunk <= 0) return fail(DART_ERR_SHAPE, "chunk = %lld must be > 0", (long long)dims->chunk);
   if (max_chunks < 0) return fail(DART_ERR_SHAPE, "max_chunks = %lld < 0", (long long)max_chunks);
   if (max_chunks >= kMaxIndex) return fail(DART_ERR_SHAPE, "max_chunks must be < 2^31");
@@ -300,6 +457,7 @@ int dart_decode_state_update(const dart_dims_t* dims, int dtype, int64_t max_chu
   const Buf bp{pos, s.b * 4, "pos"};
   const Buf bk{cache, prod({s.b, s.H, max_chunks, s.P, s.N}) * es, "cache"};
   const Buf bn{n_chunks, s.b * 4, "n_chunks"};
+  const Buf brc{r_cache, prod({s.b, s.H, max_chunks, s.N}) * 4, "r_cache"};
   // x, B, a, pos are read element by element: per-token slices of larger
   // tensors are accepted at element alignment; state and cache are accessed
   // in 16-byte vectors.
@@ -312,13 +470,36 @@ int dart_decode_state_update(const dart_dims_t* dims, int dtype, int64_t max_chu
   if ((st = check_ptrs({bs}))) return st;
   if (max_chunks > 0 && cache == nullptr) return fail(DART_ERR_NULL, "cache is NULL");
   if ((st = check_opt_align(cache, "cache"))) return st;
+  if (rms && max_chunks > 0 && r_cache == nullptr) return fail(DART_ERR_NULL, "r_cache is NULL");
+  if (rms && (st = check_opt_align(r_cache, "r_cache"))) return st;
   if (n_chunks != nullptr && ((uintptr_t)n_chunks & 3u) != 0)
     return fail(DART_ERR_ALIGN, "n_chunks is not 4-byte aligned");
-  if ((st = check_alias({bs, bk, bn}, {bx, bb, ba, bp}, nullptr, nullptr))) return st;
+  if ((st = check_alias({bs, bk, bn, rms ? brc : Buf{nullptr, 0, ""}}, {bx, bb, ba, bp}, nullptr, nullptr)))
+    return st;
   if (prod({s.b, s.H}) >= kMaxIndex) return fail(DART_ERR_SHAPE, "b * H is too large for one launch");
   return hip_status(dart::launch_decode_update(s, dtype == DART_BF16, max_chunks, x, B, a, state, pos,
-                                               cache, n_chunks, (hipStream_t)stream),
-                    "dart_decode_state_update");
+                                               cache, n_chunks, rms ? r_cache : nullptr, eps,
+                                               (hipStream_t)stream),
+                    rms ? "dart_decode_state_update_rms" : "dart_decode_state_update");
+}
+
+}  // namespace
+
+extern "C" {
+
+int dart_decode_state_update(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* x,
+                             const void* B, const float* a, float* state, const int32_t* pos,
+                             void* cache, int32_t* n_chunks, void* stream) {
+  return decode_update_impl(dims, dtype, max_chunks, false, 0.f, x, B, a, state, pos, cache, nullptr,
+                            n_chunks, stream);
+}
+
+int dart_decode_state_update_rms(const dart_dims_t* dims, int dtype, int64_t max_chunks, float eps,
+                                 const void* x, const void* B, const float* a, float* state,
+                                 const int32_t* pos, void* cache, float* r_cache, int32_t* n_chunks,
+                                 void* stream) {
+  return decode_update_impl(dims, dtype, max_chunks, true, eps, x, B, a, state, pos, cache, r_cache,
+                            n_chunks, stream);
 }
 
 size_t dart_sma_bwd_workspace_bytes(const dart_dims_t* dims) {

@@ -27,6 +27,7 @@
 // float32, rounded once to bf16.  Underflow to zero is the correct value.
 #include "dart_internal.h"
 #include "dev_common.h"
+#include "lds_dma.h"
 
 namespace dart {
 namespace {
@@ -48,27 +49,17 @@ struct CsArgs {
   const bf16_t* B;
   const float* A;
   bf16_t* dH;
+  // RMS-normalised score branch (all nullable): inverse RMS of each key row
+  // r [b][H][M][N] and the float16 score memory, RMSNorm weights folded in
+  float* r;
+  _Float16* dHs;
+  const float* wq;
+  const float* we;
+  float eps;
   int64_t L;
   int H, G, hpg, S, M;
 };
 
-
-// Direct global->LDS load through a buffer resource: every lane fetches 16
-// bytes at byte `voff` of [base, base + nbytes) (past the end: zeros), and
-// lane l's bytes land at lds + 16 l.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
-  // word 3: 32-bit data format, the value every gfx9 raw buffer access uses
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
-}
-__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
-                                           0, 0, 0);
-}
-
-// LDS byte address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Six transposing reads (4 bf16 = 8 bytes each) that return together.  The
 // compiler treats its own form of this read as possibly overlapping the
@@ -93,12 +84,9 @@ __device__ __forceinline__ void ld_tr6(uint64_t (&o)[6], const uint32_t (&ad)[6]
 __device__ __forceinline__ int swz_x(int row) { return (row & 3) << 1; }
 __device__ __forceinline__ int swz_b(int row) { return (row & 3) << 2; }
 
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt
-// in 11:8; a field at its maximum does not wait).
-constexpr unsigned kWaitVm0 = 0x0f70;
+// s_waitcnt immediates beyond the shared ones: vmcnt(6), vmcnt(12)
 constexpr unsigned kWaitVm6 = 0x0f76;
 constexpr unsigned kWaitVm12 = 0x0f7c;
-constexpr unsigned kWaitLgkm0 = 0xc07f;
 
 // Block barrier for data exchanged through LDS only.  __syncthreads() would
 // also wait for every outstanding global->LDS load (its fence covers global
@@ -124,6 +112,7 @@ __device__ __forceinline__ void barrier_loads(int n) {
   asm volatile("" ::: "memory");
 }
 
+template <bool kRms>
 __global__ __launch_bounds__(kThreads) void chunk_states_mfma_kernel(CsArgs a) {
   // Sub-block ring, and (a separate object, so that reading it does not make
   // the compiler wait for the loads into the ring) the current group's
@@ -277,20 +266,55 @@ __global__ __launch_bounds__(kThreads) void chunk_states_mfma_kernel(CsArgs a) {
   }
 
   // D[p][n]: register r of row block rb is p = 32 rb + 8 (r/4) + 4 half + r%4
-  bf16_t* outp = a.dH + ((int64_t)bh * a.M + c) * (kP * kN) + 32 * wave + (lane & 31);
+  const int64_t mem = ((int64_t)bh * a.M + c) * (kP * kN);
+  const int n = 32 * wave + (lane & 31);
+  bf16_t* outp = a.dH + mem + n;
+  uint32_t h0[16], h1[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int p = 8 * (r >> 2) + 4 * half + (r & 3);
-    outp[p * kN] = (bf16_t)f32_to_bf16(acc0[r]);
-    outp[(32 + p) * kN] = (bf16_t)f32_to_bf16(acc1[r]);
+    h0[r] = f32_to_bf16(acc0[r]);
+    h1[r] = f32_to_bf16(acc1[r]);
+    outp[p * kN] = (bf16_t)h0[r];
+    outp[(32 + p) * kN] = (bf16_t)h1[r];
+  }
+  if (kRms) {
+    // r_c[n] = (mean_p dH[p][n]^2 + eps)^(-1/2) of the memory as stored
+    // [App. B.1 Eq. 26]: this lane holds 32 of the 64 p of key row n, lane
+    // l ^ 32 the others; then the score memory w_e[p] dH[p][n] r[n] w_q[n]
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x0 = bf16_to_f32(h0[r]), x1 = bf16_to_f32(h1[r]);
+      ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+    }
+    const float rn = 1.f / sqrtf(halves_sum(ss) * (1.f / kP) + a.eps);
+    if (a.r && half == 0) a.r[((int64_t)bh * a.M + c) * kN + n] = rn;
+    if (a.dHs) {
+      const float rq = a.wq ? rn * a.wq[n] : rn;
+      _Float16* sp = a.dHs + mem + n;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = 8 * (r >> 2) + 4 * half + (r & 3);
+        const float w0 = a.we ? a.we[p] : 1.f, w1 = a.we ? a.we[32 + p] : 1.f;
+        sp[p * kN] = (_Float16)(bf16_to_f32(h0[r]) * rq * w0);
+        sp[(32 + p) * kN] = (_Float16)(bf16_to_f32(h1[r]) * rq * w1);
+      }
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_chunk_states_mfma(const Shape& s, const void* X, const void* B, const float* A,
-                                    void* dH, hipStream_t st) {
+                                    void* dH, hipStream_t st, float eps, const float* wq,
+                                    const float* we, float* r, void* dHs) {
   CsArgs a;
+  a.r = r;
+  a.dHs = (_Float16*)dHs;
+  a.wq = wq;
+  a.we = we;
+  a.eps = eps;
   a.X = (const bf16_t*)X;
   a.B = (const bf16_t*)B;
   a.A = A;
@@ -303,7 +327,10 @@ hipError_t launch_chunk_states_mfma(const Shape& s, const void* X, const void* B
   a.M = (int)s.M;
   const int64_t blocks = s.b * s.H * s.M;
   if (blocks == 0) return hipSuccess;
-  chunk_states_mfma_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  if (r || dHs)
+    chunk_states_mfma_kernel<true><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  else
+    chunk_states_mfma_kernel<false><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 

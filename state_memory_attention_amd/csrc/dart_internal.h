@@ -24,9 +24,26 @@ hipError_t launch_sma_decode_general(const Shape& s, bool bf16, int64_t max_chun
                                      int gate_pc, void* out, float* R, float* lse, hipStream_t st);
 
 // ---- decode-side cache maintenance (any N, P) -----------------------------
+// r_cache (nullable): inverse RMS of every chunk closed by the call
 hipError_t launch_decode_update(const Shape& s, bool bf16, int64_t max_chunks, const void* x,
                                 const void* B, const float* a, float* state, const int32_t* pos,
-                                void* cache, int32_t* n_chunks, hipStream_t st);
+                                void* cache, int32_t* n_chunks, float* r_cache, float eps,
+                                hipStream_t st);
+
+// ---- RMS-normalised score branch (general kernels; r and the score memory
+// from dH as stored: float16 score memory for bfloat16, float32 otherwise) --
+hipError_t launch_chunk_rms(const Shape& s, bool bf16, float eps, const void* dH, const float* wq,
+                            const float* we, float* r, void* dHs, hipStream_t st);
+hipError_t launch_sma_fwd_rms_general(const Shape& s, bool bf16, float eps, const void* Q,
+                                      const void* C, const void* E, const void* dH, const void* dHs,
+                                      const void* Y, const void* gate, int gate_pc, void* out,
+                                      float* R, float* lse, hipStream_t st);
+hipError_t launch_sma_decode_rms_general(const Shape& s, bool bf16, int64_t max_chunks, float eps,
+                                         const void* q, const void* c, const void* e,
+                                         const void* cache, const float* r_cache,
+                                         const int32_t* n_chunks, const float* wq, const float* we,
+                                         const void* y, const void* gate, int gate_pc, void* out,
+                                         float* R, float* lse, hipStream_t st);
 
 // ---- backward, general kernels -------------------------------------------
 size_t sma_bwd_workspace_bytes(const Shape& s);
@@ -46,11 +63,21 @@ hipError_t launch_chunk_states_bwd_mfma(const Shape& s, const void* X, const voi
                                         float* wsw, float* wsdw, hipStream_t st);
 
 // ---- MFMA kernels (bfloat16, N = 128, P = 64) -----------------------------
+// With r or dHs (the RMS-normalised score branch) the epilogue also writes
+// the inverse RMS of every key row and the float16 score memory.
 hipError_t launch_chunk_states_mfma(const Shape& s, const void* X, const void* B, const float* A,
-                                    void* dH, hipStream_t st);
+                                    void* dH, hipStream_t st, float eps = 0.f,
+                                    const float* wq = nullptr, const float* we = nullptr,
+                                    float* r = nullptr, void* dHs = nullptr);
 hipError_t launch_sma_fwd_mfma(const Shape& s, const void* Q, const void* C, const void* E,
                                const void* dH, const void* Y, const void* gate, int gate_pc,
                                void* out, float* R, float* lse, hipStream_t st);
+
+// RMS-normalised forward on the matrix core (float16 score memory)
+hipError_t launch_sma_fwd_rms_mfma(const Shape& s, float eps, const void* Q, const void* C,
+                                   const void* E, const void* dH, const void* dHs, const void* Y,
+                                   const void* gate, int gate_pc, void* out, float* R, float* lse,
+                                   hipStream_t st);
 
 // Backward on the matrix core: pass A (recompute, p and dl, dE, dgate, dR),
 // pass BC (dQ, dC), pass D (d_dH); per-head partials summed over groups.
@@ -80,10 +107,12 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 DecodePlan decode_plan(int64_t b, int64_t H, int64_t P, int64_t max_chunks);
+// r_cache non-null selects the RMS-normalised score branch (weights nullable)
 hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const DecodePlan& plan,
                                   const void* q, const void* c, const void* e, const void* cache,
                                   const int32_t* n_chunks, const void* y, const void* gate,
                                   int gate_pc, void* out, float* R, float* lse, float* ws,
+                                  const float* r_cache, const float* wq, const float* we, float eps,
                                   hipStream_t st);
 
 }  // namespace dart

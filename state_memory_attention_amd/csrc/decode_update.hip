@@ -1,6 +1,7 @@
 // Decode-side cache maintenance: the in-progress chunk memory of every
 // (batch row, head) absorbs one new token, and a chunk that the token closes
-// is appended to the chunk-memory cache.
+// is appended to the chunk-memory cache (with its inverse RMS along the value
+// axis when the normalised score branch is in use, App. B.1 Eq. 26).
 //
 // Paper: "DART: Decoded Attention over Recurrent States for Efficient
 // Long-Context Sequence Modeling" (arXiv 2608.02032).  The cache holds one
@@ -27,7 +28,8 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void decode_update_kernel(
     int64_t H, int64_t G, int N, int P, int64_t S, int64_t max_chunks, const T* __restrict__ x,
     const T* __restrict__ B, const float* __restrict__ a, float* __restrict__ state,
-    const int32_t* __restrict__ pos, T* __restrict__ cache, int32_t* __restrict__ n_chunks) {
+    const int32_t* __restrict__ pos, T* __restrict__ cache, int32_t* __restrict__ n_chunks,
+    float* __restrict__ r_cache, float eps) {
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / H, h = bh % H, g = h / (H / G);
   const int64_t t = pos[b];
@@ -76,23 +78,37 @@ __global__ __launch_bounds__(kThreads) void decode_update_kernel(
       }
     }
   }
+  // Inverse RMS of the memory just closed, along the value axis, from the
+  // values as cached [App. B.1 Eq. 26]: read back after the block's stores.
+  if (r_cache && dst) {
+    __syncthreads();
+    for (int n = threadIdx.x; n < N; n += kThreads) {
+      float ss = 0.f;
+      for (int p = 0; p < P; ++p) {
+        const float v = Elem<T>::ld(dst, (int64_t)p * N + n);
+        ss = fmaf(v, v, ss);
+      }
+      r_cache[(bh * max_chunks + c) * N + n] = 1.f / sqrtf(ss / (float)P + eps);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_update(const Shape& s, bool bf16, int64_t max_chunks, const void* x,
                                 const void* B, const float* a, float* state, const int32_t* pos,
-                                void* cache, int32_t* n_chunks, hipStream_t st) {
+                                void* cache, int32_t* n_chunks, float* r_cache, float eps,
+                                hipStream_t st) {
   const int64_t blocks = s.b * s.H;
   if (blocks == 0) return hipSuccess;
   if (bf16)
     decode_update_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
         s.H, s.G, (int)s.N, (int)s.P, s.S, max_chunks, (const bf16_t*)x, (const bf16_t*)B, a, state,
-        pos, (bf16_t*)cache, n_chunks);
+        pos, (bf16_t*)cache, n_chunks, r_cache, eps);
   else
     decode_update_kernel<float><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
         s.H, s.G, (int)s.N, (int)s.P, s.S, max_chunks, (const float*)x, (const float*)B, a, state, pos,
-        (float*)cache, n_chunks);
+        (float*)cache, n_chunks, r_cache, eps);
   return hipGetLastError();
 }
 

@@ -48,6 +48,11 @@ template <> struct Elem<bf16_t> {
   __device__ static float ld(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ static void st(bf16_t* p, int64_t i, float v) { p[i] = (bf16_t)f32_to_bf16(v); }
 };
+// float16 storage (the score memory of bfloat16 inputs): round to nearest even
+template <> struct Elem<_Float16> {
+  __device__ static float ld(const _Float16* p, int64_t i) { return (float)p[i]; }
+  __device__ static void st(_Float16* p, int64_t i, float v) { p[i] = (_Float16)v; }
+};
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

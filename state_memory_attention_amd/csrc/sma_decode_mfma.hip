@@ -17,6 +17,14 @@
 //   * the 4 waves merge their (max, sum, O) states through LDS and write one
 //     partial per range to the workspace; a second kernel merges the ranges
 //     of each (b, h) in a fixed order (deterministic) and applies the gate.
+//
+// With the RMS-normalised score branch [App. B.1 Eq. 25-27] the query row of
+// A becomes RMSNorm(q) w_q r_j, which changes per chunk: it is formed in
+// float32 from r_j (read from the r cache beside each memory) and split into
+// a bfloat16 high part (row 0) and the bfloat16 rounding of the remainder
+// (row 2), so W = row 0 + row 2 of the product carries ~16 mantissa bits of
+// the scaled query; the two extra rows cost nothing on the 16-row matrix op.
+// RMSNorm(e) w_e and the per-token scales are folded into e once.
 #include "dart_internal.h"
 #include "dev_common.h"
 
@@ -35,10 +43,14 @@ struct DecArgs {
   const bf16_t* e;
   const bf16_t* cache;
   const int32_t* n_chunks;
+  const float* r_cache;  // normalised branch: [b][H][max_chunks][N]
+  const float* wq;       // normalised branch: RMSNorm weights (nullable)
+  const float* we;
   float* ws;
   int64_t max_chunks;
   int H, G, hpg, splits, cps;
   float e_scale;
+  float eps;
 };
 
 __device__ __forceinline__ int64_t valid_chunks(const DecArgs& a, int b) {
@@ -46,6 +58,7 @@ __device__ __forceinline__ int64_t valid_chunks(const DecArgs& a, int b) {
   return nb < 0 ? 0 : (nb > a.max_chunks ? a.max_chunks : nb);
 }
 
+template <bool kRms>
 __global__ __launch_bounds__(kThreads) void sma_decode_partial_kernel(DecArgs a) {
   __shared__ float s_m[4], s_d[4];
   __shared__ float s_o[4][kP];
@@ -61,23 +74,65 @@ __global__ __launch_bounds__(kThreads) void sma_decode_partial_kernel(DecArgs a)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = lane & 15, kg = lane >> 4;
 
-  // A operand rows: 0 = q, 1 = c, others zero; lane holds n = 32 kb + 8 kg + 0..7
+  // A operand rows: 0 = q, 1 = c, others zero (normalised branch: rows 0 and
+  // 2 carry the two parts of the scaled query, set per chunk); lane holds
+  // n = 32 kb + 8 kg + 0..7
+  const bool qrow = row == 0 || (kRms && row == 2);
   bf16x8_t af[4];
+  float qn[4][8];  // normalised branch: RMSNorm(q) w_q in float32
   {
-    const bf16_t* src = row == 0 ? a.q : a.c;
+    const bf16_t* src = qrow ? a.q : a.c;
     const int64_t base = ((int64_t)b * a.G + g) * kN + 8 * kg;
+    float ss = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < 2) v = *(const uint4*)(src + base + 32 * kb);
+      if (qrow || row == 1) v = *(const uint4*)(src + base + 32 * kb);
       af[kb] = __builtin_bit_cast(bf16x8_t, v);
+      if (kRms) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          qn[kb][2 * k] = bf16lo(w4[k]);
+          qn[kb][2 * k + 1] = bf16hi(w4[k]);
+          ss = fmaf(qn[kb][2 * k], qn[kb][2 * k], fmaf(qn[kb][2 * k + 1], qn[kb][2 * k + 1], ss));
+        }
+      }
+    }
+    if (kRms) {
+      // the four lanes of a row (kg = 0..3) hold the whole query [Eq. 25]
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float inv_q = 1.f / sqrtf(ss * (1.f / kN) + a.eps);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qn[kb][i] *= inv_q * (a.wq ? a.wq[32 * kb + 8 * kg + i] : 1.f);
     }
   }
   float ev[4];
+  {
+    float ss = 0.f;
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb)
-    ev[pb] = lane < 16 ? bf16_to_f32(a.e[((int64_t)b * a.G + g) * kP + 16 * pb + lane]) * a.e_scale
-                       : 0.f;
+    for (int pb = 0; pb < 4; ++pb) {
+      ev[pb] = lane < 16 ? bf16_to_f32(a.e[((int64_t)b * a.G + g) * kP + 16 * pb + lane]) : 0.f;
+      ss = fmaf(ev[pb], ev[pb], ss);
+    }
+    float es = a.e_scale;
+    if (kRms) {
+      ss += __shfl_xor(ss, 8);
+      ss += __shfl_xor(ss, 4);
+      ss += __shfl_xor(ss, 2);
+      ss += __shfl_xor(ss, 1);
+      es *= 1.f / sqrtf(ss * (1.f / kP) + a.eps);
+    }
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      ev[pb] *= es;
+      if (kRms && a.we && lane < 16) ev[pb] *= a.we[16 * pb + lane];
+    }
+  }
+  const float* rhead = kRms ? a.r_cache + (int64_t)bh * a.max_chunks * kN + 8 * kg : nullptr;
 
   float m = -INFINITY, d = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
   const uint8_t* head = (const uint8_t*)(a.cache + (int64_t)bh * a.max_chunks * (kP * kN));
@@ -91,6 +146,25 @@ __global__ __launch_bounds__(kThreads) void sma_decode_partial_kernel(DecArgs a)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         bf[pb][kb] = *(const bf16x8_t*)(cj + pb * 16 * (kN * 2) + kb * 64);
+    if (kRms && qrow) {
+      // query row of chunk j: RMSNorm(q) w_q r_j, high part on row 0, the
+      // rounding of the remainder on row 2
+      const float* rj = rhead + j * kN;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 r0 = *(const float4*)(rj + 32 * kb);
+        const float4 r1 = *(const float4*)(rj + 32 * kb + 4);
+        const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        uint32_t pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = qn[kb][2 * k] * rv[2 * k], x1 = qn[kb][2 * k + 1] * rv[2 * k + 1];
+          const uint32_t hi = pack_bf16x2(x0, x1);
+          pk[k] = row == 0 ? hi : pack_bf16x2(x0 - bf16lo(hi), x1 - bf16hi(hi));
+        }
+        af[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      }
+    }
     float part = 0.f;
     f32x4_t acc[4];
 #pragma unroll
@@ -99,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void sma_decode_partial_kernel(DecArgs a)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kb], bf[pb][kb], acc[pb], 0, 0, 0);
-      part = fmaf(acc[pb][0], ev[pb], part);  // lanes 0..15: W[16 pb + lane] * e'
+      // lanes 0..15: W[16 pb + lane] * e' (normalised branch: rows 0 + 2)
+      part = fmaf(kRms ? acc[pb][0] + acc[pb][2] : acc[pb][0], ev[pb], part);
     }
     // row-dot over the 16 lanes of each lane group (only lanes 0..15 matter)
     part += __shfl_xor(part, 8);
@@ -205,8 +280,13 @@ hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const Deco
                                   const void* q, const void* c, const void* e, const void* cache,
                                   const int32_t* n_chunks, const void* y, const void* gate,
                                   int gate_pc, void* out, float* R, float* lse, float* ws,
+                                  const float* r_cache, const float* wq, const float* we, float eps,
                                   hipStream_t st) {
   DecArgs a;
+  a.r_cache = r_cache;
+  a.wq = wq;
+  a.we = we;
+  a.eps = eps;
   a.q = (const bf16_t*)q;
   a.c = (const bf16_t*)c;
   a.e = (const bf16_t*)e;
@@ -223,7 +303,10 @@ hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const Deco
   const int64_t bh = s.b * s.H;
   if (bh == 0) return hipSuccess;
   if (max_chunks > 0) {
-    sma_decode_partial_kernel<<<dim3((unsigned)(bh * plan.splits)), dim3(kThreads), 0, st>>>(a);
+    if (r_cache)
+      sma_decode_partial_kernel<true><<<dim3((unsigned)(bh * plan.splits)), dim3(kThreads), 0, st>>>(a);
+    else
+      sma_decode_partial_kernel<false><<<dim3((unsigned)(bh * plan.splits)), dim3(kThreads), 0, st>>>(a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

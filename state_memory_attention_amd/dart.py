@@ -31,6 +31,8 @@ ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
                 "dart_sma_decode_workspace_bytes", "dart_sma_bwd", "dart_sma_bwd_workspace_bytes",
                 "dart_chunk_states_bwd", "dart_chunk_states_bwd_workspace_bytes",
                 "dart_decode_state_update",
+                "dart_chunk_states_rms", "dart_chunk_rms", "dart_sma_fwd_rms", "dart_sma_decode_rms",
+                "dart_decode_state_update_rms",
                 "dart_status_string", "dart_last_error", "dart_abi_version", "dart_set_path")
 
 
@@ -80,6 +82,18 @@ def lib() -> ctypes.CDLL:
     L.dart_chunk_states_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.dart_decode_state_update.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.dart_decode_state_update.restype = i32
+    f32 = ctypes.c_float
+    L.dart_chunk_states_rms.argtypes = [dp, i32, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp]
+    L.dart_chunk_states_rms.restype = i32
+    L.dart_chunk_rms.argtypes = [dp, i32, vp, f32, vp, vp, vp, vp, vp]
+    L.dart_chunk_rms.restype = i32
+    L.dart_sma_fwd_rms.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
+    L.dart_sma_fwd_rms.restype = i32
+    L.dart_sma_decode_rms.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp,
+                                      vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dart_sma_decode_rms.restype = i32
+    L.dart_decode_state_update_rms.argtypes = [dp, i32, i64, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dart_decode_state_update_rms.restype = i32
     L.dart_status_string.argtypes = [i32]
     L.dart_status_string.restype = ctypes.c_char_p
     L.dart_last_error.argtypes = []
@@ -328,3 +342,181 @@ def dart_decode_state_update(x: torch.Tensor, B: torch.Tensor, a: torch.Tensor,
     _check(lib().dart_decode_state_update(ctypes.byref(dims), _code(dt), Mx, _ptr(x), _ptr(B),
                                           _ptr(a), _ptr(state), _ptr(pos), _ptr(cache),
                                           _ptr(n_chunks), _stream(x)))
+
+
+# ---------------------------------------------------------------------------
+# RMS-normalised score branch
+# ---------------------------------------------------------------------------
+
+def score_dtype(dtype: torch.dtype) -> torch.dtype:
+    """Storage type of the score memory: float16 for bfloat16 inputs, else float32."""
+    return torch.float16 if dtype == torch.bfloat16 else torch.float32
+
+
+def _weight(w, name, n, dev):
+    if w is not None:
+        _need(w, name, (n,), torch.float32, dev)
+    return w
+
+
+def dart_chunk_states_rms(X: torch.Tensor, B: torch.Tensor, A: torch.Tensor, chunk: int, eps: float,
+                          w_q: Optional[torch.Tensor] = None, w_e: Optional[torch.Tensor] = None,
+                          dH: Optional[torch.Tensor] = None, r: Optional[torch.Tensor] = None,
+                          dH_score: Optional[torch.Tensor] = None, want_r: bool = True,
+                          want_score: bool = True):
+    """Chunk memories dH (b, H, M, P, N), their inverse RMS r (b, H, M, N)
+    float32 and the score memory (b, H, M, P, N) with the RMSNorm weights
+    w_q (N,), w_e (P,) folded in.  Returns (dH, r, dH_score)."""
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = X.device, X.dtype
+    _need(X, "X", (b, L, H, P), dt, dev)
+    _need(B, "B", (b, L, G, N), dt, dev)
+    _need(A, "A", (b, L, H), torch.float32, dev)
+    _weight(w_q, "w_q", N, dev)
+    _weight(w_e, "w_e", P, dev)
+    if dH is None:
+        dH = torch.empty((b, H, M, P, N), dtype=dt, device=dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    if r is None and want_r:
+        r = torch.empty((b, H, M, N), dtype=torch.float32, device=dev)
+    if r is not None:
+        _need(r, "r", (b, H, M, N), torch.float32, dev)
+    if dH_score is None and want_score:
+        dH_score = torch.empty((b, H, M, P, N), dtype=score_dtype(dt), device=dev)
+    if dH_score is not None:
+        _need(dH_score, "dH_score", (b, H, M, P, N), score_dtype(dt), dev)
+    dims = Dims(b, L, H, G, N, P, chunk)
+    _check(lib().dart_chunk_states_rms(ctypes.byref(dims), _code(dt), _ptr(X), _ptr(B), _ptr(A),
+                                       float(eps), _ptr(w_q), _ptr(w_e), _ptr(dH), _ptr(r),
+                                       _ptr(dH_score), _stream(X)))
+    return dH, r, dH_score
+
+
+def dart_chunk_rms(dH: torch.Tensor, chunk_count_L: int, chunk: int, eps: float,
+                   w_q: Optional[torch.Tensor] = None, w_e: Optional[torch.Tensor] = None,
+                   r: Optional[torch.Tensor] = None, dH_score: Optional[torch.Tensor] = None,
+                   want_r: bool = True, want_score: bool = True):
+    """r (b, H, M, N) and the score memory of given chunk memories
+    dH (b, H, M, P, N), M = ceil(chunk_count_L / chunk).  Returns (r, dH_score)."""
+    b, H, M, P, N = dH.shape
+    dev, dt = dH.device, dH.dtype
+    if num_chunks(chunk_count_L, chunk) != M:
+        raise DartError(-2, f"dH holds {M} chunks, L={chunk_count_L}, S={chunk} give "
+                            f"{num_chunks(chunk_count_L, chunk)}")
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    _weight(w_q, "w_q", N, dev)
+    _weight(w_e, "w_e", P, dev)
+    if r is None and want_r:
+        r = torch.empty((b, H, M, N), dtype=torch.float32, device=dev)
+    if dH_score is None and want_score:
+        dH_score = torch.empty((b, H, M, P, N), dtype=score_dtype(dt), device=dev)
+    if r is not None:
+        _need(r, "r", (b, H, M, N), torch.float32, dev)
+    if dH_score is not None:
+        _need(dH_score, "dH_score", (b, H, M, P, N), score_dtype(dt), dev)
+    dims = Dims(b, chunk_count_L, H, 1, N, P, chunk)
+    _check(lib().dart_chunk_rms(ctypes.byref(dims), _code(dt), _ptr(dH), float(eps), _ptr(w_q), _ptr(w_e),
+                                _ptr(r), _ptr(dH_score), _stream(dH)))
+    return r, dH_score
+
+
+def dart_sma_fwd_rms(Q: torch.Tensor, C: torch.Tensor, E: torch.Tensor, dH: torch.Tensor,
+                     dH_score: torch.Tensor, Y: torch.Tensor, gate: torch.Tensor, chunk: int,
+                     eps: float, out: Optional[torch.Tensor] = None, R: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_R: bool = False, want_lse: bool = False):
+    """SMA with the normalised score branch and the gated residual.
+    Returns (out, R, lse)."""
+    b, L, G, N = Q.shape
+    H, P = Y.shape[2], Y.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = Q.device, Q.dtype
+    _need(C, "C", (b, L, G, N), dt, dev)
+    _need(E, "E", (b, L, G, P), dt, dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    _need(dH_score, "dH_score", (b, H, M, P, N), score_dtype(dt), dev)
+    _need(Y, "Y", (b, L, H, P), dt, dev)
+    gpc = gate.dim() == 4
+    _need(gate, "gate", (b, L, H, P) if gpc else (b, L, H), dt, dev)
+    if out is None:
+        out = torch.empty((b, L, H, P), dtype=dt, device=dev)
+    _need(out, "out", (b, L, H, P), dt, dev)
+    if R is None and want_R:
+        R = torch.empty((b, L, H, P), dtype=torch.float32, device=dev)
+    if R is not None:
+        _need(R, "R", (b, L, H, P), torch.float32, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((b, H, L), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (b, H, L), torch.float32, dev)
+    dims = Dims(b, L, H, G, N, P, chunk)
+    _check(lib().dart_sma_fwd_rms(ctypes.byref(dims), _code(dt), _ptr(Q), _ptr(C), _ptr(E), _ptr(dH),
+                                  _ptr(dH_score), _ptr(Y), _ptr(gate), int(gpc), float(eps), _ptr(out),
+                                  _ptr(R), _ptr(lse), _stream(Q)))
+    return out, R, lse
+
+
+def dart_sma_decode_rms(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: torch.Tensor,
+                        r_cache: torch.Tensor, y: torch.Tensor, gate: torch.Tensor, eps: float,
+                        w_q: Optional[torch.Tensor] = None, w_e: Optional[torch.Tensor] = None,
+                        n_chunks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        R: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, want_R: bool = False,
+                        want_lse: bool = False):
+    """Decode with the normalised score branch: cache (b, H, Mmax, P, N) and
+    r_cache (b, H, Mmax, N) float32.  Returns (out, R, lse)."""
+    b, G, N = q.shape
+    H, Mx, P = cache.shape[1], cache.shape[2], cache.shape[3]
+    dev, dt = q.device, q.dtype
+    _need(c, "c", (b, G, N), dt, dev)
+    _need(e, "e", (b, G, P), dt, dev)
+    _need(cache, "cache", (b, H, Mx, P, N), dt, dev)
+    _need(r_cache, "r_cache", (b, H, Mx, N), torch.float32, dev)
+    _need(y, "y", (b, H, P), dt, dev)
+    _weight(w_q, "w_q", N, dev)
+    _weight(w_e, "w_e", P, dev)
+    gpc = gate.dim() == 3
+    _need(gate, "gate", (b, H, P) if gpc else (b, H), dt, dev)
+    if n_chunks is not None:
+        _need(n_chunks, "n_chunks", (b,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((b, H, P), dtype=dt, device=dev)
+    _need(out, "out", (b, H, P), dt, dev)
+    if R is None and want_R:
+        R = torch.empty((b, H, P), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((b, H), dtype=torch.float32, device=dev)
+    dims = Dims(b, 1, H, G, N, P, 1)
+    need = int(lib().dart_sma_decode_workspace_bytes(ctypes.byref(dims), Mx))
+    workspace = _workspace(need, dev, workspace)
+    _check(lib().dart_sma_decode_rms(ctypes.byref(dims), _code(dt), Mx, _ptr(q), _ptr(c), _ptr(e),
+                                     _ptr(cache), _ptr(r_cache), _ptr(n_chunks), _ptr(y), _ptr(gate),
+                                     int(gpc), float(eps), _ptr(w_q), _ptr(w_e), _ptr(out), _ptr(R),
+                                     _ptr(lse), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, R, lse
+
+
+def dart_decode_state_update_rms(x: torch.Tensor, B: torch.Tensor, a: torch.Tensor,
+                                 state: torch.Tensor, pos: torch.Tensor, cache: torch.Tensor,
+                                 r_cache: torch.Tensor, chunk: int, eps: float,
+                                 n_chunks: Optional[torch.Tensor] = None) -> None:
+    """dart_decode_state_update, also writing r_cache (b, H, Mmax, N) float32
+    for every chunk the token closes."""
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    Mx = cache.shape[2]
+    dev, dt = x.device, x.dtype
+    _need(B, "B", (b, G, N), dt, dev)
+    _need(a, "a", (b, H), torch.float32, dev)
+    _need(state, "state", (b, H, P, N), torch.float32, dev)
+    _need(pos, "pos", (b,), torch.int32, dev)
+    _need(cache, "cache", (b, H, Mx, P, N), dt, dev)
+    _need(r_cache, "r_cache", (b, H, Mx, N), torch.float32, dev)
+    if n_chunks is not None:
+        _need(n_chunks, "n_chunks", (b,), torch.int32, dev)
+    dims = Dims(b, 1, H, G, N, P, chunk)
+    _check(lib().dart_decode_state_update_rms(ctypes.byref(dims), _code(dt), Mx, float(eps), _ptr(x),
+                                              _ptr(B), _ptr(a), _ptr(state), _ptr(pos), _ptr(cache),
+                                              _ptr(r_cache), _ptr(n_chunks), _stream(x)))

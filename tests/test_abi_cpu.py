@@ -231,3 +231,63 @@ def test_decode_update_validation():
     bad = dims(S=0)
     assert upd(bad) == -2
     assert upd(dims(b=0)) == 0
+
+
+def cs_rms(d, dtype=1, eps=1e-6, over=None):
+    p = [ADDR[0], ADDR[1], ADDR[2], None, None, ADDR[3], ADDR[4], ADDR[5]]  # X B A wq we dH r dHs
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_chunk_states_rms(ctypes.byref(d), dtype, p[0], p[1], p[2], eps, p[3], p[4],
+                                         p[5], p[6], p[7], None)
+
+
+def fwd_rms(d, dtype=1, eps=1e-6, over=None):
+    p = list(ADDR[:8])  # Q C E dH dHs Y gate out
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_sma_fwd_rms(ctypes.byref(d), dtype, p[0], p[1], p[2], p[3], p[4], p[5], p[6], 1,
+                                    eps, p[7], None, None, None)
+
+
+def dec_rms(d, max_chunks=8, eps=1e-6, over=None, ws_bytes=1 << 40):
+    p = list(ADDR[:10])  # q c e cache r_cache y gate out ws wq
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_sma_decode_rms(ctypes.byref(d), 1, max_chunks, p[0], p[1], p[2], p[3], p[4], None,
+                                       p[5], p[6], 1, eps, p[9], None, p[7], None, None, p[8], ws_bytes,
+                                       None)
+
+
+def upd_rms(d, max_chunks=4, eps=1e-6, over=None):
+    p = [ADDR[0], ADDR[1], ADDR[2], ADDR[3], ADDR[4], ADDR[5], ADDR[6], None]  # x B a state pos cache r n
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_decode_state_update_rms(ctypes.byref(d), 1, max_chunks, eps, *p, None)
+
+
+def test_rms_validation():
+    d = dims()
+    # chunk states with r and the score memory
+    assert cs_rms(d, over={5: None}) == -1 and "dH" in last()
+    assert cs_rms(d, eps=-1.0) == -2 and "eps" in last()
+    assert cs_rms(d, eps=float("nan")) == -2
+    assert cs_rms(d, over={3: ctypes.c_void_p(ADDR[9].value + 2)}) == -6 and "w_q" in last()
+    assert cs_rms(d, over={6: ctypes.c_void_p(ADDR[4].value + 4)}) == -6 and "r" in last()
+    assert cs_rms(d, over={7: ctypes.c_void_p(ADDR[0].value)}) == -2 and "overlaps" in last()
+    assert cs_rms(dims(b=0)) == 0
+    # forward: the score memory is required
+    assert fwd_rms(d, over={4: None}) == -1 and "dH_score" in last()
+    assert fwd_rms(d, over={4: ctypes.c_void_p(ADDR[4].value + 8)}) == -6
+    assert fwd_rms(d, over={7: ctypes.c_void_p(ADDR[4].value)}) == -2 and "overlaps" in last()
+    assert fwd_rms(d, eps=float("inf")) == -2
+    assert fwd_rms(dims(L=0)) == 0
+    # decode: r_cache required when chunks are cached
+    assert dec_rms(d, over={4: None}) == -1 and "r_cache" in last()
+    assert dec_rms(d, over={9: ctypes.c_void_p(ADDR[9].value + 1)}) == -6 and "w_q" in last()
+    assert dec_rms(d, ws_bytes=0) == -4
+    assert dec_rms(d, over={7: ctypes.c_void_p(ADDR[4].value)}) == -2 and "overlaps" in last()
+    # update: r_cache required, 16-byte aligned
+    assert upd_rms(d, over={6: None}) == -1 and "r_cache" in last()
+    assert upd_rms(d, over={6: ctypes.c_void_p(ADDR[6].value + 4)}) == -6
+    assert upd_rms(d, eps=-0.5) == -2
+    assert upd_rms(dims(b=0)) == 0
