@@ -103,14 +103,14 @@ constexpr unsigned kWaitVm8Lgkm0 = 0x0078;
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sma_fwd_mfma_kernel(FwdArgs a) {
-  // 64 KB ring of chunk memories (first used to stage the Q and C tiles) and
-  // 16 KB for the E tile: 80 KB, two blocks per CU.  One LDS object on
-  // purpose: the loop's waits for the in-flight chunk loads are explicit
-  // (below), and with a single object the compiler adds no wait of its own
-  // for them before each read of the ring.
+  // 64 KB ring of chunk memories and a 16 KB area for the Y tile (later the
+  // out tile): 80 KB, two blocks per CU.  One LDS object on purpose: the
+  // loop's waits for the in-flight chunk loads are explicit (below), and with
+  // a single object the compiler adds no wait of its own for them before
+  // each read of the ring.
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kRing * kMemBytes + kTile * kP * 2];
   uint8_t* const s_mem = s_lds;
-  uint8_t* const s_e = s_lds + kRing * kMemBytes;
+  uint8_t* const s_y = s_lds + kRing * kMemBytes;
 
   const int blk = blockIdx.x;
   const int bh = blk % a.BHp;
@@ -127,25 +127,22 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   const int my_hist = (t0 + wave * 32 + col < a.L) ? (int)((t0 + wave * 32 + col) / a.S) : 0;
 
   // ---- streamed inputs.  Slots in order: chunk memories 0..n_hist-1, then
-  // the Y tile, then the per-channel gate tile.  Slot 0 lands in the 16 KB
-  // E/out area while the Q and C tiles are staged in the ring; slot s >= 1
-  // goes to ring buffer (s-1) % kRing.  Every slot costs every wave exactly 4
-  // direct-to-LDS loads, so the waits below only count slots; Y and gate
-  // arrive during the last chunk iterations in buffers the chunks no longer
-  // need.  A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4 loads
-  // of 4 rows); a token-tile load of wave w writes the wave's own token rows
-  // 32w .. 32w+31 (4 loads of 8 rows of 128 B).  One such load writes 1 KB
-  // contiguously, so the XOR swizzle is applied on the global side: the lane
-  // that fills physical piece f of row r fetches logical piece f ^ (r & 15)
-  // (256-byte rows) or f ^ (r & 7) (128-byte rows).
+  // the per-channel gate tile; slot s goes to ring buffer s % kRing.  Every
+  // slot costs every wave exactly 4 direct-to-LDS loads, so the waits below
+  // only count slots; the first three slots are always issued (zero-length
+  // loads stand in for missing ones), the Y tile goes to its own area with
+  // them.  A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4
+  // loads of 4 rows); a token-tile load of wave w writes the wave's own token
+  // rows 32w .. 32w+31 (4 loads of 8 rows of 128 B).  One such load writes
+  // 1 KB contiguously, so the XOR swizzle is applied on the global side: the
+  // lane that fills physical piece f of row r fetches logical piece
+  // f ^ (r & 15) (256-byte rows) or f ^ (r & 7) (128-byte rows).
   const int64_t row0 = (int64_t)b * a.L;  // token index of this batch row
   const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
   // lane part of a chunk load: row 16 wave + 4 i + lane/16 (+ 4 rows per i)
   const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
-  const int n_slots = n_hist + 1 + (a.gate_pc ? 1 : 0);
-  auto slot_buf = [&](int s) -> uint8_t* {
-    return s == 0 ? s_e : s_mem + ((s - 1) % kRing) * kMemBytes;
-  };
+  const int n_slots = n_hist + (a.gate_pc ? 1 : 0);
+  auto slot_buf = [&](int s) -> uint8_t* { return s_mem + (s % kRing) * kMemBytes; };
   auto issue_mem = [&](int s) {
     const auto rs = buf_rsrc(mem_head + (int64_t)s * kMemBytes, kMemBytes);
     uint8_t* dst = slot_buf(s) + wave * 16 * 256;
@@ -158,9 +155,9 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   // token rows of this tile past the sequence end re-read the last token
   const int last_r = (int)(a.L - 1 - t0 < kTile - 1 ? a.L - 1 - t0 : kTile - 1);
   const uint32_t tok_bytes = (uint32_t)(last_r * a.H * kP + kP) * 2;
-  auto issue_tok = [&](int s) {
-    const auto rs = buf_rsrc((s == n_hist ? a.Y : a.gate) + ((row0 + t0) * a.H + h) * kP, tok_bytes);
-    uint8_t* dst = slot_buf(s) + wave * 16 * 256;
+  auto issue_tok = [&](const bf16_t* base, uint8_t* area) {
+    const auto rs = buf_rsrc(base + ((row0 + t0) * a.H + h) * kP, tok_bytes);
+    uint8_t* dst = area + wave * 16 * 256;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 32 * wave + 8 * k + (lane >> 3);
@@ -168,45 +165,65 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
       buf_dma16(rs, (uint32_t)(rr * a.H * kP + (((lane & 7) ^ (r & 7)) << 3)) * 2, dst + k * 8 * 128);
     }
   };
+  // Slot s (a chunk, the gate tile or, past the last slot, a zero-length
+  // stand-in) without branches: the compiler places its waits for the token
+  // operands below from the loads issued on every path, and with a branch
+  // here it would count the fewest and drain the slots as well.
+  const uint8_t* tok_gate = (const uint8_t*)(a.gate + ((row0 + t0) * a.H + h) * kP);
   auto issue = [&](int s) {
-    if (s < n_hist) issue_mem(s);
-    else issue_tok(s);
+    const bool is_mem = s < n_hist, is_tok = !is_mem && s < n_slots;
+    const uint8_t* base = is_mem ? mem_head + (int64_t)s * kMemBytes : (is_tok ? tok_gate : mem_head);
+    const auto rs = buf_rsrc(base, is_mem ? kMemBytes : (is_tok ? tok_bytes : 0u));
+    uint8_t* dst = slot_buf(s) + wave * 16 * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      const uint32_t vm = mem_dma + i * 1024 + (((lane & 15) ^ (row & 15)) << 4);
+      const int r = 32 * wave + 8 * i + (lane >> 3);
+      const int rr = r < last_r ? r : last_r;
+      const uint32_t vt = (uint32_t)(rr * a.H * kP + (((lane & 7) ^ (r & 7)) << 3)) * 2;
+      buf_dma16(rs, is_tok ? vt : vm, dst + i * 1024);
+    }
   };
 
-  // ---- token operands.  Consecutive tokens are G*N*2 bytes apart, so the Q
-  // and C tiles are fetched as whole rows (one direct-to-LDS load = 4 rows, all
-  // bytes used) and then read from LDS in the MFMA layout, with the 256-byte
-  // row swizzle so the reads are conflict free.  Each wave stages and reads
-  // only its own 32 token rows.  E goes straight to registers, which leaves
-  // the E/out area free for slot 0: the first chunk memory then arrives in the
-  // same memory round trip as the token tiles.
+  // ---- the first three slots and the Y tile, then the token operands
+  // straight to registers: Q and C as MFMA B operands (lane holds token
+  // `col`, n = 16 ks + 8 half + 0..7), E in the accumulator layout (register
+  // r of row-block rb holds p = 32 rb + 8 (r / 4) + 4 half + r % 4).  All of
+  // it is one round trip: the loop starts once everything has landed.
+  issue(0);
+  issue_tok(a.Y, s_y);
+  issue(1);
+  issue(2);
   bf16x8_t qf[8], cf[8];
   float ef[2][16];
   {
+    const int64_t tl = t0 + wave * 32 + col;
+    const int64_t tok = row0 + (tl < a.L ? tl : a.L - 1);
+    const int64_t qrow = (tok * a.G + g) * kN + 8 * half;
+    uint4 qv[8], cv[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 32 * wave + 4 * k + (lane >> 4);
-      const int64_t tok = (t0 + r < a.L) ? t0 + r : a.L - 1;
-      const int64_t off = ((row0 + tok) * a.G + g) * kN + (((lane & 15) ^ (r & 15)) << 3);
-      dma16(a.Q + off, s_mem + (32 * wave + 4 * k) * 256);
-      dma16(a.C + off, s_mem + 32768 + (32 * wave + 4 * k) * 256);
+    for (int ks = 0; ks < 8; ++ks) {
+      qv[ks] = *(const uint4*)(a.Q + qrow + 16 * ks);
+      cv[ks] = *(const uint4*)(a.C + qrow + 16 * ks);
     }
-    issue(0);
-    // E in the accumulator layout: register r of row-block rb holds
-    // p = 32 rb + 8 (r / 4) + 4 half + r % 4.
     uint2 ev[2][4];
-    {
-      const int64_t tl = t0 + wave * 32 + col;
-      const bf16_t* ep = a.E + ((row0 + (tl < a.L ? tl : a.L - 1)) * a.G + g) * kP + 4 * half;
+    const bf16_t* ep = a.E + (tok * a.G + g) * kP + 4 * half;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) ev[rb][gq] = *(const uint2*)(ep + 32 * rb + 8 * gq);
+      for (int gq = 0; gq < 4; ++gq) ev[rb][gq] = *(const uint2*)(ep + 32 * rb + 8 * gq);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 q = qv[ks], c = cv[ks];
+      // pinned here, where they have landed: left alone the compiler may
+      // convert them later, behind a wait that also covers the slots
+      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+      asm volatile("" : "+v"(c.x), "+v"(c.y), "+v"(c.z), "+v"(c.w));
+      qf[ks] = __builtin_bit_cast(bf16x8_t, q);
+      cf[ks] = __builtin_bit_cast(bf16x8_t, c);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    // Pin the E values here, where every load is drained: left to itself the
-    // compiler converts them in the first loop iteration, behind a wait that
-    // also covers the chunk prefetches issued by then.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -218,14 +235,6 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
         ef[rb][4 * gq + 2] = bf16lo(v.y) * a.e_scale;
         ef[rb][4 * gq + 3] = bf16hi(v.y) * a.e_scale;
       }
-    // Q, C as MFMA B operands: lane holds token `col`, n = 16 ks + 8 half + 0..7
-    const int r = 32 * wave + col;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
-      qf[ks] = *(const bf16x8_t*)(s_mem + o);
-      cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
-    }
   }
 
   float o[2][16];
@@ -233,11 +242,8 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
   float m = -INFINITY, d = 0.f;
 
-  // Every wave is done reading its token rows before the ring is refilled,
-  // and slot 0 has landed in every wave's part.
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  // slots 0..2 have landed in every wave's part
   __builtin_amdgcn_s_barrier();
-  for (int s = 1; s < kRing - 1 && s < n_slots; ++s) issue(s);
 
   for (int j = 0; j < n_hist; ++j) {
     // Chunk j must have landed in every wave's part, and every wave must be
@@ -246,16 +252,22 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     // cost hides behind queued matrix work).  The only vector-memory
     // operations in flight are these slot loads, so wait until at most slots
     // j+1 .. j+kRing-2 remain (__syncthreads() would wait for all of them).
-    // Chunk 0 was drained before the barrier above.
+    // Slots 0..2 landed before the barrier above; later slots are issued
+    // only if they exist.
     if (j > 0) {
-      if (n_slots - 1 - j >= 2)
+      // loads that may stay in flight: those of slots j+1 and j+2 issued in
+      // the loop (slots past 2 that exist)
+      const int after = (j + 1 >= 3 && j + 1 < n_slots) + (j + 2 >= 3 && j + 2 < n_slots);
+      if (after == 2)
         __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
-      else
+      else if (after == 1)
         __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0 & kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
     }
 
-    if (j + kRing - 1 >= n_hist && j + kRing - 1 < n_slots) issue_tok(j + kRing - 1);
+    if (j + kRing - 1 == n_hist && j + kRing - 1 < n_slots) issue_tok(a.gate, slot_buf(j + kRing - 1));
 
     // The MFMA burst runs at raised wave priority, so that a wave entering
     // it is not held back by the other block's softmax work on this SIMD.
@@ -330,19 +342,17 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
 
   // ---- epilogue: R = O / d, lse = m + log d, out = Y + g * R  [§3 Eq. 10-11]
   // Each wave reads only the Y / gate rows it loaded itself, so waiting for
-  // its own loads is enough.  `out` goes through this wave's rows of the
-  // (now free) E area and leaves as whole 128-byte rows.
+  // its own loads is enough.  `out` replaces the wave's Y rows in place
+  // (every lane rewrites exactly the bytes it read) and leaves as whole
+  // 128-byte rows.
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  // with a single chunk no barrier separates its reads of the E/out area from
-  // the out rows written there below
-  if (n_hist == 1) __builtin_amdgcn_s_barrier();
   const int64_t t = t0 + wave * 32 + col;
   const bool tok_ok = t < a.L;
   const int64_t tc = tok_ok ? t : a.L - 1;
   const float inv = d > 0.f ? 1.f / d : 0.f;
   const int tr = 32 * wave + col;  // this lane's token row in the tile
-  const uint8_t* ybuf = slot_buf(n_hist);
-  const uint8_t* gbuf = slot_buf(n_hist + 1);
+  const uint8_t* ybuf = s_y;
+  const uint8_t* gbuf = slot_buf(n_hist);
   const int64_t orow = (row0 + tc) * a.H + h;
   const float gs = a.gate_pc ? 0.f : bf16_to_f32(a.gate[orow]);
   float* rp = (a.R && tok_ok) ? a.R + orow * kP + 4 * half : nullptr;
@@ -362,7 +372,7 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
       uint2 ov;
       ov.x = pack_bf16x2(fmaf(g0, r0, bf16lo(yv.x)), fmaf(g1, r1, bf16hi(yv.x)));
       ov.y = pack_bf16x2(fmaf(g2, r2, bf16lo(yv.y)), fmaf(g3, r3, bf16hi(yv.y)));
-      *(uint2*)(s_e + lo) = ov;
+      *(uint2*)(s_y + lo) = ov;
       if (rp) *(float4*)(rp + 32 * rb + 8 * gq) = make_float4(r0, r1, r2, r3);
     }
   if (a.lse && half == 0 && tok_ok)
@@ -373,7 +383,7 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     const int r = 32 * wave + 8 * k + (lane >> 3);
     const int f = lane & 7;
     if (t0 + r < a.L) {
-      const uint4 v = *(const uint4*)(s_e + r * 128 + ((f ^ (r & 7)) << 4));
+      const uint4 v = *(const uint4*)(s_y + r * 128 + ((f ^ (r & 7)) << 4));
       *(uint4*)(a.out + ((row0 + t0 + r) * a.H + h) * kP + f * 8) = v;
     }
   }
