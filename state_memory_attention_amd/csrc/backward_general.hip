@@ -284,20 +284,59 @@ __global__ __launch_bounds__(kThreads) void chunk_states_bwd_kernel(
   }
 }
 
-// (4) dA_k = w_k u_k, u_{s0} = 0, u_{k+1} = a_k u_k + dw_k; one thread per (b, h, c).
-__global__ __launch_bounds__(kThreads) void decay_grad_kernel(Shape s, const float* __restrict__ A,
-                                                              const float* __restrict__ wsw,
-                                                              const float* __restrict__ wsdw,
-                                                              float* __restrict__ dA) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // (b, h, c)
-  if (i >= s.b * s.H * s.M) return;
+// (4) dA_k = w_k u_k with u_{s0} = 0, u_{k+1} = a_k u_k + dw_k: one wave per
+// (b, h, c).  The recurrence is affine in u, so a chunk is scanned 256 tokens
+// at a time: every lane composes the maps u -> a_k u + dw_k of its 4 tokens,
+// a wave scan (log2 64 steps of lane shuffles) composes the lanes before it,
+// and each lane then replays its own tokens from the u it starts with.  Only
+// products and sums: exact where a_k = 0.
+constexpr int kScanLanes = 64;
+
+__global__ __launch_bounds__(kScanLanes) void decay_grad_kernel(Shape s, const float* __restrict__ A,
+                                                                const float* __restrict__ wsw,
+                                                                const float* __restrict__ wsdw,
+                                                                float* __restrict__ dA) {
+  const int64_t i = blockIdx.x;  // (b, h, c)
   const int64_t c = i % s.M, bh = i / s.M, b = bh / s.H, h = bh % s.H;
   const int64_t s0 = c * s.S, s1 = (s0 + s.S < s.L) ? s0 + s.S : s.L;
-  float u = 0.f;
-  for (int64_t k = s0; k < s1; ++k) {
-    const int64_t ai = (b * s.L + k) * s.H + h;
-    dA[ai] = wsw[bh * s.L + k] * u;
-    u = fmaf(A[ai], u, wsdw[bh * s.L + k]);
+  const int lane = threadIdx.x;
+  float carry = 0.f;  // u at the start of the current 256-token segment
+  for (int64_t seg = s0; seg < s1; seg += 4 * kScanLanes) {
+    float av[4], dw[4], wv[4];
+    float al = 1.f, be = 0.f;  // this lane's map u -> al u + be
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = seg + 4 * lane + k;
+      const bool ok = t < s1;
+      av[k] = ok ? A[(b * s.L + t) * s.H + h] : 1.f;
+      dw[k] = ok ? wsdw[bh * s.L + t] : 0.f;
+      wv[k] = ok ? wsw[bh * s.L + t] : 0.f;
+      be = fmaf(av[k], be, dw[k]);
+      al *= av[k];
+    }
+    // inclusive scan of the maps over lanes: (al, be) <- (al, be) o (al', be')
+#pragma unroll
+    for (int d = 1; d < kScanLanes; d <<= 1) {
+      const float pa = __shfl_up(al, d), pb = __shfl_up(be, d);
+      if (lane >= d) {
+        be = fmaf(al, pb, be);
+        al *= pa;
+      }
+    }
+    // exclusive: the lanes before this one applied to the segment's carry
+    float ea = __shfl_up(al, 1), eb = __shfl_up(be, 1);
+    if (lane == 0) {
+      ea = 1.f;
+      eb = 0.f;
+    }
+    float u = fmaf(ea, carry, eb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = seg + 4 * lane + k;
+      if (t < s1) dA[(b * s.L + t) * s.H + h] = wv[k] * u;
+      u = fmaf(av[k], u, dw[k]);
+    }
+    carry = __shfl(u, kScanLanes - 1);
   }
 }
 
@@ -380,7 +419,7 @@ hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, bool mfma,
   else
     chunk_states_bwd_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(
         s, (const float*)X, (const float*)B, A, ddH, dX, hb, hs, wsw, wsdw);
-  decay_grad_kernel<<<grid1(s.b * s.H * s.M), dim3(kThreads), 0, st>>>(s, A, wsw, wsdw, dA);
+  decay_grad_kernel<<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kScanLanes), 0, st>>>(s, A, wsw, wsdw, dA);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !grouped) return e;
   const int64_t rows = s.b * s.L;

@@ -627,12 +627,15 @@ void sma_bwd_d_kernel(BwdDArgs a) {
   const int nsb = (int)((n_tok + kSB - 1) / kSB);
   const int n_steps = 2 * nsb;                          // term 1 sub-blocks, then term 2
 
-  // Step q: term = q / nsb, sub-block q % nsb.  Wave w loads rows 16w..16w+15
-  // of both tiles (2 + 4 loads) and the weights of chunk c0 + w (1 load).
+  // Step q: term = q / nsb, sub-block nsb - 1 - q % nsb: the tokens are
+  // streamed from the end of the sequence, so the chunk groups of one head
+  // (same XCD) start on the same tiles and share them in L2.  Wave w loads
+  // rows 16w..16w+15 of both tiles (2 + 4 loads) and the weights of chunk
+  // c0 + w (1 load).
   auto issue = [&](int q) {
     const bool live = q < n_steps;
     const int term = live ? q / nsb : 0;
-    const int sbk = live ? q % nsb : 0;
+    const int sbk = live ? nsb - 1 - q % nsb : 0;
     const int64_t sb = ts + (int64_t)sbk * kSB;
     const int cnt = live ? (int)((a.L - sb) < kSB ? (a.L - sb) : kSB) : 1;
     uint8_t* st = s_lds + (q % kStagesD) * kStageD;
@@ -684,7 +687,7 @@ void sma_bwd_d_kernel(BwdDArgs a) {
     if (q >= 1 && q + 2 < n_steps) issue(q + 2);
 
     const int term = q / nsb;
-    const int64_t sb = ts + (int64_t)(q % nsb) * kSB;
+    const int64_t sb = ts + (int64_t)(nsb - 1 - q % nsb) * kSB;
     const uint8_t* st = s_lds + (q % kStagesD) * kStageD;
     const uint32_t sa = lds_addr(st), sbb = sa + kATile;
     const uint32_t swt = sa + kATile + kBTile;  // weights: chunk k at + 256 k
