@@ -39,8 +39,9 @@ design notes):
     [App. C Eq. 33-35]; gradients of projections shared by a group of heads
     are summed over those heads.
 
-Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
-and ``tests/test_oracle_backward_pins.py`` against brute force, closed forms,
+Parity pins: every function here is checked in ``tests/test_oracle_pins.py``,
+``tests/test_oracle_backward_pins.py``, ``tests/test_oracle_rms_pins.py`` and
+``tests/test_oracle_ssd_pins.py`` against brute force, closed forms,
 special cases, central finite differences (the backward) and the paper's
 printed numbers; none is "parity unpinned".
 """
@@ -77,6 +78,9 @@ __all__ = [
     "sma_head_rms",
     "sma_forward_rms",
     "sma_decode_rms",
+    "ssm_output_head",
+    "ssd_chunked_head",
+    "ssm_output",
 ]
 
 
@@ -580,3 +584,76 @@ def sma_decode_rms(q, c, e, cache, n_chunks, eps: float, hpg: int = 1, wq=None, 
             R[bi, h], lse[bi, h] = sma_token_rms(q[bi, g], c[bi, g], e[bi, g], cache[bi, h, :nb], eps,
                                                  wq, we)
     return R, lse
+
+
+# ---------------------------------------------------------------------------
+# SSM branch: the Mamba-2 output Y_t = C_t H_t  [§2 Eq. 2; App. A Eq. 15],
+# and its chunked scan [App. A Eq. 17-24].  The step recurrence is the
+# definition; the chunked form is the algorithm the GPU path follows and is
+# pinned against it.
+# ---------------------------------------------------------------------------
+
+
+def ssm_output_head(X, B, C, a, H0=None):
+    """Y_t = C_t H_t along the step recurrence H_t = a_t H_{t-1} + B_t^T X_t
+    [§2 Eq. 2; App. A Eq. 15], H_{-1} = H0 (zero by default).
+    X (L, P), B, C (L, N), a (L,)  ->  Y (L, P), last state (N, P)."""
+    X, C = _f64(X), _f64(C)
+    L, P = X.shape
+    N = C.shape[1]
+    if L == 0:
+        return np.zeros((0, P)), (np.zeros((N, P)) if H0 is None else _f64(H0).copy())
+    Hs = ssm_recurrence(X, B, a, H0)
+    return np.einsum("tn,tnp->tp", C, Hs), Hs[-1].copy()
+
+
+def ssd_chunked_head(X, B, C, a, S: int, H0=None):
+    """The Mamba-2 chunked scan of one head, in the paper's steps:
+    chunk contributions dH_[c] [App. A Eq. 20], boundary states
+    H_[c] = A_{a_c:b_c} H_[c-1] + dH_[c] with H_[-1] = H0 [Eq. 17-18], and
+    Y_t = Y_t^intra + Y_t^inter [Eq. 19] with
+        Y_t^intra = sum_{s in chunk, s <= t} C_t A_{s+1:t} B_s^T X_s   [Eq. 21]
+        Y_t^inter = C_t A_{a_c:t} H_[c-1]                              [Eq. 22]
+    Returns (Y (L, P), dH (M, N, P), last boundary state (N, P))."""
+    X, B, C, a = _f64(X), _f64(B), _f64(C), _f64(a)
+    L, P = X.shape
+    N = B.shape[1]
+    M = num_chunks(L, S)
+    dH = chunk_states_head(X, B, a, S)
+    Y = np.zeros((L, P))
+    prev = np.zeros((N, P)) if H0 is None else _f64(H0).copy()
+    for c in range(M):
+        s0, s1 = chunk_bounds(c, L, S)
+        for t in range(s0, s1):
+            y = np.zeros(P)
+            for s in range(s0, t + 1):
+                dec = 1.0
+                for k in range(s + 1, t + 1):
+                    dec *= a[k]                      # A_{s+1:t}  [Eq. 16]
+                y += dec * (C[t] @ B[s]) * X[s]
+            dec = 1.0
+            for k in range(s0, t + 1):
+                dec *= a[k]                          # A_{a_c:t}
+            Y[t] = y + dec * (C[t] @ prev)
+        full = 1.0
+        for k in range(s0, s1):
+            full *= a[k]                             # A_{a_c:b_c}
+        prev = full * prev + dH[c]                   # [Eq. 18]
+    return Y, dH, prev
+
+
+def ssm_output(X, B, C, A, H0=None):
+    """Batched ssm_output_head.  X (b, L, H, P), B, C (b, L, G, N), A (b, L, H),
+    H0 (b, H, N, P) or None  ->  Y (b, L, H, P), last states (b, H, N, P)."""
+    X, B, C, A = _f64(X), _f64(B), _f64(C), _f64(A)
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    hpg = H // G
+    Y = np.zeros((b, L, H, P))
+    Hl = np.zeros((b, H, N, P))
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            Y[bi, :, h], Hl[bi, h] = ssm_output_head(X[bi, :, h], B[bi, :, g], C[bi, :, g], A[bi, :, h],
+                                                     None if H0 is None else H0[bi, h])
+    return Y, Hl
