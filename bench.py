@@ -157,6 +157,47 @@ def time_rms(torch, dart, synth, cfg, steps=10, warmup=2, eps=1e-6):
     return res
 
 
+def time_ssd(torch, dart, synth, cfg, steps=10, warmup=2):
+    """The SSM branch by the chunked scan on the same workload: dart_ssd_fwd
+    (chunk states, chunk decays, scan over chunks, outputs).  Bound by HBM:
+    compulsory bytes = X, B, C, A read, Y and the chunk memories written, the
+    state entering every chunk written and read back."""
+    import ctypes
+
+    from state_memory_attention_amd import dart as D
+    b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
+    G, N, P = cfg["ngroups"], cfg["d_state"], cfg["d_head"]
+    M = dart.num_chunks(L, S)
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    Y = torch.empty_like(d["X"])
+    dH = torch.empty((b, H, M, P, N), dtype=torch.bfloat16, device="cuda")
+    dims = D.Dims(b, L, H, G, N, P, S)
+    ws = torch.empty(int(D.lib().dart_ssd_fwd_workspace_bytes(ctypes.byref(dims), 1)), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        dart.dart_ssd_fwd(d["X"], d["B"], d["C"], d["A"], S, Y=Y, dH=dH, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = 2 * (b * L * H * P * 2 + b * L * G * N * 2 + b * H * M * P * N * 3) + b * L * H * 4
+    res = {"workload": cfg["name"], "kernel": "dart_ssd_fwd", "us_per_call": t * 1e6, "bytes_per_call": nbytes,
+           "achieved_GBs": nbytes / t / 1e9, "peak_GBs": PEAK_HBM_GBS, "frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
+           "tokens_per_s": b * L / t}
+    del d, Y, dH, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def traffic_record(kernel, workload, sources=None):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; else None."""
@@ -417,6 +458,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-rms", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run each hot kernel a few times for a hardware-counter pass, then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -496,6 +538,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_rms:
         result["rms"] = time_rms(torch, dart, synth, cfg)
+    if not args.no_ssd:
+        result["ssd"] = time_ssd(torch, dart, synth, cfg)
     if not args.no_backward:
         result["backward"] = time_backward(torch, dart, synth, cfg)
     if not args.no_decode:

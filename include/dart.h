@@ -12,6 +12,9 @@
  *   - decode-side cache maintenance   dart_decode_state_update  [§2 Eq. 2; §4]
  *   - gradients of the SMA branch     dart_sma_bwd        [§4 "Efficient Training";
  *     and of the chunk states         dart_chunk_states_bwd   App. C Eq. 33-35]
+ *   - the SSM branch output by the    dart_ssd_fwd        [§2 Eq. 2; App. A Eq. 15-24]
+ *     Mamba-2 chunked scan, with the
+ *     chunk memories alongside
  *   - the RMS-normalised score        dart_chunk_states_rms, dart_chunk_rms,
  *     branch                          dart_sma_fwd_rms, dart_sma_decode_rms,
  *                                     dart_decode_state_update_rms
@@ -267,6 +270,27 @@ int dart_decode_state_update_rms(const dart_dims_t* dims, int dtype, int64_t max
                                  const void* x, const void* B, const float* a, float* state,
                                  const int32_t* pos, void* cache, float* r_cache, int32_t* n_chunks,
                                  void* stream);
+
+/* The SSM branch of the block by the Mamba-2 chunked scan [§2 Eq. 2; App. A
+ * Eq. 15-24]:  Y_t = C_t H_t,  H_t = a_t H_{t-1} + B_t^T X_t,  H_{-1} = H0,
+ * computed per chunk c as the chunk state memory dH_[c] (Eq. 20, exactly
+ * what dart_chunk_states writes), the boundary states
+ * H_[c] = A_{a_c:b_c} H_[c-1] + dH_[c] (Eq. 17-18) and
+ * Y_t = sum_{s in c, s <= t} C_t A_{s+1:t} B_s^T X_s + C_t A_{a_c:t} H_[c-1]
+ * (Eq. 19-22).  Y is the Y_ssm input of dart_sma_fwd; dH its chunk memories.
+ *   X [b][L][H][P], B, C [b][L][G][N] (dtype), A [b][L][H] float32
+ *   H0 [b][H][P][N] float32 (state before the first token, NULL = 0; the
+ *      same [P][N] orientation as dH)
+ *   Y [b][L][H][P] (dtype), dH [b][H][M][P][N] (dtype)
+ *   H_final [b][H][P][N] float32: the state after the last token (NULL skips it)
+ *   workspace: at least dart_ssd_fwd_workspace_bytes(dims, dtype) bytes
+ *      (chunk decays and the state entering every chunk, stored in dtype).
+ * Arithmetic in float32; the state entering each chunk is rounded to dtype
+ * once before it is read back. */
+int dart_ssd_fwd(const dart_dims_t* dims, int dtype, const void* X, const void* B, const void* C,
+                 const float* A, const float* H0, void* Y, void* dH, float* H_final, void* workspace,
+                 size_t workspace_bytes, void* stream);
+size_t dart_ssd_fwd_workspace_bytes(const dart_dims_t* dims, int dtype);
 
 const char* dart_status_string(int status);
 /* Message for this thread's last failing call ("" if none). */

@@ -9,6 +9,6 @@ from .dart import (  # noqa: F401
     DART_BF16, DART_F32, DART_PATH_AUTO, DART_PATH_GENERAL, DartError, abi_version,
     dart_chunk_states, dart_chunk_states_bwd, dart_decode_state_update, dart_sma_bwd,
     dart_sma_decode, dart_sma_fwd,
-    dart_chunk_rms, dart_chunk_states_rms, dart_decode_state_update_rms, dart_sma_decode_rms, dart_sma_fwd_rms,
+    dart_chunk_rms, dart_chunk_states_rms, dart_decode_state_update_rms, dart_ssd_fwd, dart_sma_decode_rms, dart_sma_fwd_rms,
     decode_workspace_bytes, num_chunks, score_dtype, set_path,
 )

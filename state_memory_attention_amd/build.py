@@ -32,6 +32,7 @@ SOURCES = [
     "sma_bwd_mfma.hip",
     "rms_general.hip",
     "sma_fwd_rms_mfma.hip",
+    "ssd.hip",
 ]
 # A plain 16-byte-vector copy kernel in its own library, used only to
 # calibrate hardware memory-traffic counters (bench.py --profile-kernels).

@@ -502,6 +502,46 @@ int dart_decode_state_update_rms(const dart_dims_t* dims, int dtype, int64_t max
                             n_chunks, stream);
 }
 
+size_t dart_ssd_fwd_workspace_bytes(const dart_dims_t* dims, int dtype) {
+  t_err[0] = '\0';
+  if (dims == nullptr || check_dims(dims, dtype, true) != DART_OK) return 0;
+  const dart::Shape s = make_shape(dims);
+  if (prod({s.b, s.H, s.M, s.P, s.N, 4}) < 0) return 0;
+  return dart::ssd_workspace_bytes(s, dtype == DART_BF16);
+}
+
+int dart_ssd_fwd(const dart_dims_t* dims, int dtype, const void* X, const void* B, const void* C,
+                 const float* A, const float* H0, void* Y, void* dH, float* H_final, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const Buf bx{X, prod({s.b, s.L, s.H, s.P}) * es, "X"};
+  const Buf bb{B, prod({s.b, s.L, s.G, s.N}) * es, "B"};
+  const Buf bc{C, prod({s.b, s.L, s.G, s.N}) * es, "C"};
+  const Buf ba{A, prod({s.b, s.L, s.H}) * 4, "A"};
+  const Buf b0{H0, prod({s.b, s.H, s.P, s.N}) * 4, "H0"};
+  const Buf by{Y, prod({s.b, s.L, s.H, s.P}) * es, "Y"};
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf bf{H_final, prod({s.b, s.H, s.P, s.N}) * 4, "H_final"};
+  const size_t need = dart::ssd_workspace_bytes(s, dtype == DART_BF16);
+  const Buf bw{workspace, (int64_t)need, "workspace"};
+  if ((st = check_ptrs({bx, bb, bc, ba, by, bd}))) return st;
+  if ((st = check_opt_align(H0, "H0")) || (st = check_opt_align(H_final, "H_final"))) return st;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((st = check_opt_align(workspace, "workspace"))) return st;
+  if ((st = check_alias({by, bd, bf, bw}, {bx, bb, bc, ba, b0}, nullptr, nullptr))) return st;
+  if (prod({s.b, s.H, s.M, (s.N * s.P + 255) / 256}) >= kMaxIndex || prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "problem is too large for one launch");
+  return hip_status(dart::launch_ssd_fwd(s, dtype == DART_BF16, use_mfma(dtype, dims), X, B, C, A, H0, Y, dH,
+                                         H_final, workspace, (hipStream_t)stream),
+                    "dart_ssd_fwd");
+}
+
 size_t dart_sma_bwd_workspace_bytes(const dart_dims_t* dims) {
   t_err[0] = '\0';
   if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;

@@ -99,6 +99,13 @@ hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, con
 hipError_t launch_group_sum(const float* in, float* out, int64_t rows, int64_t G, int64_t hpg,
                             int64_t K, hipStream_t st);
 
+// ---- SSM branch by the chunked scan (chunk states, chunk decays, scan over
+// chunks, outputs); mfma: bfloat16, N = 128, P = 64 ------------------------
+size_t ssd_workspace_bytes(const Shape& s, bool bf16);
+hipError_t launch_ssd_fwd(const Shape& s, bool bf16, bool mfma, const void* X, const void* B, const void* C,
+                          const float* A, const float* H0, void* Y, void* dH, float* Hfin, void* ws,
+                          hipStream_t st);
+
 // Split-chunk decode: per (b, h, split) partial softmax states in the
 // workspace, then a fixed-order combine.
 struct DecodePlan {

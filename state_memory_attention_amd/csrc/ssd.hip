@@ -1,0 +1,401 @@
+// The Mamba-2 SSM branch by the chunked scan: Y_t = C_t H_t with
+// H_t = a_t H_{t-1} + B_t^T X_t, computed alongside the chunk state memories.
+//
+// Paper: "DART: Decoded Attention over Recurrent States for Efficient
+// Long-Context Sequence Modeling" (arXiv 2608.02032), §2 Eq. 2 and App. A
+// Eq. 15-24.  Per chunk c with first token a_c and last token b_c:
+//   dH_[c] = sum_{s in c} A_{s+1:b_c} B_s^T X_s                  (Eq. 20)
+//   H_[c]  = A_{a_c:b_c} H_[c-1] + dH_[c],  H_[-1] = H0          (Eq. 17-18)
+//   Y_t    = sum_{s in c, s <= t} C_t A_{s+1:t} B_s^T X_s         (Eq. 21)
+//          + C_t A_{a_c:t} H_[c-1]                               (Eq. 22)
+// Four steps, each a kernel: the chunk states (the SMA's chunk memories,
+// shared with dart_chunk_states), the full decay A_{a_c:b_c} of every chunk,
+// the scan over chunks (writing the state entering each chunk), and the
+// outputs.  Within a chunk the decays enter as
+//   A_{s+1:t} = 2^(l_t - l_s),  l_t = sum_{k = a_c}^{t} log2 a_k,
+// with tokens whose a_k = 0 left out of l and tracked instead as the last
+// zero z_t at or before t: the product is 0 exactly when z_t > s.  Only
+// products, sums and exponentials of sums: no division by a decay.
+#include "dart_internal.h"
+#include "dev_common.h"
+#include "lds_dma.h"
+
+namespace dart {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Full decay of every chunk, A_{a_c:b_c}: one wave per (b, h, c).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void chunk_decay_kernel(Shape s, const float* __restrict__ A,
+                                                         float* __restrict__ alpha) {
+  const int64_t i = blockIdx.x;  // (b, h, c)
+  const int64_t c = i % s.M, bh = i / s.M, b = bh / s.H, h = bh % s.H;
+  const int64_t s0 = c * s.S, s1 = (s0 + s.S < s.L) ? s0 + s.S : s.L;
+  float v = 1.f;
+  for (int64_t t = s0 + threadIdx.x; t < s1; t += 64) v *= A[(b * s.L + t) * s.H + h];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v *= __shfl_xor(v, off);
+  if (threadIdx.x == 0) alpha[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Scan over chunks: Hin_c = H_[c-1] (stored in the input dtype, the operand
+// of the output kernel), H_[c] = alpha_c H_[c-1] + dH_[c] in float32.
+// Every thread owns V consecutive entries of one (b, h) state.
+// ---------------------------------------------------------------------------
+template <typename T, int V>
+__global__ __launch_bounds__(kThreads) void state_pass_kernel(Shape s, int64_t slices,
+                                                              const T* __restrict__ dH,
+                                                              const float* __restrict__ alpha,
+                                                              const float* __restrict__ H0,
+                                                              T* __restrict__ Hin,
+                                                              float* __restrict__ Hfin) {
+  const int64_t bh = blockIdx.x / slices;
+  const int64_t e0 = ((blockIdx.x % slices) * kThreads + threadIdx.x) * V;
+  const int64_t nPN = s.P * s.N;
+  if (e0 >= nPN) return;
+  float st[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) st[k] = (H0 && e0 + k < nPN) ? H0[bh * nPN + e0 + k] : 0.f;
+  const T* src = dH + bh * s.M * nPN + e0;
+  T* dst = Hin + bh * s.M * nPN + e0;
+  const float* al = alpha + bh * s.M;
+#pragma unroll 4
+  for (int64_t c = 0; c < s.M; ++c) {
+    const float a = al[c];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      if (V > 1 || e0 + k < nPN) {
+        Elem<T>::st(dst + c * nPN, k, st[k]);
+        st[k] = fmaf(a, st[k], Elem<T>::ld(src + c * nPN, k));
+      }
+    }
+  }
+  if (Hfin)
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (V > 1 || e0 + k < nPN) Hfin[bh * nPN + e0 + k] = st[k];
+}
+
+// ---------------------------------------------------------------------------
+// Outputs, general kernel: one wave per token (any N, P <= 256).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ssd_out_general_kernel(Shape s, const T* __restrict__ X,
+                                                                   const T* __restrict__ B,
+                                                                   const T* __restrict__ C,
+                                                                   const float* __restrict__ A,
+                                                                   const T* __restrict__ Hin,
+                                                                   T* __restrict__ Y,
+                                                                   int64_t groups_per_head) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t bh = blockIdx.x / groups_per_head;
+  const int64_t t = (blockIdx.x % groups_per_head) * 4 + wave;
+  if (t >= s.L) return;
+  const int64_t b = bh / s.H, h = bh % s.H, g = h / (s.H / s.G);
+  const int N = (int)s.N, P = (int)s.P;
+  const int64_t c = t / s.S, s0 = c * s.S;
+  const T* ct = C + ((b * s.L + t) * s.G + g) * N;
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  float dec = 1.f;  // A_{s+1:t}
+  for (int64_t u = t; u >= s0; --u) {
+    const T* bu = B + ((b * s.L + u) * s.G + g) * N;
+    float part = 0.f;
+    for (int n = lane; n < N; n += 64) part = fmaf(Elem<T>::ld(ct, n), Elem<T>::ld(bu, n), part);
+    const float w = wave_sum(part) * dec;  // C_t A_{s+1:t} B_s^T  [Eq. 21]
+    const T* xu = X + ((b * s.L + u) * s.H + h) * P;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lane + 64 * k < P) y[k] = fmaf(w, Elem<T>::ld(xu, lane + 64 * k), y[k]);
+    dec *= A[(b * s.L + u) * s.H + h];
+  }
+  // dec = A_{a_c:t} now: the inter-chunk readout [Eq. 22]
+  const T* hc = Hin + (bh * s.M + c) * (int64_t)P * N;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int p = lane + 64 * k;
+    if (p < P) {
+      float v = 0.f;
+      for (int n = 0; n < N; ++n) v = fmaf(Elem<T>::ld(ct, n), Elem<T>::ld(hc, (int64_t)p * N + n), v);
+      Elem<T>::st(Y, ((b * s.L + t) * s.H + h) * P + p, fmaf(dec, v, y[k]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Outputs on the matrix core: bfloat16, N = 128, P = 64, S a multiple of 32
+// up to 256.  One block per (b, h, chunk); the chunk's tokens form slices of
+// 32, wave w takes slices w and 7 - w (equal causal work).  Per slice, with
+// one token per lane and P along registers (the transposed output Y^T):
+//   Y^T  = Hin_c^T C^T  scaled per token by A_{a_c:t}         (Eq. 22)
+//   for every 32-token block of earlier or equal tokens s:
+//     G^T = B_s C^T  (32 s x 32 t),  masked and decayed by A_{s+1:t},
+//     Y^T += X_s^T G^T                                          (Eq. 21)
+// G^T leaves the matrix core with s along registers; a swap between the
+// half-waves (v_permlane32_swap) puts 8 consecutive s in each lane, the
+// layout of the next product's B operand, with no trip through LDS.  X^T is
+// read from the chunk's X tile in LDS with the transposing read.
+// ---------------------------------------------------------------------------
+constexpr int kN = 128;
+constexpr int kP = 64;
+constexpr int kMaxS = 256;
+
+struct SsdArgs {
+  const bf16_t* X;
+  const bf16_t* B;
+  const bf16_t* C;
+  const float* A;
+  const bf16_t* Hin;
+  bf16_t* Y;
+  int64_t L;
+  int H, G, hpg, S, M;
+};
+
+__device__ __forceinline__ int swz_x(int row) { return (row & 3) << 1; }
+
+// Four transposing reads that return together (the compiler's own form of
+// the read would drain the global loads in flight before it).
+__device__ __forceinline__ void ld_tr4(uint64_t (&o)[4], const uint32_t (&ad)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+}
+
+__global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[kMaxS * kP * 2];  // X tile, 128-byte rows
+  __shared__ __attribute__((aligned(16))) float s_l[kMaxS];             // l_t (base 2)
+  __shared__ __attribute__((aligned(16))) int s_z[kMaxS];               // last zero decay at or before t
+  __shared__ float s_tl[4];
+  __shared__ int s_tz[4];
+
+  const int blk = blockIdx.x;
+  const int BH = gridDim.x / a.M;
+  const int c = blk / BH, bh = blk % BH;
+  const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5, grp16 = (lane >> 4) & 1, j16 = lane & 15;
+  const int64_t s0 = (int64_t)c * a.S;
+  const int clen = (int)((s0 + a.S < a.L) ? a.S : a.L - s0);
+  const int64_t row0 = (int64_t)b * a.L;
+
+  // ---- X tile of the chunk (rows past its end read as zeros): wave w loads
+  // rows 64w .. 64w+63, 8 rows of 128 B per load, swizzled on the global side
+  {
+    const auto rx = buf_rsrc(a.X + ((row0 + s0) * a.H + h) * kP, (uint32_t)((clen - 1) * a.H * kP + kP) * 2);
+    for (int i = 0; i < a.S / 32; ++i) {
+      const int r = 8 * (wave + 4 * i) + (lane >> 3);  // rows in groups of 8 per load
+      const int piece = (lane & 7) ^ swz_x(r);
+      buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + 8 * (wave + 4 * i) * 128);
+    }
+  }
+  // ---- l and z of the chunk's tokens: block-wide inclusive scans (sum, max)
+  {
+    const float av = tid < clen ? a.A[(row0 + s0 + tid) * a.H + h] : 1.f;
+    float lv = av > 0.f ? fast_log2(av) : 0.f;
+    int zv = (tid < clen && av == 0.f) ? tid : -1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float lu = __shfl_up(lv, off);
+      const int zu = __shfl_up(zv, off);
+      if (lane >= off) {
+        lv += lu;
+        zv = zu > zv ? zu : zv;
+      }
+    }
+    if (lane == 63) {
+      s_tl[wave] = lv;
+      s_tz[wave] = zv;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    for (int w2 = 0; w2 < wave; ++w2) {
+      lv += s_tl[w2];
+      zv = s_tz[w2] > zv ? s_tz[w2] : zv;
+    }
+    if (tid < kMaxS) {
+      s_l[tid] = lv;
+      s_z[tid] = zv;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  const int n_sl = a.S / 32;
+  const uint8_t* hin = (const uint8_t*)(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN));
+  for (int sl2 = 0; sl2 < 2; ++sl2) {
+    const int sl = sl2 == 0 ? wave : 7 - wave;
+    if (sl >= n_sl || 32 * sl >= clen) continue;  // uniform per wave
+    const int tl = 32 * sl + col;                 // this lane's token within the chunk
+    const bool tok_ok = tl < clen;
+    const int64_t tg = row0 + s0 + (tok_ok ? tl : clen - 1);
+    // C^T operand: lane holds token tl, n = 16 kk + 8 half + 0..7
+    bf16x8_t cq[8];
+    const bf16_t* cp = a.C + (tg * a.G + g) * kN + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) cq[kk] = *(const bf16x8_t*)(cp + 16 * kk);
+    const float lt = s_l[tl < a.S ? tl : a.S - 1];
+    const int zt = s_z[tl < a.S ? tl : a.S - 1];
+
+    // inter-chunk readout, then its decay A_{a_c:t}
+    f32x16_t y0 = {}, y1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8_t h0 = *(const bf16x8_t*)(hin + (col * kN + 16 * kk + 8 * half) * 2);
+      const bf16x8_t h1 = *(const bf16x8_t*)(hin + ((32 + col) * kN + 16 * kk + 8 * half) * 2);
+      y0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, cq[kk], y0, 0, 0, 0);
+      y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, cq[kk], y1, 0, 0, 0);
+    }
+    const float din = zt < 0 ? fast_exp2(lt) : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      y0[r] *= din;
+      y1[r] *= din;
+    }
+
+    // intra-chunk terms, one 32-token block of s at a time
+    for (int sb = 0; sb <= sl; ++sb) {
+      const int sa = 32 * sb;
+      const int srow = sa + col < clen ? sa + col : clen - 1;
+      const bf16_t* bp = a.B + ((row0 + s0 + srow) * a.G + g) * kN + 8 * half;
+      f32x16_t gt = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8_t bo = *(const bf16x8_t*)(bp + 16 * kk);
+        gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, cq[kk], gt, 0, 0, 0);
+      }
+      // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = tl.  Keep s <= t with
+      // no zero decay in (s, t], weighted by 2^(l_t - l_s).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sr = sa + 8 * j + 4 * half;
+        const float4 ls = *(const float4*)(s_l + sr);
+        const float lsv[4] = {ls.x, ls.y, ls.z, ls.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sv = sr + i;
+          const bool keep = sv <= tl && zt <= sv;
+          gt[4 * j + i] = keep ? gt[4 * j + i] * fast_exp2(lt - lsv[i]) : 0.f;
+        }
+      }
+      // s to 8 consecutive values per lane: swap registers r and r + 4
+      // between the half-waves, then two k-steps of 16 s each
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float xs[4], ys[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gt[8 * kb + i]),
+                                                           __float_as_uint(gt[8 * kb + 4 + i]), false, false);
+          xs[i] = __uint_as_float(sw[0]);
+          ys[i] = __uint_as_float(sw[1]);
+        }
+        const bf16x8_t mop = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]), pack_bf16x2(ys[0], ys[1]),
+                                 pack_bf16x2(ys[2], ys[3])));
+        // X^T operands (p rows, 8 consecutive s) from the X tile: lane (column
+        // j16 + 16 grp16, k-octet half) receives tokens ... + 4 hh + 0..3 of
+        // read hh, addressing token row ... + 4 hh + j16 / 4
+        uint32_t ad[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r = sa + 16 * kb + 8 * half + 4 * hh + (j16 >> 2);
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const int pb = 32 * f + 16 * grp16 + 4 * (j16 & 3);
+            ad[2 * f + hh] = lds_addr(s_x + r * 128 + (((pb >> 3) ^ swz_x(r)) << 4) + ((pb & 7) >> 2) * 8);
+          }
+        }
+        uint64_t rd[4];
+        ld_tr4(rd, ad);
+        const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[0], (uint32_t)(rd[0] >> 32),
+                                                                    (uint32_t)rd[1], (uint32_t)(rd[1] >> 32)));
+        const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
+                                                                    (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
+        y0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y0, 0, 0, 0);
+        y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y1, 0, 0, 0);
+      }
+    }
+
+    // Y^T[p][t]: register r of y_f holds p = 32 f + 8 (r / 4) + 4 half + r % 4
+    if (tok_ok) {
+      bf16_t* yp = a.Y + ((row0 + s0 + tl) * a.H + h) * kP + 4 * half;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *(uint2*)(yp + 8 * j) = make_uint2(pack_bf16x2(y0[4 * j], y0[4 * j + 1]), pack_bf16x2(y0[4 * j + 2], y0[4 * j + 3]));
+        *(uint2*)(yp + 32 + 8 * j) =
+            make_uint2(pack_bf16x2(y1[4 * j], y1[4 * j + 1]), pack_bf16x2(y1[4 * j + 2], y1[4 * j + 3]));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t ssd_workspace_bytes(const Shape& s, bool bf16) {
+  const size_t alpha = ((size_t)(s.b * s.H * s.M) * 4 + 255) / 256 * 256;
+  return alpha + (size_t)(s.b * s.H * s.M * s.P * s.N) * (bf16 ? 2 : 4);
+}
+
+hipError_t launch_ssd_fwd(const Shape& s, bool bf16, bool mfma, const void* X, const void* B, const void* C,
+                          const float* A, const float* H0, void* Y, void* dH, float* Hfin, void* ws,
+                          hipStream_t st) {
+  if (s.b * s.H * s.M == 0) return hipSuccess;
+  hipError_t e = mfma ? launch_chunk_states_mfma(s, X, B, A, dH, st)
+                      : launch_chunk_states_general(s, bf16, X, B, A, dH, st);
+  if (e != hipSuccess) return e;
+  float* alpha = (float*)ws;
+  void* hin = (uint8_t*)ws + ((size_t)(s.b * s.H * s.M) * 4 + 255) / 256 * 256;
+  chunk_decay_kernel<<<dim3((unsigned)(s.b * s.H * s.M)), dim3(64), 0, st>>>(s, A, alpha);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nPN = s.P * s.N;
+  if (bf16 && nPN % 8 == 0) {
+    const int64_t slices = (nPN / 8 + kThreads - 1) / kThreads;
+    state_pass_kernel<bf16_t, 8><<<dim3((unsigned)(s.b * s.H * slices)), dim3(kThreads), 0, st>>>(
+        s, slices, (const bf16_t*)dH, alpha, H0, (bf16_t*)hin, Hfin);
+  } else if (bf16) {
+    const int64_t slices = (nPN + kThreads - 1) / kThreads;
+    state_pass_kernel<bf16_t, 1><<<dim3((unsigned)(s.b * s.H * slices)), dim3(kThreads), 0, st>>>(
+        s, slices, (const bf16_t*)dH, alpha, H0, (bf16_t*)hin, Hfin);
+  } else {
+    const int64_t slices = (nPN + kThreads - 1) / kThreads;
+    state_pass_kernel<float, 1><<<dim3((unsigned)(s.b * s.H * slices)), dim3(kThreads), 0, st>>>(
+        s, slices, (const float*)dH, alpha, H0, (float*)hin, Hfin);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (mfma && s.S % 32 == 0 && s.S <= kMaxS) {
+    SsdArgs a;
+    a.X = (const bf16_t*)X;
+    a.B = (const bf16_t*)B;
+    a.C = (const bf16_t*)C;
+    a.A = A;
+    a.Hin = (const bf16_t*)hin;
+    a.Y = (bf16_t*)Y;
+    a.L = s.L;
+    a.H = (int)s.H;
+    a.G = (int)s.G;
+    a.hpg = (int)(s.H / s.G);
+    a.S = (int)s.S;
+    a.M = (int)s.M;
+    ssd_out_mfma_kernel<<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kThreads), 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const int64_t gph = (s.L + 3) / 4;
+  if (bf16)
+    ssd_out_general_kernel<bf16_t><<<dim3((unsigned)(s.b * s.H * gph)), dim3(kThreads), 0, st>>>(
+        s, (const bf16_t*)X, (const bf16_t*)B, (const bf16_t*)C, A, (const bf16_t*)hin, (bf16_t*)Y, gph);
+  else
+    ssd_out_general_kernel<float><<<dim3((unsigned)(s.b * s.H * gph)), dim3(kThreads), 0, st>>>(
+        s, (const float*)X, (const float*)B, (const float*)C, A, (const float*)hin, (float*)Y, gph);
+  return hipGetLastError();
+}
+
+}  // namespace dart

@@ -32,7 +32,7 @@ ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
                 "dart_chunk_states_bwd", "dart_chunk_states_bwd_workspace_bytes",
                 "dart_decode_state_update",
                 "dart_chunk_states_rms", "dart_chunk_rms", "dart_sma_fwd_rms", "dart_sma_decode_rms",
-                "dart_decode_state_update_rms",
+                "dart_decode_state_update_rms", "dart_ssd_fwd", "dart_ssd_fwd_workspace_bytes",
                 "dart_status_string", "dart_last_error", "dart_abi_version", "dart_set_path")
 
 
@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
     L.dart_sma_decode_rms.restype = i32
     L.dart_decode_state_update_rms.argtypes = [dp, i32, i64, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.dart_decode_state_update_rms.restype = i32
+    L.dart_ssd_fwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dart_ssd_fwd.restype = i32
+    L.dart_ssd_fwd_workspace_bytes.argtypes = [dp, i32]
+    L.dart_ssd_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.dart_status_string.argtypes = [i32]
     L.dart_status_string.restype = ctypes.c_char_p
     L.dart_last_error.argtypes = []
@@ -520,3 +524,43 @@ def dart_decode_state_update_rms(x: torch.Tensor, B: torch.Tensor, a: torch.Tens
     _check(lib().dart_decode_state_update_rms(ctypes.byref(dims), _code(dt), Mx, float(eps), _ptr(x),
                                               _ptr(B), _ptr(a), _ptr(state), _ptr(pos), _ptr(cache),
                                               _ptr(r_cache), _ptr(n_chunks), _stream(x)))
+
+
+# ---------------------------------------------------------------------------
+# SSM branch by the chunked scan
+# ---------------------------------------------------------------------------
+
+def dart_ssd_fwd(X: torch.Tensor, B: torch.Tensor, C: torch.Tensor, A: torch.Tensor, chunk: int,
+                 H0: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
+                 dH: Optional[torch.Tensor] = None, H_final: Optional[torch.Tensor] = None,
+                 want_final: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Y_t = C_t H_t of the SSM branch, with the chunk memories dH
+    (b, H, M, P, N).  X (b, L, H, P), B, C (b, L, G, N), A (b, L, H) float32,
+    H0 (b, H, P, N) float32 or None.  Returns (Y, dH, H_final)."""
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = X.device, X.dtype
+    _need(X, "X", (b, L, H, P), dt, dev)
+    _need(B, "B", (b, L, G, N), dt, dev)
+    _need(C, "C", (b, L, G, N), dt, dev)
+    _need(A, "A", (b, L, H), torch.float32, dev)
+    if H0 is not None:
+        _need(H0, "H0", (b, H, P, N), torch.float32, dev)
+    if Y is None:
+        Y = torch.empty((b, L, H, P), dtype=dt, device=dev)
+    _need(Y, "Y", (b, L, H, P), dt, dev)
+    if dH is None:
+        dH = torch.empty((b, H, M, P, N), dtype=dt, device=dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    if H_final is None and want_final:
+        H_final = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    if H_final is not None:
+        _need(H_final, "H_final", (b, H, P, N), torch.float32, dev)
+    dims = Dims(b, L, H, G, N, P, chunk)
+    need = int(lib().dart_ssd_fwd_workspace_bytes(ctypes.byref(dims), _code(dt)))
+    workspace = _workspace(need, dev, workspace)
+    _check(lib().dart_ssd_fwd(ctypes.byref(dims), _code(dt), _ptr(X), _ptr(B), _ptr(C), _ptr(A), _ptr(H0),
+                              _ptr(Y), _ptr(dH), _ptr(H_final), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(X)))
+    return Y, dH, H_final

@@ -291,3 +291,28 @@ def test_rms_validation():
     assert upd_rms(d, over={6: ctypes.c_void_p(ADDR[6].value + 4)}) == -6
     assert upd_rms(d, eps=-0.5) == -2
     assert upd_rms(dims(b=0)) == 0
+
+
+def ssd(d, dtype=1, over=None, ws_bytes=1 << 40):
+    p = list(ADDR[:10])  # X B C A H0 Y dH Hfin ws
+    p[4] = None
+    p[7] = None
+    for k, v in (over or {}).items():
+        p[k] = v
+    return D.lib().dart_ssd_fwd(ctypes.byref(d), dtype, p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8],
+                                ws_bytes, None)
+
+
+def test_ssd_validation():
+    d = dims()
+    need = D.lib().dart_ssd_fwd_workspace_bytes(ctypes.byref(d), 1)
+    b, L, H, N, P, M = 2, 512, 4, 128, 64, 2
+    assert need == -(-(4 * b * H * M) // 256) * 256 + 2 * b * H * M * P * N
+    assert D.lib().dart_ssd_fwd_workspace_bytes(ctypes.byref(d), 0) == -(-(4 * b * H * M) // 256) * 256 + 4 * b * H * M * P * N
+    assert ssd(d, ws_bytes=need - 1) == -4
+    assert ssd(d, over={8: None}) == -4
+    assert ssd(d, over={2: None}) == -1 and "C" in last()
+    assert ssd(d, over={4: ctypes.c_void_p(ADDR[4].value + 4)}) == -6 and "H0" in last()
+    assert ssd(d, over={5: ctypes.c_void_p(ADDR[0].value)}) == -2 and "overlaps" in last()
+    assert ssd(dims(L=0)) == 0
+    assert ssd(d, dtype=7) == -3
