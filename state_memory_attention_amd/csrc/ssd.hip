@@ -171,6 +171,7 @@ __device__ __forceinline__ void ld_tr4(uint64_t (&o)[4], const uint32_t (&ad)[4]
 
 __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kMaxS * kP * 2];  // X tile, 128-byte rows
+  __shared__ __attribute__((aligned(16))) uint8_t s_h[kP * kN * 2];     // Hin_c^T, 256-byte rows
   __shared__ __attribute__((aligned(16))) float s_l[kMaxS];             // l_t (base 2)
   __shared__ __attribute__((aligned(16))) int s_z[kMaxS];               // last zero decay at or before t
   __shared__ float s_tl[4];
@@ -195,6 +196,14 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
       const int r = 8 * (wave + 4 * i) + (lane >> 3);  // rows in groups of 8 per load
       const int piece = (lane & 7) ^ swz_x(r);
       buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + 8 * (wave + 4 * i) * 128);
+    }
+    // the state entering the chunk, shared by every slice: wave w loads rows
+    // p = 16w .. 16w+15, pieces XOR-swizzled by the row (mem_off)
+    const auto rh = buf_rsrc(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN), kP * kN * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      buf_dma16(rh, (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4)), s_h + (16 * wave + 4 * i) * 256);
     }
   }
   // ---- l and z of the chunk's tokens: block-wide inclusive scans (sum, max)
@@ -230,7 +239,6 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
   __syncthreads();
 
   const int n_sl = a.S / 32;
-  const uint8_t* hin = (const uint8_t*)(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN));
   for (int sl2 = 0; sl2 < 2; ++sl2) {
     const int sl = sl2 == 0 ? wave : 7 - wave;
     if (sl >= n_sl || 32 * sl >= clen) continue;  // uniform per wave
@@ -249,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
     f32x16_t y0 = {}, y1 = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8_t h0 = *(const bf16x8_t*)(hin + (col * kN + 16 * kk + 8 * half) * 2);
-      const bf16x8_t h1 = *(const bf16x8_t*)(hin + ((32 + col) * kN + 16 * kk + 8 * half) * 2);
+      const bf16x8_t h0 = *(const bf16x8_t*)(s_h + mem_off(col, 2 * kk + half));
+      const bf16x8_t h1 = *(const bf16x8_t*)(s_h + mem_off(32 + col, 2 * kk + half));
       y0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, cq[kk], y0, 0, 0, 0);
       y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, cq[kk], y1, 0, 0, 0);
     }
@@ -266,12 +274,13 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
       const int sa = 32 * sb;
       const int srow = sa + col < clen ? sa + col : clen - 1;
       const bf16_t* bp = a.B + ((row0 + s0 + srow) * a.G + g) * kN + 8 * half;
+      // all eight operand loads first: one memory round trip per block of s
+      bf16x8_t bo[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) bo[kk] = *(const bf16x8_t*)(bp + 16 * kk);
       f32x16_t gt = {};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8_t bo = *(const bf16x8_t*)(bp + 16 * kk);
-        gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, cq[kk], gt, 0, 0, 0);
-      }
+      for (int kk = 0; kk < 8; ++kk) gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[kk], cq[kk], gt, 0, 0, 0);
       // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = tl.  Keep s <= t with
       // no zero decay in (s, t], weighted by 2^(l_t - l_s).
 #pragma unroll
