@@ -24,6 +24,7 @@ namespace dart {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr unsigned kWaitVm2 = 0x0f72;  // s_waitcnt vmcnt(2)
 
 // ---------------------------------------------------------------------------
 // Full decay of every chunk, A_{a_c:b_c}: one wave per (b, h, c).
@@ -127,20 +128,25 @@ __global__ __launch_bounds__(kThreads) void ssd_out_general_kernel(Shape s, cons
 // ---------------------------------------------------------------------------
 // Outputs on the matrix core: bfloat16, N = 128, P = 64, S a multiple of 32
 // up to 256.  One block per (b, h, chunk); the chunk's tokens form slices of
-// 32, wave w takes slices w and 7 - w (equal causal work).  Per slice, with
-// one token per lane and P along registers (the transposed output Y^T):
+// 32 and wave w owns slices w and 7 - w (equal causal work).  With one token
+// per lane and P along registers (the transposed output Y^T), per slice:
 //   Y^T  = Hin_c^T C^T  scaled per token by A_{a_c:t}         (Eq. 22)
 //   for every 32-token block of earlier or equal tokens s:
 //     G^T = B_s C^T  (32 s x 32 t),  masked and decayed by A_{s+1:t},
 //     Y^T += X_s^T G^T                                          (Eq. 21)
-// G^T leaves the matrix core with s along registers; a swap between the
-// half-waves (v_permlane32_swap) puts 8 consecutive s in each lane, the
-// layout of the next product's B operand, with no trip through LDS.  X^T is
-// read from the chunk's X tile in LDS with the transposing read.
+// The blocks of s are visited by all waves together: block s is staged once
+// in an LDS ring (three stages, two in flight) and serves every slice at or
+// after it.  G^T leaves the matrix core with s along registers; a swap
+// between the half-waves (v_permlane32_swap) puts 8 consecutive s in each
+// lane, the layout of the next product's B operand, with no trip through
+// LDS.  X^T is read from the chunk's X tile with the transposing LDS read;
+// Hin_c^T and B_s like the chunk memories of the SMA forward (256-byte rows,
+// pieces XOR-swizzled by the row).
 // ---------------------------------------------------------------------------
 constexpr int kN = 128;
 constexpr int kP = 64;
 constexpr int kMaxS = 256;
+constexpr int kBStage = 32 * kN * 2;  // 32 rows of B: 8 KB
 
 struct SsdArgs {
   const bf16_t* X;
@@ -156,7 +162,7 @@ struct SsdArgs {
 __device__ __forceinline__ int swz_x(int row) { return (row & 3) << 1; }
 
 // Four transposing reads that return together (the compiler's own form of
-// the read would drain the global loads in flight before it).
+// the read would drain the loads in flight before it).
 __device__ __forceinline__ void ld_tr4(uint64_t (&o)[4], const uint32_t (&ad)[4]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %4\n\t"
@@ -169,13 +175,22 @@ __device__ __forceinline__ void ld_tr4(uint64_t (&o)[4], const uint32_t (&ad)[4]
       : "memory");
 }
 
-__global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[kMaxS * kP * 2];  // X tile, 128-byte rows
-  __shared__ __attribute__((aligned(16))) uint8_t s_h[kP * kN * 2];     // Hin_c^T, 256-byte rows
-  __shared__ __attribute__((aligned(16))) float s_l[kMaxS];             // l_t (base 2)
-  __shared__ __attribute__((aligned(16))) int s_z[kMaxS];               // last zero decay at or before t
-  __shared__ float s_tl[4];
-  __shared__ int s_tz[4];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ssd_out_mfma_kernel(SsdArgs a) {
+  // One LDS object (so that the compiler adds no waits of its own for the
+  // staged loads): X tile (128-byte rows), Hin_c^T, the B ring, l and z.
+  constexpr int kOffH = kMaxS * kP * 2;
+  constexpr int kOffB = kOffH + kP * kN * 2;
+  constexpr int kOffL = kOffB + 3 * kBStage;
+  constexpr int kOffZ = kOffL + kMaxS * 4;
+  constexpr int kOffT = kOffZ + kMaxS * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kOffT + 32];
+  uint8_t* const s_x = s_lds;
+  uint8_t* const s_h = s_lds + kOffH;
+  float* const s_l = (float*)(s_lds + kOffL);
+  int* const s_z = (int*)(s_lds + kOffZ);
+  float* const s_tl = (float*)(s_lds + kOffT);
+  int* const s_tz = (int*)(s_lds + kOffT + 16);
 
   const int blk = blockIdx.x;
   const int BH = gridDim.x / a.M;
@@ -186,29 +201,43 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
   const int col = lane & 31, half = lane >> 5, grp16 = (lane >> 4) & 1, j16 = lane & 15;
   const int64_t s0 = (int64_t)c * a.S;
   const int clen = (int)((s0 + a.S < a.L) ? a.S : a.L - s0);
+  const int n_sb = (clen + 31) / 32;  // blocks of 32 tokens holding data
   const int64_t row0 = (int64_t)b * a.L;
+  // this thread's token decay, loaded before the staged loads so that waiting
+  // for it leaves them in flight
+  const float av = tid < clen ? a.A[(row0 + s0 + tid) * a.H + h] : 1.f;
 
-  // ---- X tile of the chunk (rows past its end read as zeros): wave w loads
-  // rows 64w .. 64w+63, 8 rows of 128 B per load, swizzled on the global side
+  // ---- staged loads.  X tile: wave w loads row groups w, w+4, ... (8 rows
+  // of 128 B each); Hin_c^T: rows 16w .. 16w+15; B block j: rows 8w .. 8w+7
+  // of its stage.  Rows past the chunk end read as zeros.
+  const auto rbb = buf_rsrc(a.B + ((row0 + s0) * a.G + g) * kN, (uint32_t)((clen - 1) * a.G * kN + kN) * 2);
+  auto issue_b = [&](int j) {
+    uint8_t* st = s_lds + kOffB + (j % 3) * kBStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * wave + 4 * i + (lane >> 4);  // row within the block
+      const int rr = 32 * j + r;                     // row within the chunk
+      buf_dma16(rbb, (uint32_t)(rr * a.G * kN * 2 + (((lane & 15) ^ (r & 15)) << 4)), st + (8 * wave + 4 * i) * 256);
+    }
+  };
   {
     const auto rx = buf_rsrc(a.X + ((row0 + s0) * a.H + h) * kP, (uint32_t)((clen - 1) * a.H * kP + kP) * 2);
     for (int i = 0; i < a.S / 32; ++i) {
-      const int r = 8 * (wave + 4 * i) + (lane >> 3);  // rows in groups of 8 per load
+      const int r = 8 * (wave + 4 * i) + (lane >> 3);
       const int piece = (lane & 7) ^ swz_x(r);
       buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + 8 * (wave + 4 * i) * 128);
     }
-    // the state entering the chunk, shared by every slice: wave w loads rows
-    // p = 16w .. 16w+15, pieces XOR-swizzled by the row (mem_off)
     const auto rh = buf_rsrc(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN), kP * kN * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * wave + 4 * i + (lane >> 4);
       buf_dma16(rh, (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4)), s_h + (16 * wave + 4 * i) * 256);
     }
+    issue_b(0);
+    if (n_sb > 1) issue_b(1);
   }
   // ---- l and z of the chunk's tokens: block-wide inclusive scans (sum, max)
   {
-    const float av = tid < clen ? a.A[(row0 + s0 + tid) * a.H + h] : 1.f;
     float lv = av > 0.f ? fast_log2(av) : 0.f;
     int zv = (tid < clen && av == 0.f) ? tid : -1;
 #pragma unroll
@@ -230,69 +259,94 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
       lv += s_tl[w2];
       zv = s_tz[w2] > zv ? s_tz[w2] : zv;
     }
-    if (tid < kMaxS) {
-      s_l[tid] = lv;
-      s_z[tid] = zv;
-    }
+    s_l[tid] = lv;
+    s_z[tid] = zv;
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
 
+  // ---- this wave's slices: C^T operands (lane holds a token, n = 16 kk +
+  // 8 half + 0..7), its l_t and z_t
   const int n_sl = a.S / 32;
-  for (int sl2 = 0; sl2 < 2; ++sl2) {
-    const int sl = sl2 == 0 ? wave : 7 - wave;
-    if (sl >= n_sl || 32 * sl >= clen) continue;  // uniform per wave
-    const int tl = 32 * sl + col;                 // this lane's token within the chunk
-    const bool tok_ok = tl < clen;
-    const int64_t tg = row0 + s0 + (tok_ok ? tl : clen - 1);
-    // C^T operand: lane holds token tl, n = 16 kk + 8 half + 0..7
-    bf16x8_t cq[8];
+  int sls[2] = {wave, 7 - wave};
+  bool act[2];
+  bf16x8_t cq[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    act[q] = sls[q] < n_sl && 32 * sls[q] < clen;  // uniform per wave
+    const int tl = 32 * sls[q] + col;
+    const int64_t tg = row0 + s0 + (tl < clen ? tl : clen - 1);
     const bf16_t* cp = a.C + (tg * a.G + g) * kN + 8 * half;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) cq[kk] = *(const bf16x8_t*)(cp + 16 * kk);
-    const float lt = s_l[tl < a.S ? tl : a.S - 1];
-    const int zt = s_z[tl < a.S ? tl : a.S - 1];
+    for (int kk = 0; kk < 8; ++kk) cq[q][kk] = *(const bf16x8_t*)(cp + 16 * kk);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+  float lt[2];
+  int zt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int tl = 32 * sls[q] + col;
+    lt[q] = s_l[tl < kMaxS ? tl : kMaxS - 1];
+    zt[q] = s_z[tl < kMaxS ? tl : kMaxS - 1];
+  }
 
-    // inter-chunk readout, then its decay A_{a_c:t}
-    f32x16_t y0 = {}, y1 = {};
+  // ---- inter-chunk readout, then its decay A_{a_c:t}  [Eq. 22]
+  f32x16_t y[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    y[q][0] = f32x16_t{};
+    y[q][1] = f32x16_t{};
+    if (!act[q]) continue;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8_t h0 = *(const bf16x8_t*)(s_h + mem_off(col, 2 * kk + half));
       const bf16x8_t h1 = *(const bf16x8_t*)(s_h + mem_off(32 + col, 2 * kk + half));
-      y0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, cq[kk], y0, 0, 0, 0);
-      y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, cq[kk], y1, 0, 0, 0);
+      y[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, cq[q][kk], y[q][0], 0, 0, 0);
+      y[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, cq[q][kk], y[q][1], 0, 0, 0);
     }
-    const float din = zt < 0 ? fast_exp2(lt) : 0.f;
+    const float din = zt[q] < 0 ? fast_exp2(lt[q]) : 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      y0[r] *= din;
-      y1[r] *= din;
+      y[q][0][r] *= din;
+      y[q][1][r] *= din;
     }
+  }
 
-    // intra-chunk terms, one 32-token block of s at a time
-    for (int sb = 0; sb <= sl; ++sb) {
-      const int sa = 32 * sb;
-      const int srow = sa + col < clen ? sa + col : clen - 1;
-      const bf16_t* bp = a.B + ((row0 + s0 + srow) * a.G + g) * kN + 8 * half;
-      // all eight operand loads first: one memory round trip per block of s
-      bf16x8_t bo[8];
+  // ---- intra-chunk terms, all waves on block j of s together  [Eq. 21]
+  for (int j = 0; j < n_sb; ++j) {
+    if (j > 0) {
+      // block j has landed (block j + 1 may still be in flight); every wave
+      // is done with block j - 1, whose stage takes block j + 2
+      if (j + 1 < n_sb && j + 1 >= 2)
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_barrier();
+    }
+    if (j + 2 < n_sb) issue_b(j + 2);
+    const uint8_t* bst = s_lds + kOffB + (j % 3) * kBStage;
+    const int sa = 32 * j;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) bo[kk] = *(const bf16x8_t*)(bp + 16 * kk);
+    for (int q = 0; q < 2; ++q) {
+      if (!act[q] || sls[q] < j) continue;  // uniform per wave
+      const int tl = 32 * sls[q] + col;
       f32x16_t gt = {};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[kk], cq[kk], gt, 0, 0, 0);
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8_t bo = *(const bf16x8_t*)(bst + mem_off(col, 2 * kk + half));
+        gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, cq[q][kk], gt, 0, 0, 0);
+      }
       // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = tl.  Keep s <= t with
       // no zero decay in (s, t], weighted by 2^(l_t - l_s).
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sr = sa + 8 * j + 4 * half;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int sr = sa + 8 * jj + 4 * half;
         const float4 ls = *(const float4*)(s_l + sr);
         const float lsv[4] = {ls.x, ls.y, ls.z, ls.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int sv = sr + i;
-          const bool keep = sv <= tl && zt <= sv;
-          gt[4 * j + i] = keep ? gt[4 * j + i] * fast_exp2(lt - lsv[i]) : 0.f;
+          const bool keep = sv <= tl && zt[q] <= sv;
+          gt[4 * jj + i] = keep ? gt[4 * jj + i] * fast_exp2(lt[q] - lsv[i]) : 0.f;
         }
       }
       // s to 8 consecutive values per lane: swap registers r and r + 4
@@ -329,20 +383,24 @@ __global__ __launch_bounds__(kThreads) void ssd_out_mfma_kernel(SsdArgs a) {
                                                                     (uint32_t)rd[1], (uint32_t)(rd[1] >> 32)));
         const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
                                                                     (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
-        y0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y0, 0, 0, 0);
-        y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y1, 0, 0, 0);
+        y[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y[q][0], 0, 0, 0);
+        y[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y[q][1], 0, 0, 0);
       }
     }
+  }
 
-    // Y^T[p][t]: register r of y_f holds p = 32 f + 8 (r / 4) + 4 half + r % 4
-    if (tok_ok) {
-      bf16_t* yp = a.Y + ((row0 + s0 + tl) * a.H + h) * kP + 4 * half;
+  // ---- Y^T[p][t]: register r of y[q][f] holds p = 32 f + 8 (r / 4) + 4 half + r % 4
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *(uint2*)(yp + 8 * j) = make_uint2(pack_bf16x2(y0[4 * j], y0[4 * j + 1]), pack_bf16x2(y0[4 * j + 2], y0[4 * j + 3]));
-        *(uint2*)(yp + 32 + 8 * j) =
-            make_uint2(pack_bf16x2(y1[4 * j], y1[4 * j + 1]), pack_bf16x2(y1[4 * j + 2], y1[4 * j + 3]));
-      }
+  for (int q = 0; q < 2; ++q) {
+    const int tl = 32 * sls[q] + col;
+    if (!act[q] || tl >= clen) continue;
+    bf16_t* yp = a.Y + ((row0 + s0 + tl) * a.H + h) * kP + 4 * half;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      *(uint2*)(yp + 8 * jj) = make_uint2(pack_bf16x2(y[q][0][4 * jj], y[q][0][4 * jj + 1]),
+                                          pack_bf16x2(y[q][0][4 * jj + 2], y[q][0][4 * jj + 3]));
+      *(uint2*)(yp + 32 + 8 * jj) = make_uint2(pack_bf16x2(y[q][1][4 * jj], y[q][1][4 * jj + 1]),
+                                               pack_bf16x2(y[q][1][4 * jj + 2], y[q][1][4 * jj + 3]));
     }
   }
 }
