@@ -31,11 +31,14 @@ _CSRC = "state_memory_attention_amd/csrc/"
 # hash keys a committed counter summary to the code it was taken on
 KERNEL_SOURCES = {
     "sma_fwd": [_CSRC + "sma_fwd_mfma.hip", _CSRC + "dev_common.h"],
-    "chunk_states": [_CSRC + "chunk_states_mfma.hip", _CSRC + "dev_common.h"],
+    "chunk_states": [_CSRC + "chunk_states_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "decode": [_CSRC + "sma_decode_mfma.hip", _CSRC + "dev_common.h"],
     "sma_bwd": [_CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "chunk_states_bwd": [_CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "state_update": [_CSRC + "decode_update.hip", _CSRC + "dev_common.h"],
+    "sma_fwd_rms": [_CSRC + "sma_fwd_rms_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
+    "chunk_states_rms": [_CSRC + "chunk_states_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
+    "ssd": [_CSRC + "ssd.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
 }
 
 
@@ -149,6 +152,7 @@ def time_rms(torch, dart, synth, cfg, steps=10, warmup=2, eps=1e-6):
     t_fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps / 1e3
     f_sma, _ = fwd_flops(cfg)
     res = {"workload": cfg["name"], "kernel": "dart_sma_fwd_rms", "us_per_call": t_fwd * 1e6,
+           "traffic": traffic_record("sma_fwd_rms", cfg["name"]),
            "achieved_TFLOPs": f_sma / t_fwd / 1e12, "peak_TFLOPs": PEAK_BF16_TFLOPS,
            "frac": f_sma / t_fwd / 1e12 / PEAK_BF16_TFLOPS, "chunk_states_rms_us": t_cs * 1e6,
            "tokens_per_s": b * L / (t_cs + t_fwd)}
@@ -192,7 +196,7 @@ def time_ssd(torch, dart, synth, cfg, steps=10, warmup=2):
     nbytes = 2 * (b * L * H * P * 2 + b * L * G * N * 2 + b * H * M * P * N * 3) + b * L * H * 4
     res = {"workload": cfg["name"], "kernel": "dart_ssd_fwd", "us_per_call": t * 1e6, "bytes_per_call": nbytes,
            "achieved_GBs": nbytes / t / 1e9, "peak_GBs": PEAK_HBM_GBS, "frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
-           "tokens_per_s": b * L / t}
+           "tokens_per_s": b * L / t, "traffic_out_kernel": traffic_record("ssd_out", cfg["name"], "ssd")}
     del d, Y, dH, ws
     torch.cuda.empty_cache()
     return res
@@ -379,6 +383,21 @@ def profile_kernels(launches=3):
     for _ in range(launches):
         dart.dart_chunk_states_bwd(d["X"], d["B"], d["A"], g[3], S)
     torch.cuda.synchronize()
+    del g, R, lse, dout
+    # the normalised score branch, then the SSM branch, on the same workload
+    M = dart.num_chunks(cfg["seqlen"], S)
+    dHs = torch.empty((cfg["batch"], cfg["nheads"], M, cfg["d_head"], cfg["d_state"]), dtype=torch.float16,
+                      device="cuda")
+    for _ in range(launches):
+        dart.dart_chunk_states_rms(d["X"], d["B"], d["A"], S, 1e-6, dH=dH, dH_score=dHs, want_r=False)
+    torch.cuda.synchronize()
+    out = torch.empty_like(d["Y"])
+    for _ in range(launches):
+        dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["Y"], d["gate"], S, 1e-6, out=out)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        dart.dart_ssd_fwd(d["X"], d["B"], d["C"], d["A"], S, Y=out, dH=dH)
+    torch.cuda.synchronize()
     print("profile-kernels done", flush=True)
 
 
@@ -433,7 +452,11 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
             ("sma_bwd_a", "sma_bwd", "sma_bwd_a_kernel", w2, 0),
             ("sma_bwd_bc", "sma_bwd", "sma_bwd_bc_kernel", w2, 0),
             ("sma_bwd_d", "sma_bwd", "sma_bwd_d_kernel", w2, 0),
-            ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w2, 0)]
+            ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w2, 0),
+            ("chunk_states_rms", "chunk_states_rms", "chunk_states_mfma_kernel<true>", w2, 0),
+            ("sma_fwd_rms", "sma_fwd_rms", "sma_fwd_rms_mfma_kernel", w2, 0),
+            ("ssd_out", "ssd", "ssd_out_mfma_kernel", w2, 0),
+            ("ssd_state_pass", "ssd", "state_pass_kernel", w2, 0)]
     for label, kernel, sym, workload, first in plan:
         rd, wr = per_kernel(sym, first, launches)
         rec = {"kernel": sym, "workload": workload, "source_sha256_16": source_hash(KERNEL_SOURCES[kernel]),
