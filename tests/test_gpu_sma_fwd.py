@@ -92,6 +92,21 @@ def test_mfma_stress_shapes(L, S, G, gate_pc):
     same_input_case(cfg, gains={"Q": math.sqrt(128)}, gate_pc=gate_pc, seed=L)
 
 
+@pytest.mark.parametrize("b,H,G,L,S,gate_pc", [
+    (1, 3, 3, 128 * 200 + 37, 1024, True),   # 3 of 8 head slots real, ragged tail tile
+    (1, 2, 1, 128 * 70 + 5, 64, False),      # long tiles of many small chunks, scalar gate
+    (2, 4, 2, 128 * 80, 256, True),          # no padded head slots
+])
+def test_mfma_several_tiles_per_block(b, H, G, L, S, gate_pc):
+    # More (head, tile) items than the chip holds 128-token tiles at once (two
+    # per compute unit), with padded head slots, a ragged tail and long tiles
+    # of many small chunks; every output is checked.
+    cfg = dict(BF, batch=b, nheads=H, ngroups=G, seqlen=L, chunk=S)
+    items = (b * H + 7) // 8 * 8 * ((L + 127) // 128)
+    assert items > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    same_input_case(cfg, gains={"Q": math.sqrt(128)}, gate_pc=gate_pc, seed=L + S)
+
+
 @pytest.mark.parametrize("N,P,dtype,L,S", [
     (16, 16, "f32", 1024, 64), (64, 32, "bf16", 500, 32), (7, 5, "f32", 300, 16),
     (256, 256, "f32", 192, 64), (1, 1, "f32", 50, 5), (128, 64, "f32", 700, 256),
