@@ -33,6 +33,7 @@ constexpr int kTile = 128;       // tokens per block in the token-major passes
 constexpr int kThreads = 256;
 constexpr int kMemBytes = kP * kN * 2;
 constexpr int kRing = 4;         // LDS buffers for chunk memories (3 in flight)
+constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access: streamed, not kept in L2
 
 // ---------------------------------------------------------------------------
 // Pass A
@@ -88,8 +89,12 @@ void sma_bwd_a_kernel(BwdAArgs a) {
   const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
   const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
   auto slot_buf = [&](int s) -> uint8_t* { return s == 0 ? s_e : s_mem + ((s - 1) % kRing) * kMemBytes; };
+  // A slot past the last chunk is a zero-length stand-in (it reads nothing
+  // and fills a buffer no later chunk uses), so that every slot costs every
+  // wave 4 loads and the loop's waits are fixed counts.
   auto issue_mem = [&](int s) {
-    const auto rs = buf_rsrc(mem_head + (int64_t)s * kMemBytes, kMemBytes);
+    const bool real = s < n_hist;
+    const auto rs = buf_rsrc(mem_head + (int64_t)(real ? s : 0) * kMemBytes, real ? kMemBytes : 0u);
     uint8_t* dst = slot_buf(s) + wave * 16 * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -182,21 +187,32 @@ void sma_bwd_a_kernel(BwdAArgs a) {
 
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
-  for (int s = 1; s < kRing - 1 && s < n_hist; ++s) issue_mem(s);
+  if (n_hist > 0) {
+    issue_mem(1);
+    issue_mem(2);
+  }
 
-  // (p, dl) rows of this wave's 32 tokens: a uniform base per chunk plus the lane
+  // (p, dl) rows of this wave's 32 tokens: a uniform base per chunk plus the
+  // lane.  Both rows are written by buffer stores of every lane (those of
+  // the second half-wave, and tokens past the end, fall outside the
+  // resource and are dropped), so that each chunk costs exactly 2 stores.
   const int64_t pd_base = (int64_t)bh * a.M * 2 * a.L + t0 + 32 * wave;
+  const int64_t nv = a.L - (t0 + 32 * wave);
+  const uint32_t pd_bytes = (uint32_t)(nv < 32 ? (nv > 0 ? nv : 0) : 32) * 4;
+  const uint32_t pd_voff = half ? 0x80000000u : (uint32_t)col * 4;
   for (int j = 0; j < n_hist; ++j) {
-    // chunk j landed everywhere, chunk j-1 free (see the forward kernel)
-    if (j > 0) {
-      if (n_hist - 1 - j >= 2)
-        __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
-      else if (n_hist - 1 - j == 1)
-        __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
-      else
-        __builtin_amdgcn_s_waitcnt(kWaitVm0 & kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();
-    }
+    // Chunk j landed everywhere, chunk j-1 free (see the forward kernel).
+    // In flight after slot j's loads: slots j+1 and j+2 (4 loads each, real
+    // or stand-in) and the (p, dl) stores of the chunks since slot j was
+    // issued (2 each: chunks j-3 .. j-1, or 0 .. j-1 for the slots issued
+    // before the loop).
+    if (j == 1)
+      __builtin_amdgcn_s_waitcnt(0x007a);  // vmcnt(10) lgkmcnt(0)
+    else if (j == 2)
+      __builtin_amdgcn_s_waitcnt(0x007c);  // vmcnt(12) lgkmcnt(0)
+    else if (j > 2)
+      __builtin_amdgcn_s_waitcnt(0x007e);  // vmcnt(14) lgkmcnt(0)
+    if (j > 0) __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(1);
     f32x16_t w0 = {}, w1 = {}, v0 = {}, v1 = {};
     const uint8_t* sm = slot_buf(j);
@@ -214,7 +230,7 @@ void sma_bwd_a_kernel(BwdAArgs a) {
       w1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], w1, 0, 0, 0);
       v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cf[ks], v0, 0, 0, 0);
       v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cf[ks], v1, 0, 0, 0);
-      if (ks == 1 && j + kRing - 1 < n_hist) issue_mem(j + kRing - 1);
+      if (ks == 1) issue_mem(j + kRing - 1);
       if (ks == 0) __builtin_amdgcn_s_setprio(2);
     }
 #pragma unroll
@@ -267,12 +283,16 @@ void sma_bwd_a_kernel(BwdAArgs a) {
       de[0][r] = fmaf(dls, w0[r], de[0][r]);
       de[1][r] = fmaf(dls, w1[r], de[1][r]);
     }
-    if (half == 0 && tok_ok) {
+    {
+      // streamed out, read back by later passes only: non-temporal
       const int64_t rowj = pd_base + (int64_t)j * 2 * a.L;
-      a.pd[rowj + col] = pj;
-      a.pd[rowj + a.L + col] = dls;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pj), buf_rsrc(a.pd + rowj, pd_bytes), pd_voff, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dls), buf_rsrc(a.pd + rowj + a.L, pd_bytes), pd_voff, 0,
+                                            kNonTemporal);
     }
   }
+  // the stand-in slots past the last chunk land before the block ends
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   if (tok_ok) {
     float* dp = a.dE + (((row0 + t) * a.dE_heads) + (a.dE_heads == a.H ? h : g)) * kP + 4 * half;
@@ -580,42 +600,102 @@ __device__ __forceinline__ int swz_b(int row) { return (row & 3) << 2; }
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
-// Six transposing reads plus eight 16-byte reads (the weights of the block's
-// chunks), returned together like ld_tr6: the compiler would otherwise drain
-// the loads in flight before reading the weights of the staged slot.
-__device__ __forceinline__ void ld_tr6_w8(uint64_t (&o)[6], f32x4v_t (&w)[8], const uint32_t (&ad)[6],
-                                          uint32_t wad) {
+// Ten transposing reads plus one 4-byte read (this lane's weight), returned
+// together like ld_tr6: the compiler would otherwise drain the loads in
+// flight before reading the weights of the staged slot.  k-step KS of a
+// sub-block reads 16 KS token rows further on: its addresses are those of
+// k-step 0 plus immediate offsets (rows of 128 B for ad[0..1], 256 B for
+// ad[2..9], 4 B per weight).
+template <int KS>
+__device__ __forceinline__ void ld_tr10_w1(uint64_t (&o)[10], uint32_t& w, const uint32_t (&ad)[10], uint32_t wad) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %14\n\t"
-      "ds_read_b64_tr_b16 %1, %15\n\t"
-      "ds_read_b64_tr_b16 %2, %16\n\t"
-      "ds_read_b64_tr_b16 %3, %17\n\t"
-      "ds_read_b64_tr_b16 %4, %18\n\t"
-      "ds_read_b64_tr_b16 %5, %19\n\t"
-      "ds_read_b128 %6, %20\n\t"
-      "ds_read_b128 %7, %20 offset:16\n\t"
-      "ds_read_b128 %8, %20 offset:256\n\t"
-      "ds_read_b128 %9, %20 offset:272\n\t"
-      "ds_read_b128 %10, %20 offset:512\n\t"
-      "ds_read_b128 %11, %20 offset:528\n\t"
-      "ds_read_b128 %12, %20 offset:768\n\t"
-      "ds_read_b128 %13, %20 offset:784\n\t"
+      "ds_read_b64_tr_b16 %0, %11 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %2, %13 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %3, %14 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %4, %15 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %7, %18 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %8, %19 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%23\n\t"
+      "ds_read_b32 %10, %21 offset:%24\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(w[0]),
-        "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(wad)
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+        "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(w)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "v"(ad[8]), "v"(ad[9]), "v"(wad), "i"(KS * 16 * 128), "i"(KS * 16 * 256), "i"(KS * 16 * 4)
       : "memory");
+}
+
+// Weight of lane I of this lane's row of 16 (a DPP row broadcast, folded by
+// the compiler into the multiply that uses it).
+template <int I>
+__device__ __forceinline__ float row_bcast(uint32_t wbits) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)wbits, 0x150 + I, 0xf, 0xf, false));
+}
+
+// 8 bf16 (a k-step's 8 tokens of one row) times the weights of chunk E (row
+// lanes 8 E + 0..7 hold that chunk's weights of the lane's 8 tokens), rounded
+// back to bf16.
+template <int E>
+__device__ __forceinline__ bf16x8_t scale_by_row_weights(const float (&x)[8], uint32_t wbits) {
+  uint4 r;
+  r.x = pack_bf16x2(x[0] * row_bcast<8 * E + 0>(wbits), x[1] * row_bcast<8 * E + 1>(wbits));
+  r.y = pack_bf16x2(x[2] * row_bcast<8 * E + 2>(wbits), x[3] * row_bcast<8 * E + 3>(wbits));
+  r.z = pack_bf16x2(x[4] * row_bcast<8 * E + 4>(wbits), x[5] * row_bcast<8 * E + 5>(wbits));
+  r.w = pack_bf16x2(x[6] * row_bcast<8 * E + 6>(wbits), x[7] * row_bcast<8 * E + 7>(wbits));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// One k-step (16 tokens) of a staged sub-block of pass D: this lane's reads
+// at `ad` (k-step 0) plus the k-step's offsets (token rows 16 KS + r keep
+// the swizzle of rows r, which depends on r & 3), its weight slot at `wad`.
+template <int KS>
+__device__ __forceinline__ void d_kstep(const uint32_t (&ad)[10], uint32_t wad, int64_t sb, int64_t first1,
+                                      int64_t wfirst, int half, int lane, f32x16_t (&acc)[2][4]) {
+  uint64_t rd[10];
+  uint32_t wbits;
+  ld_tr10_w1<KS>(rd, wbits, ad, wad);
+  // tokens before the weight's chunk sees them carry no weight
+  if (sb < first1) {
+    const int64_t tok = sb + 16 * KS + 8 * half + (lane & 7);
+    wbits = tok >= wfirst ? wbits : 0u;
+  }
+  float x[8];
+  x[0] = bf16lo((uint32_t)rd[0]); x[1] = bf16hi((uint32_t)rd[0]);
+  x[2] = bf16lo((uint32_t)(rd[0] >> 32)); x[3] = bf16hi((uint32_t)(rd[0] >> 32));
+  x[4] = bf16lo((uint32_t)rd[1]); x[5] = bf16hi((uint32_t)rd[1]);
+  x[6] = bf16lo((uint32_t)(rd[1] >> 32)); x[7] = bf16hi((uint32_t)(rd[1] >> 32));
+  // both chunks every k-step (branches here would copy accumulators): a
+  // chunk that sees none of the sub-block has all weights zeroed above,
+  // and a chunk past the last one is never stored
+  const bf16x8_t as0 = scale_by_row_weights<0>(x, wbits);
+  const bf16x8_t as1 = scale_by_row_weights<1>(x, wbits);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const bf16x8_t bn = __builtin_bit_cast(
+        bf16x8_t, make_uint4((uint32_t)rd[2 + 2 * nb], (uint32_t)(rd[2 + 2 * nb] >> 32),
+                             (uint32_t)rd[3 + 2 * nb], (uint32_t)(rd[3 + 2 * nb] >> 32)));
+    acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as0, bn, acc[0][nb], 0, 0, 0);
+    acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as1, bn, acc[1][nb], 0, 0, 0);
+  }
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sma_bwd_d_kernel(BwdDArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kStagesD * kStageD];
 
-  // heads fastest, chunk groups from the first (longest token stream) on
+  // One block per (head, chunk group, term): heads fastest, then the two
+  // terms, chunk groups from the first (longest token stream) on.  The two
+  // terms of a chunk group stream disjoint inputs (dR, C and p; E, Q and dl)
+  // and add into a zeroed d_dH: two addends per entry, so the sum does not
+  // depend on their order.
   const int blk = blockIdx.x;
   const int bh = blk % a.BHp;
   if (bh >= a.BH) return;
-  const int cg = blk / a.BHp;
+  const int term = (blk / a.BHp) & 1;
+  const int cg = blk / (2 * a.BHp);
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -624,18 +704,16 @@ void sma_bwd_d_kernel(BwdDArgs a) {
   const int64_t row0 = (int64_t)b * a.L;
   const int64_t ts = (int64_t)(c0 + 1) * a.S;          // first token any chunk of the block sees
   const int64_t n_tok = ts < a.L ? a.L - ts : 0;
-  const int nsb = (int)((n_tok + kSB - 1) / kSB);
-  const int n_steps = 2 * nsb;                          // term 1 sub-blocks, then term 2
+  const int n_steps = (int)((n_tok + kSB - 1) / kSB);   // sub-blocks of 64 tokens
 
-  // Step q: term = q / nsb, sub-block nsb - 1 - q % nsb: the tokens are
-  // streamed from the end of the sequence, so the chunk groups of one head
-  // (same XCD) start on the same tiles and share them in L2.  Wave w loads
-  // rows 16w..16w+15 of both tiles (2 + 4 loads) and the weights of chunk
-  // c0 + w (1 load).
+  // Step q streams sub-block n_steps - 1 - q: the tokens are streamed from
+  // the end of the sequence, so the chunk groups of one head (same XCD)
+  // start on the same tiles and share them in L2.  Wave w loads rows
+  // 16w..16w+15 of both tiles (2 + 4 loads) and the weights of chunk c0 + w
+  // (1 load).
   auto issue = [&](int q) {
     const bool live = q < n_steps;
-    const int term = live ? q / nsb : 0;
-    const int sbk = live ? nsb - 1 - q % nsb : 0;
+    const int sbk = live ? n_steps - 1 - q : 0;
     const int64_t sb = ts + (int64_t)sbk * kSB;
     const int cnt = live ? (int)((a.L - sb) < kSB ? (a.L - sb) : kSB) : 1;
     uint8_t* st = s_lds + (q % kStagesD) * kStageD;
@@ -669,9 +747,38 @@ void sma_bwd_d_kernel(BwdDArgs a) {
 #pragma unroll
   for (int q = 0; q < kStagesD; ++q) issue(q);
 
-  f32x16_t acc[kChunksD][2];
+  // Wave w computes p rows 32 ph .. 32 ph + 31 (ph = w & 1) of the two
+  // chunks c0 + 2 cp, c0 + 2 cp + 1 (cp = w >> 1) over all 128 n: the scaled
+  // operand (dR or E, 8 values per lane and k-step) serves four MFMAs per
+  // chunk.
+  const int ph = wave & 1, cp = wave >> 1;
+  f32x16_t acc[2][4];
 #pragma unroll
-  for (int k = 0; k < kChunksD; ++k) acc[k][0] = acc[k][1] = f32x16_t{};
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[e][nb] = f32x16_t{};
+  // first token chunk c0 + 2 cp + e sees; this lane's weight slot: chunk
+  // 2 cp + e with e = (lane >> 3) & 1, token 8 half + (lane & 7) of a k-step
+  const int64_t first0 = (int64_t)(c0 + 2 * cp + 1) * a.S, first1 = first0 + a.S;
+  const int we = (lane >> 3) & 1;
+  const int64_t wfirst = we ? first1 : first0;
+  const uint32_t w_lane = (uint32_t)((2 * cp + we) * kSB + 8 * half + (lane & 7)) * 4;
+  // this lane's read offsets in k-step 0 of a staged sub-block: dR or E
+  // (row p 32 ph + ..., 128-byte token rows) and C or Q (n block nb,
+  // 256-byte token rows), each as two reads of 4 tokens
+  uint32_t lane_off[10];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 8 * half + 4 * hh + (j16 >> 2);
+    const int cb = 16 * grp16 + 4 * (j16 & 3);
+    const int pb = 32 * ph + cb;
+    lane_off[hh] = r * 128 + (((pb >> 3) ^ swz_x(r)) << 4) + ((pb & 7) >> 2) * 8;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int nc = 32 * nb + cb;
+      lane_off[2 + 2 * nb + hh] = r * 256 + (((nc >> 3) ^ swz_b(r)) << 4) + ((nc & 7) >> 2) * 8;
+    }
+  }
 
   for (int q = 0; q < n_steps; ++q) {
     const int after = n_steps - 1 - q;
@@ -686,79 +793,50 @@ void sma_bwd_d_kernel(BwdDArgs a) {
     asm volatile("" ::: "memory");
     if (q >= 1 && q + 2 < n_steps) issue(q + 2);
 
-    const int term = q / nsb;
-    const int64_t sb = ts + (int64_t)(nsb - 1 - q % nsb) * kSB;
+    const int64_t sb = ts + (int64_t)(n_steps - 1 - q) * kSB;
+    // skip a sub-block that neither chunk of the wave sees (uniform); a
+    // chunk whose first visible token lies inside or after it has the
+    // earlier tokens' weights zeroed
+    if (c0 + 2 * cp >= a.M || sb + kSB <= first0) continue;
     const uint8_t* st = s_lds + (q % kStagesD) * kStageD;
     const uint32_t sa = lds_addr(st), sbb = sa + kATile;
     const uint32_t swt = sa + kATile + kBTile;  // weights: chunk k at + 256 k
-    // chunks that see some token of this sub-block (uniform); a chunk whose
-    // first visible token lies inside the sub-block is masked per token
+    uint32_t ad[10];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) ad[i] = (i < 2 ? sa : sbb) + lane_off[i];
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < kSB / 16; ++ks) {
-      uint32_t ad[6];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = 16 * ks + 8 * half + 4 * hh + (j16 >> 2);
-        const int cb = 16 * grp16 + 4 * (j16 & 3);
-        const int nb = 32 * wave + cb;
-        ad[hh] = sbb + r * 256 + (((nb >> 3) ^ swz_b(r)) << 4) + ((nb & 7) >> 2) * 8;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int pb = 32 * f + cb;
-          ad[2 + 2 * f + hh] = sa + r * 128 + (((pb >> 3) ^ swz_x(r)) << 4) + ((pb & 7) >> 2) * 8;
-        }
-      }
-      uint64_t rd[6];
-      f32x4v_t wv[8];  // chunk k: tokens 16 ks + 8 half + 0..3 (2k), + 4..7 (2k+1)
-      ld_tr6_w8(rd, wv, ad, swt + (16 * ks + 8 * half) * 4);
-      const uint2 b0 = __builtin_bit_cast(uint2, rd[0]), b1 = __builtin_bit_cast(uint2, rd[1]);
-      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
-                                                                  (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
-      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[4], (uint32_t)(rd[4] >> 32),
-                                                                  (uint32_t)rd[5], (uint32_t)(rd[5] >> 32)));
-      const int64_t tk = sb + 16 * ks + 8 * half;  // this lane's first token of the k-step
-#pragma unroll
-      for (int k = 0; k < kChunksD; ++k) {
-        const int64_t first = (int64_t)(c0 + k + 1) * a.S;  // chunk c0+k sees tokens >= first
-        if (c0 + k >= a.M || sb + kSB <= first) continue;    // uniform: nothing to add
-        float4 w0 = make_float4(wv[2 * k][0], wv[2 * k][1], wv[2 * k][2], wv[2 * k][3]);
-        float4 w1 = make_float4(wv[2 * k + 1][0], wv[2 * k + 1][1], wv[2 * k + 1][2], wv[2 * k + 1][3]);
-        if (sb < first) {  // straddling sub-block: drop the tokens before `first`
-          w0.x = tk + 0 >= first ? w0.x : 0.f; w0.y = tk + 1 >= first ? w0.y : 0.f;
-          w0.z = tk + 2 >= first ? w0.z : 0.f; w0.w = tk + 3 >= first ? w0.w : 0.f;
-          w1.x = tk + 4 >= first ? w1.x : 0.f; w1.y = tk + 5 >= first ? w1.y : 0.f;
-          w1.z = tk + 6 >= first ? w1.z : 0.f; w1.w = tk + 7 >= first ? w1.w : 0.f;
-        }
-        uint4 bs;
-        bs.x = pack_bf16x2(bf16lo(b0.x) * w0.x, bf16hi(b0.x) * w0.y);
-        bs.y = pack_bf16x2(bf16lo(b0.y) * w0.z, bf16hi(b0.y) * w0.w);
-        bs.z = pack_bf16x2(bf16lo(b1.x) * w1.x, bf16hi(b1.x) * w1.y);
-        bs.w = pack_bf16x2(bf16lo(b1.y) * w1.z, bf16hi(b1.y) * w1.w);
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bs);
-        acc[k][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, acc[k][0], 0, 0, 0);
-        acc[k][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, acc[k][1], 0, 0, 0);
-      }
-    }
+    d_kstep<0>(ad, swt + w_lane, sb, first1, wfirst, half, lane, acc);
+    d_kstep<1>(ad, swt + w_lane, sb, first1, wfirst, half, lane, acc);
+    d_kstep<2>(ad, swt + w_lane, sb, first1, wfirst, half, lane, acc);
+    d_kstep<3>(ad, swt + w_lane, sb, first1, wfirst, half, lane, acc);
     __builtin_amdgcn_s_setprio(0);
   }
 
   // a block with no token to stream still issued its (zero-length) prologue
   // loads into LDS: let them land before the block ends
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (n_steps == 0) return;
 
-  // d_dH_c^T[p][n]: register r of row block rb is p = 32 rb + 8 (r/4) + 4 half + r%4
+  // d_dH_c^T[p][n] += this term: register r holds p = 32 ph + 8 (r/4) +
+  // 4 half + r%4, n = 32 nb + lane % 32
 #pragma unroll
-  for (int k = 0; k < kChunksD; ++k) {
-    if (c0 + k >= a.M) continue;
-    float* outp = a.ddH + ((int64_t)bh * a.M + c0 + k) * (kP * kN) + 32 * wave + (lane & 31);
+  for (int e = 0; e < 2; ++e) {
+    const int c = c0 + 2 * cp + e;
+    if (c >= a.M) continue;
+    float* outp = a.ddH + ((int64_t)bh * a.M + c) * (kP * kN) + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int p = 8 * (r >> 2) + 4 * half + (r & 3);
-      outp[p * kN] = acc[k][0][r];
-      outp[(32 + p) * kN] = acc[k][1][r];
+      const int p = 32 * ph + 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) unsafeAtomicAdd(outp + p * kN + 32 * nb, acc[e][nb][r]);
     }
   }
+}
+
+// d_dH = 0 before the two terms add into it.
+__global__ __launch_bounds__(256) void zero_f32_kernel(float4* p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace
@@ -782,8 +860,12 @@ hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, 
   a.BH = (int)(s.b * s.H);
   a.BHp = (a.BH + 7) / 8 * 8;
   a.inv_sqrt_n = 1.f / sqrtf((float)kN);
-  const int64_t blocks = (int64_t)a.BHp * a.n_groups;
+  const int64_t blocks = (int64_t)a.BHp * a.n_groups * 2;
   if (blocks == 0) return hipSuccess;
+  // every d_dH entry is a sum of the two terms' blocks (kP * kN floats per
+  // chunk memory: a whole number of float4)
+  const int64_t n4 = s.b * s.H * s.M * (kP * kN) / 4;
+  zero_f32_kernel<<<dim3((unsigned)(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096)), dim3(256), 0, st>>>((float4*)ddH, n4);
   sma_bwd_d_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }

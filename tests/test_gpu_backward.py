@@ -142,6 +142,22 @@ def test_bwd_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_mfma_bwd_deterministic_many_chunk_groups():
+    """The d_dH pass adds its two terms into a zeroed d_dH from separate
+    blocks; with two addends per entry the sum must not depend on which
+    lands first.  Several chunk groups per head, chunk starts inside a
+    64-token sub-block, grouped heads; three runs must agree bit for bit."""
+    cfg = dict(batch=2, nheads=4, ngroups=2, seqlen=2500, chunk=96, d_state=128, d_head=64, dtype="bf16")
+    d = synth.draw_fwd(**cfg, seed=44)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, 128, 64, "bf16", seed=45)
+    dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], 64), "bf16", 46)
+    runs = [gpu_fwd_bwd(d, mem, cfg, dout, True)[0] for _ in range(3)]
+    for r in runs[1:]:
+        for k in runs[0]:
+            assert np.array_equal(runs[0][k], r[k]), k
+
+
 # bf16, N = 128, P = 64: the matrix-core backward.  Shapes chosen to exercise
 # tiles spanning several chunks (S < 128), chunk starts inside a 64-token
 # sub-block of the d_dH pass (S % 64 != 0), grouped heads, a ragged tail,
