@@ -1,4 +1,8 @@
 // Device helpers shared by the MFMA kernels: direct global->LDS loads, explicit
+// Cache-policy bit of a buffer access for data streamed once: non-temporal,
+// so that the stream does not evict data that other blocks re-read from L2.
+constexpr int kNonTemporal = 2;
+
 // s_waitcnt immediates and the swizzled layout of a staged chunk memory.
 #pragma once
 

@@ -33,7 +33,6 @@ constexpr int kTile = 128;       // tokens per block in the token-major passes
 constexpr int kThreads = 256;
 constexpr int kMemBytes = kP * kN * 2;
 constexpr int kRing = 4;         // LDS buffers for chunk memories (3 in flight)
-constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access: streamed, not kept in L2
 
 // ---------------------------------------------------------------------------
 // Pass A

@@ -36,6 +36,7 @@
 // (b, h) lands on the same XCD and reuses that head's chunk memories in its L2.
 #include "dart_internal.h"
 #include "dev_common.h"
+#include "lds_dma.h"
 
 namespace dart {
 namespace {
@@ -64,42 +65,6 @@ struct FwdArgs {
   int BH, BHp, n_tiles;
   float e_scale;  // log2(e) / sqrt(N)
 };
-
-// Byte offset of 16-byte piece `piece` (0..15) of row `row` (0..63) of a
-// staged dH_j^T: rows are 256 bytes, pieces XOR-swizzled by the row.
-__device__ __forceinline__ uint32_t mem_off(int row, int piece) {
-  return (uint32_t)(row * 256 + ((piece ^ (row & 15)) << 4));
-}
-
-// One direct global->LDS load: every lane fetches 16 bytes from `src`, and
-// lane l's bytes land at lds + 16 l (the LDS address is wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
-// The same through a buffer resource (bytes [0, nbytes) of `base`; a lane
-// offset past the end reads zeros).  The compiler counts a global-to-LDS load
-// as an access that may still be outstanding on the LDS counter as well, which
-// turns every LDS wait it places while one is in flight into a full drain; the
-// buffer form is counted on the vector-memory counter only.  The loads that
-// stay in flight across the chunk loop use this form.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
-  // word 3: 32-bit data format, the value every gfx9 raw buffer access uses
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
-}
-__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
-                                           0, 0, 0);
-}
-
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt
-// in 11:8; a field at its maximum does not wait).  Issued as builtins, not as
-// inline asm, so that the compiler's own wait insertion takes them into account.
-constexpr unsigned kWaitAll = 0x0000;
-constexpr unsigned kWaitVm0 = 0x0f70;
-constexpr unsigned kWaitLgkm0 = 0xc07f;
-constexpr unsigned kWaitVm4Lgkm0 = 0x0074;
-constexpr unsigned kWaitVm8Lgkm0 = 0x0078;
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sma_fwd_mfma_kernel(FwdArgs a) {
