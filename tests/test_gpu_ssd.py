@@ -51,6 +51,15 @@ CASES = [
     (dict(batch=1, seqlen=333, nheads=2, ngroups=2, d_state=128, d_head=64, chunk=32, dtype="bf16"), False, (40, 41)),
     (dict(batch=1, seqlen=450, nheads=2, ngroups=2, d_state=128, d_head=64, chunk=100, dtype="bf16"), True, ()),
     (dict(batch=1, seqlen=600, nheads=2, ngroups=1, d_state=32, d_head=48, chunk=128, dtype="bf16"), True, ()),
+    # weak decay (A_t ~ 0.99): terms from every earlier 32-token slice of a
+    # chunk and from earlier chunks stay large; zero decays on both sides of
+    # slice boundaries (63 | 64, 287 | 288) and inside a slice (200)
+    (dict(batch=1, seqlen=1100, nheads=2, ngroups=2, d_state=128, d_head=64, chunk=256, dtype="bf16",
+          a_lo=0.01, a_hi=0.05), True, (63, 64, 200, 287, 288)),
+    (dict(batch=2, seqlen=1000, nheads=2, ngroups=1, d_state=128, d_head=64, chunk=128, dtype="bf16",
+          a_lo=0.01, a_hi=0.05), False, (31, 32, 95, 700)),
+    (dict(batch=1, seqlen=2048, nheads=3, ngroups=3, d_state=128, d_head=64, chunk=256, dtype="bf16",
+          a_lo=0.01, a_hi=0.05), True, ()),
 ]
 
 
