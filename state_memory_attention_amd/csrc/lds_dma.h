@@ -3,6 +3,18 @@
 // so that the stream does not evict data that other blocks re-read from L2.
 constexpr int kNonTemporal = 2;
 
+// A pointer made wave-uniform in the compiler's eyes (its value is the same
+// in every lane): a buffer resource formed from it then lives in scalar
+// registers, where a resource the compiler takes for divergent costs a loop
+// over lanes around every access.
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 // s_waitcnt immediates and the swizzled layout of a staged chunk memory.
 #pragma once
 

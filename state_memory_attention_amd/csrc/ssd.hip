@@ -175,6 +175,104 @@ __device__ __forceinline__ void ld_tr4(uint64_t (&o)[4], const uint32_t (&ad)[4]
       : "memory");
 }
 
+// Four 16-byte LDS reads at addr + 32 i (i = 0..3) that return together.
+// Written out so that the compiler, which cannot tell these reads from the
+// B stage being filled by a direct-to-LDS load, does not drain that load
+// (the next block's prefetch) before them.
+__device__ __forceinline__ void ld_lds4(float4 (&o)[4], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:32\n\t"
+      "ds_read_b128 %2, %4 offset:64\n\t"
+      "ds_read_b128 %3, %4 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(addr)
+      : "memory");
+}
+
+// Intra-chunk terms of block j of s (32 tokens from sa = 32 j, staged at bst)
+// for the NQ slices Q0 .. Q0 + NQ - 1 of this wave, all of which see it:
+// one straight-line body, so that the B and X operands and l_s are read
+// once for all of them and their matrix-core chains interleave.  Scores
+// G^T = B_s C^T (the slice's C^T operands cq), weighted by 2^(l_t - l_s) for
+// s <= t with no zero decay in (s, t], then Y^T += X_s^T G^T  [App. A Eq. 21].
+template <int Q0, int NQ>
+__device__ __forceinline__ void ssd_intra_block(f32x16_t (&y)[2][2], const bf16x8_t (&cq)[2][8], const float (&lt)[2],
+                                                const int (&zt)[2], const int (&sls)[2], const uint8_t* bst,
+                                                const uint8_t* s_x, const float* s_l, int sa, int col, int half,
+                                                int grp16, int j16) {
+  bf16x8_t bo[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) bo[kk] = *(const bf16x8_t*)(bst + mem_off(col, 2 * kk + half));
+  f32x16_t gt[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) gt[i] = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) gt[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[kk], cq[Q0 + i][kk], gt[i], 0, 0, 0);
+  // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = the lane's token
+  float4 lsq[4];
+  ld_lds4(lsq, lds_addr(s_l + sa + 4 * half));
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int sr = sa + 8 * jj + 4 * half;
+    const float lsv[4] = {lsq[jj].x, lsq[jj].y, lsq[jj].z, lsq[jj].w};
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = Q0 + i;
+      const int tl = 32 * sls[q] + col;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sv = sr + e;
+        const bool keep = sv <= tl && zt[q] <= sv;
+        gt[i][4 * jj + e] = keep ? gt[i][4 * jj + e] * fast_exp2(lt[q] - lsv[e]) : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // X^T operands (p rows, 8 consecutive s) from the X tile: lane (column
+    // j16 + 16 grp16, k-octet half) receives tokens ... + 4 hh + 0..3 of read
+    // hh, addressing token row ... + 4 hh + j16 / 4
+    uint32_t ad[4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = sa + 16 * kb + 8 * half + 4 * hh + (j16 >> 2);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int pb = 32 * f + 16 * grp16 + 4 * (j16 & 3);
+        ad[2 * f + hh] = lds_addr(s_x + r * 128 + (((pb >> 3) ^ swz_x(r)) << 4) + ((pb & 7) >> 2) * 8);
+      }
+    }
+    uint64_t rd[4];
+    ld_tr4(rd, ad);
+    const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[0], (uint32_t)(rd[0] >> 32),
+                                                                (uint32_t)rd[1], (uint32_t)(rd[1] >> 32)));
+    const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
+                                                                (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      // s to 8 consecutive values per lane: swap registers r and r + 4
+      // between the half-waves, then two k-steps of 16 s each
+      float xs[4], ys[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gt[i][8 * kb + e]),
+                                                         __float_as_uint(gt[i][8 * kb + 4 + e]), false, false);
+        xs[e] = __uint_as_float(sw[0]);
+        ys[e] = __uint_as_float(sw[1]);
+      }
+      const bf16x8_t mop = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]), pack_bf16x2(ys[0], ys[1]),
+                               pack_bf16x2(ys[2], ys[3])));
+      y[Q0 + i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y[Q0 + i][0], 0, 0, 0);
+      y[Q0 + i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y[Q0 + i][1], 0, 0, 0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssd_out_mfma_kernel(SsdArgs a) {
   // One LDS object (so that the compiler adds no waits of its own for the
@@ -204,13 +302,17 @@ void ssd_out_mfma_kernel(SsdArgs a) {
   const int n_sb = (clen + 31) / 32;  // blocks of 32 tokens holding data
   const int64_t row0 = (int64_t)b * a.L;
   // this thread's token decay, loaded before the staged loads so that waiting
-  // for it leaves them in flight
-  const float av = tid < clen ? a.A[(row0 + s0 + tid) * a.H + h] : 1.f;
+  // for it leaves them in flight; without a branch (threads past the chunk
+  // end re-read its last token), so that the addresses below are not formed
+  // in divergent code, where the compiler would keep the buffer resources
+  // in vector registers and loop over lanes for every load
+  const float a_raw = a.A[(row0 + s0 + (tid < clen ? tid : clen - 1)) * a.H + h];
+  const float av = tid < clen ? a_raw : 1.f;
 
   // ---- staged loads.  X tile: wave w loads row groups w, w+4, ... (8 rows
   // of 128 B each); Hin_c^T: rows 16w .. 16w+15; B block j: rows 8w .. 8w+7
   // of its stage.  Rows past the chunk end read as zeros.
-  const auto rbb = buf_rsrc(a.B + ((row0 + s0) * a.G + g) * kN, (uint32_t)((clen - 1) * a.G * kN + kN) * 2);
+  const auto rbb = buf_rsrc(wave_uniform(a.B + ((row0 + s0) * a.G + g) * kN), (uint32_t)((clen - 1) * a.G * kN + kN) * 2);
   auto issue_b = [&](int j) {
     uint8_t* st = s_lds + kOffB + (j % 3) * kBStage;
 #pragma unroll
@@ -221,13 +323,15 @@ void ssd_out_mfma_kernel(SsdArgs a) {
     }
   };
   {
-    const auto rx = buf_rsrc(a.X + ((row0 + s0) * a.H + h) * kP, (uint32_t)((clen - 1) * a.H * kP + kP) * 2);
-    for (int i = 0; i < a.S / 32; ++i) {
+    const auto rx = buf_rsrc(wave_uniform(a.X + ((row0 + s0) * a.H + h) * kP), (uint32_t)((clen - 1) * a.H * kP + kP) * 2);
+#pragma unroll
+    for (int i = 0; i < kMaxS / 32; ++i) {
+      if (i >= a.S / 32) break;
       const int r = 8 * (wave + 4 * i) + (lane >> 3);
       const int piece = (lane & 7) ^ swz_x(r);
       buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + 8 * (wave + 4 * i) * 128);
     }
-    const auto rh = buf_rsrc(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN), kP * kN * 2);
+    const auto rh = buf_rsrc(wave_uniform(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN)), kP * kN * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * wave + 4 * i + (lane >> 4);
@@ -235,6 +339,21 @@ void ssd_out_mfma_kernel(SsdArgs a) {
     }
     issue_b(0);
     if (n_sb > 1) issue_b(1);
+  }
+  // ---- this wave's slices: C^T operands (lane holds a token, n = 16 kk +
+  // 8 half + 0..7), issued with the staged loads: one round trip for all
+  const int n_sl = a.S / 32;
+  int sls[2] = {wave, 7 - wave};
+  bool act[2];
+  bf16x8_t cq[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    act[q] = sls[q] < n_sl && 32 * sls[q] < clen;  // uniform per wave
+    const int tl = 32 * sls[q] + col;
+    const int64_t tg = row0 + s0 + (tl < clen ? tl : clen - 1);
+    const bf16_t* cp = a.C + (tg * a.G + g) * kN + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) cq[q][kk] = *(const bf16x8_t*)(cp + 16 * kk);
   }
   // ---- l and z of the chunk's tokens: block-wide inclusive scans (sum, max)
   {
@@ -263,23 +382,9 @@ void ssd_out_mfma_kernel(SsdArgs a) {
     s_z[tid] = zv;
   }
 
-  // ---- this wave's slices: C^T operands (lane holds a token, n = 16 kk +
-  // 8 half + 0..7), its l_t and z_t
-  const int n_sl = a.S / 32;
-  int sls[2] = {wave, 7 - wave};
-  bool act[2];
-  bf16x8_t cq[2][8];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    act[q] = sls[q] < n_sl && 32 * sls[q] < clen;  // uniform per wave
-    const int tl = 32 * sls[q] + col;
-    const int64_t tg = row0 + s0 + (tl < clen ? tl : clen - 1);
-    const bf16_t* cp = a.C + (tg * a.G + g) * kN + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) cq[q][kk] = *(const bf16x8_t*)(cp + 16 * kk);
-  }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
+  // this wave's slices' l_t and z_t
   float lt[2];
   int zt[2];
 #pragma unroll
@@ -324,69 +429,14 @@ void ssd_out_mfma_kernel(SsdArgs a) {
     }
     if (j + 2 < n_sb) issue_b(j + 2);
     const uint8_t* bst = s_lds + kOffB + (j % 3) * kBStage;
-    const int sa = 32 * j;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (!act[q] || sls[q] < j) continue;  // uniform per wave
-      const int tl = 32 * sls[q] + col;
-      f32x16_t gt = {};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8_t bo = *(const bf16x8_t*)(bst + mem_off(col, 2 * kk + half));
-        gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, cq[q][kk], gt, 0, 0, 0);
-      }
-      // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = tl.  Keep s <= t with
-      // no zero decay in (s, t], weighted by 2^(l_t - l_s).
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int sr = sa + 8 * jj + 4 * half;
-        const float4 ls = *(const float4*)(s_l + sr);
-        const float lsv[4] = {ls.x, ls.y, ls.z, ls.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sv = sr + i;
-          const bool keep = sv <= tl && zt[q] <= sv;
-          gt[4 * jj + i] = keep ? gt[4 * jj + i] * fast_exp2(lt[q] - lsv[i]) : 0.f;
-        }
-      }
-      // s to 8 consecutive values per lane: swap registers r and r + 4
-      // between the half-waves, then two k-steps of 16 s each
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float xs[4], ys[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gt[8 * kb + i]),
-                                                           __float_as_uint(gt[8 * kb + 4 + i]), false, false);
-          xs[i] = __uint_as_float(sw[0]);
-          ys[i] = __uint_as_float(sw[1]);
-        }
-        const bf16x8_t mop = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]), pack_bf16x2(ys[0], ys[1]),
-                                 pack_bf16x2(ys[2], ys[3])));
-        // X^T operands (p rows, 8 consecutive s) from the X tile: lane (column
-        // j16 + 16 grp16, k-octet half) receives tokens ... + 4 hh + 0..3 of
-        // read hh, addressing token row ... + 4 hh + j16 / 4
-        uint32_t ad[4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int r = sa + 16 * kb + 8 * half + 4 * hh + (j16 >> 2);
-#pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const int pb = 32 * f + 16 * grp16 + 4 * (j16 & 3);
-            ad[2 * f + hh] = lds_addr(s_x + r * 128 + (((pb >> 3) ^ swz_x(r)) << 4) + ((pb & 7) >> 2) * 8);
-          }
-        }
-        uint64_t rd[4];
-        ld_tr4(rd, ad);
-        const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[0], (uint32_t)(rd[0] >> 32),
-                                                                    (uint32_t)rd[1], (uint32_t)(rd[1] >> 32)));
-        const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
-                                                                    (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
-        y[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y[q][0], 0, 0, 0);
-        y[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y[q][1], 0, 0, 0);
-      }
-    }
+    // slices of this wave that see block j (uniform per wave)
+    const bool see0 = act[0] && sls[0] >= j, see1 = act[1] && sls[1] >= j;
+    if (see0 && see1)
+      ssd_intra_block<0, 2>(y, cq, lt, zt, sls, bst, s_x, s_l, 32 * j, col, half, grp16, j16);
+    else if (see0)
+      ssd_intra_block<0, 1>(y, cq, lt, zt, sls, bst, s_x, s_l, 32 * j, col, half, grp16, j16);
+    else if (see1)
+      ssd_intra_block<1, 1>(y, cq, lt, zt, sls, bst, s_x, s_l, 32 * j, col, half, grp16, j16);
   }
 
   // ---- Y^T[p][t]: register r of y[q][f] holds p = 32 f + 8 (r / 4) + 4 half + r % 4
