@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void chunk_states_mfma_kernel(CsArgs a) {
     const int64_t sb = s0 + (int64_t)ib * kSB;
     const int cnt = (int)((s1 - sb) < kSB ? (s1 - sb) : kSB);
     uint8_t* st = s_lds + (q % kStages) * kStage;
-    const auto rx = buf_rsrc(a.X + ((row0 + sb) * a.H + h) * kP,
+    const auto rx = buf_rsrc(wave_uniform(a.X + ((row0 + sb) * a.H + h) * kP),
                              live ? (uint32_t)((cnt - 1) * a.H * kP + kP) * 2 : 0u);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void chunk_states_mfma_kernel(CsArgs a) {
       const int piece = (lane & 7) ^ swz_x(r);
       buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, st + (16 * wave + 8 * i) * 128);
     }
-    const auto rb = buf_rsrc(a.B + ((row0 + sb) * a.G + g) * kN,
+    const auto rb = buf_rsrc(wave_uniform(a.B + ((row0 + sb) * a.G + g) * kN),
                              live ? (uint32_t)((cnt - 1) * a.G * kN + kN) * 2 : 0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -172,10 +172,14 @@ __global__ __launch_bounds__(kThreads) void chunk_states_mfma_kernel(CsArgs a) {
     }
   };
 
-  // decay of this thread's token in the group that holds sub-block ib
+  // decay of this thread's token in the group that holds sub-block ib;
+  // without a branch (threads past the chunk end re-read its last token),
+  // so that no address is formed in divergent code, where the compiler
+  // would take it for a per-lane value
   auto load_decay = [&](int ib) {
     const int64_t t = s0 + (int64_t)(ib / 4) * kGroup + tid;
-    return t < s1 ? a.A[(row0 + t) * a.H + h] : 1.f;
+    const float v = a.A[(row0 + (t < s1 ? t : s1 - 1)) * a.H + h];
+    return t < s1 ? v : 1.f;
   };
 
   float carry = 1.f;  // product of a_k over the tokens of later groups
