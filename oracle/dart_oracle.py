@@ -66,6 +66,7 @@ __all__ = [
     "sma_decode",
     "cache_ratio",
     "sma_head_backward",
+    "sma_token_backward",
     "sma_backward",
     "gated_residual_backward",
     "chunk_states_head_backward",
@@ -390,6 +391,36 @@ def sma_head_backward(Q, C, E, dH, S: int, dR, lse=None):
         ddH[:i] += np.einsum("tc,tn,tp->cnp", p, C[s0:s1], g, optimize=True)
         ddH[:i] += np.einsum("tc,tn,tp->cnp", dl, Q[s0:s1], E[s0:s1], optimize=True) * scale
     return dQ, dC, dE, ddH
+
+
+def sma_token_backward(q, c, e, dH_visible, dR_t):
+    """Gradients of one token's SMA readout R_t  [§3 Eq. 8-10] for a loss
+    gradient dR_t (P,) on R_t: q, c (N,), e (P,), dH_visible (n, N, P)
+    ->  dq (N,), dc (N,), de (P,), d_dH (n, N, P) (this token's share of
+    the gradient of every visible chunk memory).
+
+    Per token, with V_c = C_t dH_c, K_c = dH_c E_t, l_c = Q_t K_c / sqrt(N)
+    and g = softmax(l):  dV_c = g_c dR_t;  dl_c = g_c (dR_t . V_c - dR_t . R_t)
+    (the softmax Jacobian, R_t = sum_c g_c V_c);  dq = sum_c dl_c K_c / sqrt(N),
+    de = sum_c dl_c dH_c^T q / sqrt(N),  dc = sum_c dH_c dV_c,
+    d_dH_c = c^T dV_c + dl_c q^T e / sqrt(N).  An empty set gives zeros."""
+    q, c, e, dH, g = _f64(q), _f64(c), _f64(e), _f64(dH_visible), _f64(dR_t)
+    n, N, P = dH.shape
+    if n == 0:
+        return np.zeros(N), np.zeros(N), np.zeros(P), np.zeros((0, N, P))
+    scale = 1.0 / math.sqrt(N)
+    V = np.einsum("n,cnp->cp", c, dH)          # C_t dH_c
+    K = np.einsum("cnp,p->cn", dH, e)          # dH_c E_t
+    logits = (K @ q) * scale
+    w = np.exp(logits - logits.max())
+    w /= w.sum()                               # softmax weights g_c
+    R = w @ V
+    dl = w * (V @ g - R @ g)
+    dq = (dl @ K) * scale
+    de = np.einsum("c,cnp,n->p", dl, dH, q) * scale
+    dc = np.einsum("c,cnp,p->n", w, dH, g)
+    d_dH = w[:, None, None] * np.outer(c, g)[None] + dl[:, None, None] * np.outer(q, e)[None] * scale
+    return dq, dc, de, d_dH
 
 
 def sma_backward(Q, C, E, dH, S: int, dR, lse=None):

@@ -227,3 +227,49 @@ def test_chunk_states_bwd_mfma(cfg):
     ref = dict(X=rX, B=rB, A=rA)
     compare(out[dart.DART_PATH_GENERAL], ref, TOL_SAME_INPUT["bf16"], "cs-bwd general")
     compare(out[dart.DART_PATH_AUTO], ref, TOL["bf16"], "cs-bwd mfma")
+
+
+def test_bwd_full_size_sampled():
+    """Config 2 in the launch the benchmark times (its inputs: the seed-0
+    draw, the GPU's chunk states, the forward's R and lse, the seed-3 loss
+    gradient): sampled tokens' dQ, dC, dE and dgate, and the whole d_dH of
+    chunk M - 2 (whose later tokens are the last chunk's), for sampled heads,
+    against the oracle's per-token backward on the same bf16 inputs."""
+    cfg = dict(synth.CONFIGS[2])
+    say("sma_bwd full size", cfg["name"])
+    b, H, G, L, S = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["seqlen"], cfg["chunk"]
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)
+    _, R, lse = dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S, want_R=True, want_lse=True)
+    dout = synth.draw_grad_torch((b, L, H, cfg["d_head"]), "bf16", seed=3)
+    dQ, dC, dE, ddH, dg = dart.dart_sma_bwd(d["Q"], d["C"], d["E"], dH, d["gate"], R, lse, dout, S)
+    torch.cuda.synchronize()
+    for t in (dQ, dC, dE, ddH, dg):
+        assert not torch.isnan(t).any()
+    M = dart.num_chunks(L, S)
+    hpg = H // G
+    rng = np.random.default_rng(7)
+    for bi, h in [(0, 0), (1, H - 1), (int(rng.integers(b)), int(rng.integers(H)))]:
+        g = h // hpg
+        Qh, Ch, Eh = host(d["Q"][bi, :, g]), host(d["C"][bi, :, g]), host(d["E"][bi, :, g])
+        gh, oh = host(d["gate"][bi, :, h]), host(dout[bi, :, h])
+        mem = to_oracle_mem(host(dH[bi, h]))               # (M, N, P), the GPU's own chunk memories
+        toks = sorted(set([S, S + 1, 2 * S - 1, L - 1] + [int(x) for x in rng.integers(S, L, 10)]))
+        ref = {k: [] for k in ("Q", "C", "E", "gate")}
+        for t in toks:
+            i = t // S
+            Rt, _ = O.sma_token(Qh[t], Ch[t], Eh[t], mem[:i])
+            dq, dc, de, _ = O.sma_token_backward(Qh[t], Ch[t], Eh[t], mem[:i], gh[t] * oh[t])
+            ref["Q"].append(dq)
+            ref["C"].append(dc)
+            ref["E"].append(de)
+            ref["gate"].append(oh[t] * Rt)
+        got = dict(Q=host(dQ[bi, toks, g]), C=host(dC[bi, toks, g]), E=host(dE[bi, toks, g]),
+                   gate=host(dg[bi, toks, h]))
+        compare(got, {k: np.array(v) for k, v in ref.items()}, TOL["bf16"], f"tokens of (b={bi}, h={h})")
+        # d_dH of chunk M - 2: the contributions of the last chunk's tokens
+        acc = np.zeros(mem.shape[1:])
+        for t in range((M - 1) * S, L):
+            _, _, _, dd = O.sma_token_backward(Qh[t], Ch[t], Eh[t], mem[: M - 1], gh[t] * oh[t])
+            acc += dd[M - 2]
+        compare(dict(dH=host(ddH[bi, h, M - 2])), dict(dH=acc.T), TOL["bf16"], f"d_dH[{M - 2}] of (b={bi}, h={h})")

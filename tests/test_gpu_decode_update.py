@@ -90,3 +90,45 @@ def test_streamed_decode_equals_forward():
         e_l = err(lse[0], lsef[0, :, t])
         say(f"  token {t}: n_chunks {nb}  R {e_r:.2e}  lse {e_l:.2e}")
         assert e_r <= 1e-3 and e_l <= 1e-3
+
+
+def test_update_decode_workload_shape():
+    """The decode workload's shape (64 rows, 24 heads, N = 128, P = 64,
+    S = 256) in the launch the benchmark times: one token per row in the
+    middle of chunk 100 against a random float32 in-progress state, then a
+    token that closes the chunk (its memory goes to cache row 100 and the
+    state restarts from zero).  Every entry against the oracle's update."""
+    cfg = dict(synth.CONFIGS[4])
+    b, H, G, N, P, S = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["d_state"], cfg["d_head"], cfg["chunk"]
+    say("decode update, decode workload shape", cfg["name"])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    x = torch.randn((b, H, P), generator=gen, device="cuda").to(torch.bfloat16)
+    Bt = (torch.randn((b, G, N), generator=gen, device="cuda") / N ** 0.5).to(torch.bfloat16)
+    a = torch.rand((b, H), generator=gen, device="cuda") * 0.5 + 0.5
+    state0 = torch.randn((b, H, P, N), generator=gen, device="cuda")
+    cache = torch.zeros((b, H, 256, P, N), device="cuda", dtype=torch.bfloat16)
+    nch = torch.full((b,), -1, dtype=torch.int32, device="cuda")
+    hpg = H // G
+    for pos_in_chunk, closes in [(7, False), (S - 1, True)]:
+        state = state0.clone()
+        pos = torch.full((b,), 256 * 100 + pos_in_chunk, dtype=torch.int32, device="cuda")
+        dart.dart_decode_state_update(x, Bt, a, state, pos, cache, S, n_chunks=nch)
+        torch.cuda.synchronize()
+        xs, bs, av, s0 = host(x), host(Bt), host(a), host(state0)
+        # oracle, all (row, head) at once: a_t H + B_t^T x_t, stored (P, N)
+        new = av[:, :, None, None] * s0 + np.einsum("bhp,bhn->bhpn", xs, bs[:, np.arange(H) // hpg])
+        for bi, h in [(0, 0), (b - 1, H - 1), (17, 5)]:
+            ref, closed = O.decode_state_update(s0[bi, h].T, xs[bi, h], bs[bi, h // hpg], av[bi, h],
+                                                256 * 100 + pos_in_chunk, S)
+            np.testing.assert_allclose(new[bi, h], (closed if closes else ref).T, rtol=1e-12, atol=1e-12)
+        if closes:
+            e_c = err(host(cache[:, :, 100]), new)
+            e_s = float(np.abs(host(state)).max())
+            say(f"  closing token: cache row {e_c:.2e}, state after {e_s:.1e}")
+            assert e_c <= TOL["bf16"] and e_s == 0.0
+            assert (host(nch) == 101).all()
+        else:
+            e_s = err(host(state), new)
+            say(f"  mid-chunk token: state {e_s:.2e}")
+            assert e_s <= TOL["f32"]

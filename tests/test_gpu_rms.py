@@ -224,3 +224,47 @@ def test_update_rms_writes_inverse_rms(dt, N, P, S):
     say(f"  r of closed chunks {e:.2e}")
     assert e <= 1e-5
     assert np.all(hr[:, :, nc:] == -1.0)           # open chunk: nothing written
+
+
+def test_fwd_rms_full_size_sampled():
+    """Config 2 in the launch the benchmark times (dart_chunk_states_rms,
+    then dart_sma_fwd_rms with eps = 1e-6 and no norm weights; out only),
+    then again with R and lse: out must not change, and sampled tokens of
+    sampled heads must match the oracle on the GPU's own chunk memories."""
+    cfg = dict(synth.CONFIGS[2])
+    say("sma_fwd_rms full size", cfg["name"])
+    b, H, G, L, S = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["seqlen"], cfg["chunk"]
+    eps = 1e-6
+    d = synth.draw_fwd_torch(**cfg, seed=0)
+    dH, _, s = dart.dart_chunk_states_rms(d["X"], d["B"], d["A"], S, eps, want_r=False)
+    out_bench = torch.empty_like(d["Y"])
+    dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, s, d["Y"], d["gate"], S, eps, out=out_bench)
+    out = torch.empty_like(d["Y"])
+    R = torch.empty((b, L, H, cfg["d_head"]), device="cuda")
+    lse = torch.empty((b, H, L), device="cuda")
+    dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, s, d["Y"], d["gate"], S, eps, out=out, R=R, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out_bench, out)
+    assert not torch.isnan(out).any() and not torch.isnan(R).any() and not torch.isnan(lse).any()
+    rng = np.random.default_rng(31)
+    hpg = H // G
+    for bi, h in [(0, 0), (1, H - 1), (int(rng.integers(b)), int(rng.integers(H)))]:
+        g = h // hpg
+        mem = to_oracle_mem(host(dH[bi, h]))
+        toks = sorted(set([0, S - 1, S, L - 1] + [int(x) for x in rng.integers(0, L, 12)]))
+        Qh, Ch, Eh = host(d["Q"][bi, :, g]), host(d["C"][bi, :, g]), host(d["E"][bi, :, g])
+        Yh, gh = host(d["Y"][bi, :, h]), host(d["gate"][bi, :, h])
+        rr, ll, oo = [], [], []
+        for t in toks:
+            r, l = O.sma_token_rms(Qh[t], Ch[t], Eh[t], mem[: t // S], eps)
+            rr.append(r)
+            ll.append(l)
+            oo.append(O.gated_residual(Yh[t], gh[t], r))
+        e_r = err(host(R[bi, toks, h]), np.array(rr))
+        e_o = err(host(out[bi, toks, h]), np.array(oo))
+        got_l, ref_l = host(lse[bi, h, toks]), np.array(ll)
+        assert np.array_equal(np.isinf(got_l), np.isinf(ref_l))
+        fin = np.isfinite(ref_l)
+        e_l = err(got_l[fin], ref_l[fin])
+        say(f"  (b={bi}, h={h}): out {e_o:.2e}  R {e_r:.2e}  lse {e_l:.2e}")
+        assert e_o <= TOL["bf16"] and e_r <= TOL["bf16"] and e_l <= TOL["bf16"], (bi, h, e_o, e_r, e_l)

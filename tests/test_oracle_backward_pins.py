@@ -105,3 +105,50 @@ def test_chunk_states_backward_unit_decay_and_first_token():
     a = np.exp(-rng.uniform(0.1, 1.0, L))
     _, _, da = O.chunk_states_head_backward(X, B, a, S, G)
     assert da[0] == 0 and da[4] == 0 and da[8] == 0
+
+
+def test_token_backward_matches_finite_differences():
+    """The per-token backward against central differences of dR_t . R_t,
+    with R_t from the oracle's per-token forward, in every input it takes
+    (q, c, e and each visible chunk memory)."""
+    rng = np.random.default_rng(17)
+    N, P, n = 5, 3, 4
+    q, c, e = rng.standard_normal(N), rng.standard_normal(N), rng.standard_normal(P)
+    dH = rng.standard_normal((n, N, P))
+    g = rng.standard_normal(P)
+    dq, dc, de, ddH = O.sma_token_backward(q, c, e, dH, g)
+    args = [q, c, e, dH]
+    got = [dq, dc, de, ddH]
+    eps = 1e-6
+    for x, ana in zip(args, got):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            up = float(g @ O.sma_token(*args)[0])
+            x[idx] = keep - eps
+            dn = float(g @ O.sma_token(*args)[0])
+            x[idx] = keep
+            num[idx] = (up - dn) / (2 * eps)
+        np.testing.assert_allclose(ana, num, rtol=1e-6, atol=1e-8)
+
+
+def test_token_backward_sums_to_head_backward():
+    """Summing the per-token backward over a head's tokens gives the head
+    backward (its pinned counterpart): dQ, dC, dE row by row, d_dH summed."""
+    rng = np.random.default_rng(18)
+    L, S, N, P = 23, 5, 4, 3
+    Q, C, E = rng.standard_normal((L, N)), rng.standard_normal((L, N)), rng.standard_normal((L, P))
+    M = O.num_chunks(L, S)
+    dH = rng.standard_normal((M, N, P))
+    dR = rng.standard_normal((L, P))
+    hq, hc, he, hdd = O.sma_head_backward(Q, C, E, dH, S, dR)
+    tdd = np.zeros_like(hdd)
+    for t in range(L):
+        i = t // S
+        dq, dc, de, dd = O.sma_token_backward(Q[t], C[t], E[t], dH[:i], dR[t])
+        np.testing.assert_allclose(dq, hq[t], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dc, hc[t], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(de, he[t], rtol=1e-10, atol=1e-12)
+        tdd[:i] += dd
+    np.testing.assert_allclose(tdd, hdd, rtol=1e-10, atol=1e-12)
