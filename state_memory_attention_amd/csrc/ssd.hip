@@ -24,7 +24,7 @@ namespace dart {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr unsigned kWaitVm2 = 0x0f72;  // s_waitcnt vmcnt(2)
+constexpr unsigned kWaitVm1 = 0x0f71;  // s_waitcnt vmcnt(1)
 
 // ---------------------------------------------------------------------------
 // Full decay of every chunk, A_{a_c:b_c}: one wave per (b, h, c).
@@ -192,27 +192,19 @@ __device__ __forceinline__ void ld_lds4(float4 (&o)[4], uint32_t addr) {
 }
 
 // Intra-chunk terms of block j of s (32 tokens from sa = 32 j, staged at bst)
-// for the NQ slices Q0 .. Q0 + NQ - 1 of this wave, all of which see it:
-// one straight-line body, so that the B and X operands and l_s are read
-// once for all of them and their matrix-core chains interleave.  Scores
-// G^T = B_s C^T (the slice's C^T operands cq), weighted by 2^(l_t - l_s) for
-// s <= t with no zero decay in (s, t], then Y^T += X_s^T G^T  [App. A Eq. 21].
-template <int Q0, int NQ>
-__device__ __forceinline__ void ssd_intra_block(f32x16_t (&y)[2][2], const bf16x8_t (&cq)[2][8], const float (&lt)[2],
-                                                const int (&zt)[2], const int (&sls)[2], const uint8_t* bst,
-                                                const uint8_t* s_x, const float* s_l, int sa, int col, int half,
-                                                int grp16, int j16) {
-  bf16x8_t bo[8];
+// for this wave's slice (the lane's token tl, its l_t and z_t): scores
+// G^T = B_s C^T (C^T operands cq), weighted by 2^(l_t - l_s) for s <= t with
+// no zero decay in (s, t], then Y^T += X_s^T G^T  [App. A Eq. 21].
+__device__ __forceinline__ void ssd_intra_block(f32x16_t (&y)[2], const bf16x8_t (&cq)[8], float lt, int zt, int tl,
+                                                const uint8_t* bst, const uint8_t* s_x, const float* s_l, int sa,
+                                                int col, int half, int grp16, int j16) {
+  f32x16_t gt = {};
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) bo[kk] = *(const bf16x8_t*)(bst + mem_off(col, 2 * kk + half));
-  f32x16_t gt[NQ];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) gt[i] = f32x16_t{};
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) gt[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[kk], cq[Q0 + i][kk], gt[i], 0, 0, 0);
-  // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = the lane's token
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8_t bo = *(const bf16x8_t*)(bst + mem_off(col, 2 * kk + half));
+    gt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, cq[kk], gt, 0, 0, 0);
+  }
+  // gt[r]: s = sa + 8 (r / 4) + 4 half + r % 4, t = tl
   float4 lsq[4];
   ld_lds4(lsq, lds_addr(s_l + sa + 4 * half));
 #pragma unroll
@@ -220,19 +212,27 @@ __device__ __forceinline__ void ssd_intra_block(f32x16_t (&y)[2][2], const bf16x
     const int sr = sa + 8 * jj + 4 * half;
     const float lsv[4] = {lsq[jj].x, lsq[jj].y, lsq[jj].z, lsq[jj].w};
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int q = Q0 + i;
-      const int tl = 32 * sls[q] + col;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int sv = sr + e;
-        const bool keep = sv <= tl && zt[q] <= sv;
-        gt[i][4 * jj + e] = keep ? gt[i][4 * jj + e] * fast_exp2(lt[q] - lsv[e]) : 0.f;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int sv = sr + e;
+      const bool keep = sv <= tl && zt <= sv;
+      gt[4 * jj + e] = keep ? gt[4 * jj + e] * fast_exp2(lt - lsv[e]) : 0.f;
     }
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    // s to 8 consecutive values per lane: swap registers r and r + 4
+    // between the half-waves, then two k-steps of 16 s each
+    float xs[4], ys[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gt[8 * kb + e]),
+                                                       __float_as_uint(gt[8 * kb + 4 + e]), false, false);
+      xs[e] = __uint_as_float(sw[0]);
+      ys[e] = __uint_as_float(sw[1]);
+    }
+    const bf16x8_t mop = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]), pack_bf16x2(ys[0], ys[1]),
+                             pack_bf16x2(ys[2], ys[3])));
     // X^T operands (p rows, 8 consecutive s) from the X tile: lane (column
     // j16 + 16 grp16, k-octet half) receives tokens ... + 4 hh + 0..3 of read
     // hh, addressing token row ... + 4 hh + j16 / 4
@@ -252,28 +252,19 @@ __device__ __forceinline__ void ssd_intra_block(f32x16_t (&y)[2][2], const bf16x
                                                                 (uint32_t)rd[1], (uint32_t)(rd[1] >> 32)));
     const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)rd[2], (uint32_t)(rd[2] >> 32),
                                                                 (uint32_t)rd[3], (uint32_t)(rd[3] >> 32)));
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      // s to 8 consecutive values per lane: swap registers r and r + 4
-      // between the half-waves, then two k-steps of 16 s each
-      float xs[4], ys[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gt[i][8 * kb + e]),
-                                                         __float_as_uint(gt[i][8 * kb + 4 + e]), false, false);
-        xs[e] = __uint_as_float(sw[0]);
-        ys[e] = __uint_as_float(sw[1]);
-      }
-      const bf16x8_t mop = __builtin_bit_cast(
-          bf16x8_t, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]), pack_bf16x2(ys[0], ys[1]),
-                               pack_bf16x2(ys[2], ys[3])));
-      y[Q0 + i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y[Q0 + i][0], 0, 0, 0);
-      y[Q0 + i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y[Q0 + i][1], 0, 0, 0);
-    }
+    y[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, mop, y[0], 0, 0, 0);
+    y[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, mop, y[1], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Output kernel: eight waves, one 32-token slice each.  Waves w and w + 4
+// share a SIMD and own slices w and 7 - w, so the causal work on every SIMD
+// is the same and the two pairs a SIMD has in one block of s run in two
+// waves, which overlap.
+constexpr int kWavesOut = 8;
+constexpr int kThreadsOut = 64 * kWavesOut;
+
+__global__ __launch_bounds__(kThreadsOut) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void ssd_out_mfma_kernel(SsdArgs a) {
   // One LDS object (so that the compiler adds no waits of its own for the
   // staged loads): X tile (128-byte rows), Hin_c^T, the B ring, l and z.
@@ -301,61 +292,61 @@ void ssd_out_mfma_kernel(SsdArgs a) {
   const int clen = (int)((s0 + a.S < a.L) ? a.S : a.L - s0);
   const int n_sb = (clen + 31) / 32;  // blocks of 32 tokens holding data
   const int64_t row0 = (int64_t)b * a.L;
-  // this thread's token decay, loaded before the staged loads so that waiting
-  // for it leaves them in flight; without a branch (threads past the chunk
-  // end re-read its last token), so that the addresses below are not formed
-  // in divergent code, where the compiler would keep the buffer resources
-  // in vector registers and loop over lanes for every load
+  // this thread's token decay (threads past the chunk, and the upper half of
+  // the block, hold none), loaded before the staged loads so that waiting
+  // for it leaves them in flight; without a branch (those threads re-read
+  // the chunk's last token), so that the addresses below are not formed in
+  // divergent code, where the compiler would keep the buffer resources in
+  // vector registers and loop over lanes for every load
   const float a_raw = a.A[(row0 + s0 + (tid < clen ? tid : clen - 1)) * a.H + h];
   const float av = tid < clen ? a_raw : 1.f;
 
-  // ---- staged loads.  X tile: wave w loads row groups w, w+4, ... (8 rows
-  // of 128 B each); Hin_c^T: rows 16w .. 16w+15; B block j: rows 8w .. 8w+7
-  // of its stage.  Rows past the chunk end read as zeros.
+  // ---- staged loads.  X tile: wave w loads row groups w, w+8, ... (8 rows
+  // of 128 B each); Hin_c^T: rows 8w .. 8w+7; B block j: rows 4w .. 4w+3 of
+  // its stage (one load per wave).  Rows past the chunk end read as zeros.
   const auto rbb = buf_rsrc(wave_uniform(a.B + ((row0 + s0) * a.G + g) * kN), (uint32_t)((clen - 1) * a.G * kN + kN) * 2);
   auto issue_b = [&](int j) {
     uint8_t* st = s_lds + kOffB + (j % 3) * kBStage;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * wave + 4 * i + (lane >> 4);  // row within the block
-      const int rr = 32 * j + r;                     // row within the chunk
-      buf_dma16(rbb, (uint32_t)(rr * a.G * kN * 2 + (((lane & 15) ^ (r & 15)) << 4)), st + (8 * wave + 4 * i) * 256);
-    }
+    const int r = 4 * wave + (lane >> 4);  // row within the block
+    const int rr = 32 * j + r;             // row within the chunk
+    buf_dma16(rbb, (uint32_t)(rr * a.G * kN * 2 + (((lane & 15) ^ (r & 15)) << 4)), st + 4 * wave * 256);
   };
   {
     const auto rx = buf_rsrc(wave_uniform(a.X + ((row0 + s0) * a.H + h) * kP), (uint32_t)((clen - 1) * a.H * kP + kP) * 2);
+    // every wave issues the same loads whatever the chunk length (groups
+    // past it read zeros into rows nothing reads), so that the compiler's
+    // wait for the decay load counts them all and leaves them in flight
 #pragma unroll
-    for (int i = 0; i < kMaxS / 32; ++i) {
-      if (i >= a.S / 32) break;
-      const int r = 8 * (wave + 4 * i) + (lane >> 3);
+    for (int i = 0; i < kMaxS / (8 * kWavesOut); ++i) {
+      const int rb = 8 * (wave + kWavesOut * i);  // first row of the group
+      const int r = rb + (lane >> 3);
       const int piece = (lane & 7) ^ swz_x(r);
-      buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + 8 * (wave + 4 * i) * 128);
+      buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + rb * 128);
     }
     const auto rh = buf_rsrc(wave_uniform(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN)), kP * kN * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wave + 4 * i + (lane >> 4);
-      buf_dma16(rh, (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4)), s_h + (16 * wave + 4 * i) * 256);
+    for (int i = 0; i < 2; ++i) {
+      const int row = 8 * wave + 4 * i + (lane >> 4);
+      buf_dma16(rh, (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4)), s_h + (8 * wave + 4 * i) * 256);
     }
     issue_b(0);
-    if (n_sb > 1) issue_b(1);
+    issue_b(1);
   }
-  // ---- this wave's slices: C^T operands (lane holds a token, n = 16 kk +
+  // ---- this wave's slice: C^T operands (lane holds a token, n = 16 kk +
   // 8 half + 0..7), issued with the staged loads: one round trip for all
   const int n_sl = a.S / 32;
-  int sls[2] = {wave, 7 - wave};
-  bool act[2];
-  bf16x8_t cq[2][8];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    act[q] = sls[q] < n_sl && 32 * sls[q] < clen;  // uniform per wave
-    const int tl = 32 * sls[q] + col;
+  const int sl = wave < 4 ? wave : 11 - wave;
+  const bool act = sl < n_sl && 32 * sl < clen;  // uniform per wave
+  const int tl = 32 * sl + col;
+  bf16x8_t cq[8];
+  {
     const int64_t tg = row0 + s0 + (tl < clen ? tl : clen - 1);
     const bf16_t* cp = a.C + (tg * a.G + g) * kN + 8 * half;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) cq[q][kk] = *(const bf16x8_t*)(cp + 16 * kk);
+    for (int kk = 0; kk < 8; ++kk) cq[kk] = *(const bf16x8_t*)(cp + 16 * kk);
   }
-  // ---- l and z of the chunk's tokens: block-wide inclusive scans (sum, max)
+  // ---- l and z of the chunk's tokens (threads 0 .. kMaxS-1): block-wide
+  // inclusive scans (sum, max)
   {
     float lv = av > 0.f ? fast_log2(av) : 0.f;
     int zv = (tid < clen && av == 0.f) ? tid : -1;
@@ -368,89 +359,71 @@ void ssd_out_mfma_kernel(SsdArgs a) {
         zv = zu > zv ? zu : zv;
       }
     }
-    if (lane == 63) {
+    if (lane == 63 && wave < kMaxS / 64) {
       s_tl[wave] = lv;
       s_tz[wave] = zv;
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
-    for (int w2 = 0; w2 < wave; ++w2) {
-      lv += s_tl[w2];
-      zv = s_tz[w2] > zv ? s_tz[w2] : zv;
+    if (wave < kMaxS / 64) {
+      for (int w2 = 0; w2 < wave; ++w2) {
+        lv += s_tl[w2];
+        zv = s_tz[w2] > zv ? s_tz[w2] : zv;
+      }
+      s_l[tid] = lv;
+      s_z[tid] = zv;
     }
-    s_l[tid] = lv;
-    s_z[tid] = zv;
   }
-
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
-  // this wave's slices' l_t and z_t
-  float lt[2];
-  int zt[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int tl = 32 * sls[q] + col;
-    lt[q] = s_l[tl < kMaxS ? tl : kMaxS - 1];
-    zt[q] = s_z[tl < kMaxS ? tl : kMaxS - 1];
-  }
+  // this wave's slice's l_t and z_t
+  const float lt = s_l[tl < kMaxS ? tl : kMaxS - 1];
+  const int zt = s_z[tl < kMaxS ? tl : kMaxS - 1];
 
   // ---- inter-chunk readout, then its decay A_{a_c:t}  [Eq. 22]
-  f32x16_t y[2][2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    y[q][0] = f32x16_t{};
-    y[q][1] = f32x16_t{};
-    if (!act[q]) continue;
+  f32x16_t y[2] = {f32x16_t{}, f32x16_t{}};
+  if (act) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8_t h0 = *(const bf16x8_t*)(s_h + mem_off(col, 2 * kk + half));
       const bf16x8_t h1 = *(const bf16x8_t*)(s_h + mem_off(32 + col, 2 * kk + half));
-      y[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, cq[q][kk], y[q][0], 0, 0, 0);
-      y[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, cq[q][kk], y[q][1], 0, 0, 0);
+      y[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, cq[kk], y[0], 0, 0, 0);
+      y[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, cq[kk], y[1], 0, 0, 0);
     }
-    const float din = zt[q] < 0 ? fast_exp2(lt[q]) : 0.f;
+    const float din = zt < 0 ? fast_exp2(lt) : 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      y[q][0][r] *= din;
-      y[q][1][r] *= din;
+      y[0][r] *= din;
+      y[1][r] *= din;
     }
   }
 
   // ---- intra-chunk terms, all waves on block j of s together  [Eq. 21]
   for (int j = 0; j < n_sb; ++j) {
     if (j > 0) {
-      // block j has landed (block j + 1 may still be in flight); every wave
-      // is done with block j - 1, whose stage takes block j + 2
+      // block j has landed (block j + 1 may still be in flight, one load per
+      // wave); every wave is done with block j - 1, whose stage takes block
+      // j + 2
       if (j + 1 < n_sb && j + 1 >= 2)
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+        __builtin_amdgcn_s_waitcnt(kWaitVm1);
       else
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __builtin_amdgcn_s_barrier();
     }
     if (j + 2 < n_sb) issue_b(j + 2);
-    const uint8_t* bst = s_lds + kOffB + (j % 3) * kBStage;
-    // slices of this wave that see block j (uniform per wave)
-    const bool see0 = act[0] && sls[0] >= j, see1 = act[1] && sls[1] >= j;
-    if (see0 && see1)
-      ssd_intra_block<0, 2>(y, cq, lt, zt, sls, bst, s_x, s_l, 32 * j, col, half, grp16, j16);
-    else if (see0)
-      ssd_intra_block<0, 1>(y, cq, lt, zt, sls, bst, s_x, s_l, 32 * j, col, half, grp16, j16);
-    else if (see1)
-      ssd_intra_block<1, 1>(y, cq, lt, zt, sls, bst, s_x, s_l, 32 * j, col, half, grp16, j16);
+    if (act && sl >= j)  // uniform per wave
+      ssd_intra_block(y, cq, lt, zt, tl, s_lds + kOffB + (j % 3) * kBStage, s_x, s_l, 32 * j, col, half, grp16, j16);
   }
 
-  // ---- Y^T[p][t]: register r of y[q][f] holds p = 32 f + 8 (r / 4) + 4 half + r % 4
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int tl = 32 * sls[q] + col;
-    if (!act[q] || tl >= clen) continue;
+  // ---- Y^T[p][t]: register r of y[f] holds p = 32 f + 8 (r / 4) + 4 half + r % 4
+  if (act && tl < clen) {
     bf16_t* yp = a.Y + ((row0 + s0 + tl) * a.H + h) * kP + 4 * half;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      *(uint2*)(yp + 8 * jj) = make_uint2(pack_bf16x2(y[q][0][4 * jj], y[q][0][4 * jj + 1]),
-                                          pack_bf16x2(y[q][0][4 * jj + 2], y[q][0][4 * jj + 3]));
-      *(uint2*)(yp + 32 + 8 * jj) = make_uint2(pack_bf16x2(y[q][1][4 * jj], y[q][1][4 * jj + 1]),
-                                               pack_bf16x2(y[q][1][4 * jj + 2], y[q][1][4 * jj + 3]));
+      *(uint2*)(yp + 8 * jj) = make_uint2(pack_bf16x2(y[0][4 * jj], y[0][4 * jj + 1]),
+                                          pack_bf16x2(y[0][4 * jj + 2], y[0][4 * jj + 3]));
+      *(uint2*)(yp + 32 + 8 * jj) = make_uint2(pack_bf16x2(y[1][4 * jj], y[1][4 * jj + 1]),
+                                               pack_bf16x2(y[1][4 * jj + 2], y[1][4 * jj + 3]));
     }
   }
 }
@@ -502,7 +475,7 @@ hipError_t launch_ssd_fwd(const Shape& s, bool bf16, bool mfma, const void* X, c
     a.hpg = (int)(s.H / s.G);
     a.S = (int)s.S;
     a.M = (int)s.M;
-    ssd_out_mfma_kernel<<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kThreads), 0, st>>>(a);
+    ssd_out_mfma_kernel<<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kThreadsOut), 0, st>>>(a);
     return hipGetLastError();
   }
   const int64_t gph = (s.L + 3) / 4;
