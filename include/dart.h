@@ -63,8 +63,10 @@
  *
  * Supported shapes: dtype float32 or bfloat16 (all arithmetic in float32),
  * 1 <= N <= 256, 1 <= P <= 256, any S >= 1, any L (L % S != 0 allowed).
- * bfloat16 with N = 128 and P = 64 runs the MFMA kernels; every other case
- * runs the general kernels.  b = 0 or L = 0 is a valid empty call.
+ * bfloat16 with N = 128 and P = 64 runs the MFMA kernels (for at most 4096
+ * heads and groups and fewer than 2^28 tokens per sequence, bounds that keep
+ * their 32-bit buffer offsets in range); every other case runs the general
+ * kernels.  b = 0 or L = 0 is a valid empty call.
  */
 #ifndef DART_H_
 #define DART_H_

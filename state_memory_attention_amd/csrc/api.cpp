@@ -129,8 +129,16 @@ size_t bwd_workspace(const dart::Shape& s) {
   return g > m ? g : m;
 }
 
+// The MFMA kernels address a token tile (up to 256 rows of nheads * P or
+// ngroups * N elements) and a head's per-chunk weight rows (8 seqlen bytes)
+// with 32-bit buffer offsets; these bounds keep every such offset below 2^31.
+// Larger shapes run the general kernels, which index in 64 bits.
+constexpr int64_t kMfmaMaxHeads = 4096;
+constexpr int64_t kMfmaMaxSeq = (int64_t)1 << 28;
+
 bool use_mfma(int dtype, const dart_dims_t* d) {
-  return t_path == DART_PATH_AUTO && dtype == DART_BF16 && d->d_state == 128 && d->d_head == 64;
+  return t_path == DART_PATH_AUTO && dtype == DART_BF16 && d->d_state == 128 && d->d_head == 64 &&
+         d->nheads <= kMfmaMaxHeads && d->ngroups <= kMfmaMaxHeads && d->seqlen < kMfmaMaxSeq;
 }
 
 int hip_status(hipError_t e, const char* what) {
