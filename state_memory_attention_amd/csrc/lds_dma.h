@@ -1,4 +1,12 @@
 // Device helpers shared by the MFMA kernels: direct global->LDS loads, explicit
+// s_waitcnt immediates and the swizzled layout of a staged chunk memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dart {
+
 // Cache-policy bit of a buffer access for data streamed once: non-temporal,
 // so that the stream does not evict data that other blocks re-read from L2.
 constexpr int kNonTemporal = 2;
@@ -14,14 +22,6 @@ __device__ __forceinline__ T* wave_uniform(T* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (T*)(((uint64_t)hi << 32) | lo);
 }
-
-// s_waitcnt immediates and the swizzled layout of a staged chunk memory.
-#pragma once
-
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-namespace dart {
 
 // One direct global->LDS load: every lane fetches 16 bytes from `src`, and
 // lane l's bytes land at lds + 16 l (the LDS address is wave-uniform).
