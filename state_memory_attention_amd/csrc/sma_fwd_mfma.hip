@@ -95,8 +95,8 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   // the per-channel gate tile; slot s goes to ring buffer s % kRing.  Every
   // slot costs every wave exactly 4 direct-to-LDS loads, so the waits below
   // only count slots; the first three slots are always issued (zero-length
-  // loads stand in for missing ones), the Y tile goes to its own area with
-  // them.  A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4
+  // loads stand in for missing ones), the Y tile goes to its own area once
+  // the prologue is done with it.  A chunk load of wave w writes rows 16w .. 16w+15 of dH_j^T (4
   // loads of 4 rows); a token-tile load of wave w writes the wave's own token
   // rows 32w .. 32w+31 (4 loads of 8 rows of 128 B).  One such load writes
   // 1 KB contiguously, so the XOR swizzle is applied on the global side: the
@@ -151,27 +151,40 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // ---- the first three slots and the Y tile, then the token operands
-  // straight to registers: Q and C as MFMA B operands (lane holds token
-  // `col`, n = 16 ks + 8 half + 0..7), E in the accumulator layout (register
-  // r of row-block rb holds p = 32 rb + 8 (r / 4) + 4 half + r % 4).  All of
-  // it is one round trip: the loop starts once everything has landed.
+  // ---- the first three slots, then the token operands to registers: Q and
+  // C as MFMA B operands (lane holds token `col`, n = 16 ks + 8 half + 0..7),
+  // E in the accumulator layout (register r of row-block rb holds
+  // p = 32 rb + 8 (r / 4) + 4 half + r % 4).  Q and C are staged as whole
+  // rows through a wave-private 8 KB area (ring buffer 3 and the Y area are
+  // not needed before the loop), Q with the slots and E, C in a second round:
+  // loads straight to registers in the MFMA operand layout would touch 32
+  // token rows of 32 bytes each per instruction, and cost more than the
+  // extra round.
   issue(0);
-  issue_tok(a.Y, s_y);
   issue(1);
   issue(2);
+  uint8_t* const s_st = s_mem + 3 * kMemBytes + wave * 8192;
+  const uint32_t qc_bytes = (uint32_t)(last_r * a.G * kN + kN) * 2;
+  const int64_t qc_base = ((row0 + t0) * a.G + g) * kN;
+  // token rows 32 wave + 4 k + lane/16 (past the sequence end: the last
+  // token), local row lr = 4 k + lane/16 at s_st + 256 lr, pieces swizzled
+  // as in a staged chunk memory (mem_off)
+  auto stage = [&](const bf16_t* base) {
+    const auto rs = buf_rsrc(wave_uniform(base + qc_base), qc_bytes);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int lr = 4 * k + (lane >> 4);
+      const int r = 32 * wave + lr;
+      const int rr = r < last_r ? r : last_r;
+      buf_dma16(rs, (uint32_t)(rr * a.G * kN + (((lane & 15) ^ (lr & 15)) << 3)) * 2, s_st + k * 1024);
+    }
+  };
+  stage(a.Q);
   bf16x8_t qf[8], cf[8];
   float ef[2][16];
   {
     const int64_t tl = t0 + wave * 32 + col;
     const int64_t tok = row0 + (tl < a.L ? tl : a.L - 1);
-    const int64_t qrow = (tok * a.G + g) * kN + 8 * half;
-    uint4 qv[8], cv[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qv[ks] = *(const uint4*)(a.Q + qrow + 16 * ks);
-      cv[ks] = *(const uint4*)(a.C + qrow + 16 * ks);
-    }
     uint2 ev[2][4];
     const bf16_t* ep = a.E + (tok * a.G + g) * kP + 4 * half;
 #pragma unroll
@@ -180,26 +193,24 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
       for (int gq = 0; gq < 4; ++gq) ev[rb][gq] = *(const uint2*)(ep + 32 * rb + 8 * gq);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 q = qv[ks], c = cv[ks];
-      // pinned here, where they have landed: left alone the compiler may
-      // convert them later, behind a wait that also covers the slots
-      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-      asm volatile("" : "+v"(c.x), "+v"(c.y), "+v"(c.z), "+v"(c.w));
-      qf[ks] = __builtin_bit_cast(bf16x8_t, q);
-      cf[ks] = __builtin_bit_cast(bf16x8_t, c);
-    }
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8_t*)(s_st + mem_off(col, 2 * ks + half));
+    // the Q rows have been read before the C rows overwrite them
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    stage(a.C);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint2 v = ev[rb][gq];
-        asm volatile("" : "+v"(v.x), "+v"(v.y));
         ef[rb][4 * gq + 0] = bf16lo(v.x) * a.e_scale;
         ef[rb][4 * gq + 1] = bf16hi(v.x) * a.e_scale;
         ef[rb][4 * gq + 2] = bf16lo(v.y) * a.e_scale;
         ef[rb][4 * gq + 3] = bf16hi(v.y) * a.e_scale;
       }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) cf[ks] = *(const bf16x8_t*)(s_st + mem_off(col, 2 * ks + half));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 
   float o[2][16];
@@ -207,18 +218,21 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
   float m = -INFINITY, d = 0.f;
 
-  // slots 0..2 have landed in every wave's part
+  // Slots 0..2 have landed in every wave's part and no wave reads its
+  // staging area any more: the Y tile goes to its area now, ahead of slot 3
+  // (so the loop's waits for slots 3 and later cover it as well).
   __builtin_amdgcn_s_barrier();
+  issue_tok(a.Y, s_y);
 
   for (int j = 0; j < n_hist; ++j) {
     // Chunk j must have landed in every wave's part, and every wave must be
     // done with chunk j-1 before its buffer is refilled (by slot j+kRing-1: a
     // chunk prefetch is issued inside the MFMA burst below so that its issue
-    // cost hides behind queued matrix work).  The only vector-memory
-    // operations in flight are these slot loads, so wait until at most slots
-    // j+1 .. j+kRing-2 remain (__syncthreads() would wait for all of them).
-    // Slots 0..2 landed before the barrier above; later slots are issued
-    // only if they exist.
+    // cost hides behind queued matrix work).  The vector-memory operations
+    // in flight are these slot loads and the Y tile (older than every slot
+    // past 2), so wait until at most slots j+1 .. j+kRing-2 remain
+    // (__syncthreads() would wait for all of them).  Slots 0..2 landed
+    // before the barrier above; later slots are issued only if they exist.
     if (j > 0) {
       // loads that may stay in flight: those of slots j+1 and j+2 issued in
       // the loop (slots past 2 that exist)
