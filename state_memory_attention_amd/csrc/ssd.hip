@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kThreads) void ssd_out_general_kernel(Shape s, cons
 // ---------------------------------------------------------------------------
 // Outputs on the matrix core: bfloat16, N = 128, P = 64, S a multiple of 32
 // up to 256.  One block per (b, h, chunk); the chunk's tokens form slices of
-// 32 and wave w owns slices w and 7 - w (equal causal work).  With one token
-// per lane and P along registers (the transposed output Y^T), per slice:
+// 32, one per wave (eight waves; the two waves on a SIMD own slices w and
+// 7 - w, equal causal work).  With one token per lane and P along registers
+// (the transposed output Y^T), per slice:
 //   Y^T  = Hin_c^T C^T  scaled per token by A_{a_c:t}         (Eq. 22)
 //   for every 32-token block of earlier or equal tokens s:
 //     G^T = B_s C^T  (32 s x 32 t),  masked and decayed by A_{s+1:t},
