@@ -34,6 +34,32 @@ constexpr int kThreads = 256;
 constexpr int kMemBytes = kP * kN * 2;
 constexpr int kRing = 4;         // LDS buffers for chunk memories (3 in flight)
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight 8-byte LDS reads and one 4-byte read, with their wait in the same
+// asm block: written as plain loads, the compiler cannot tell their area from
+// the one a direct-to-LDS load in flight is filling, and places a
+// vector-memory wait before them that also drains the stores issued since.
+__device__ __forceinline__ void ld_lds_8x8_4(u32x2_t (&o)[8], float& d, const uint32_t (&ad)[8], uint32_t a_d) {
+  asm volatile(
+      "ds_read_b64 %0, %9\n\t"
+      "ds_read_b64 %1, %10\n\t"
+      "ds_read_b64 %2, %11\n\t"
+      "ds_read_b64 %3, %12\n\t"
+      "ds_read_b64 %4, %13\n\t"
+      "ds_read_b64 %5, %14\n\t"
+      "ds_read_b64 %6, %15\n\t"
+      "ds_read_b64 %7, %16\n\t"
+      "ds_read_b32 %8, %17\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+        "=&v"(o[7]), "=&v"(d)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "v"(a_d)
+      : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Pass A
 // ---------------------------------------------------------------------------
@@ -102,16 +128,27 @@ void sma_bwd_a_kernel(BwdAArgs a) {
     }
   };
 
-  // ---- token operands (see the forward kernel): Q, C staged as whole rows;
-  // E and dR kept as bfloat16 pairs in the accumulator layout (register r of
-  // row block rb holds p = 32 rb + 8 (r / 4) + 4 half + r % 4).  dR = g * dout
-  // is rounded to bfloat16 once, and D = dR . R and every dR . V use the
-  // rounded values: the gradients are then exactly those of a dout perturbed
-  // by at most one bfloat16 rounding, with no cancellation error in dp - D.
+  // ---- token operands (see the forward kernel): Q and C as MFMA B
+  // operands; E and dR kept as bfloat16 pairs in the accumulator layout
+  // (register r of row block rb holds p = 32 rb + 8 (r / 4) + 4 half + r % 4).
+  // dR = g * dout is rounded to bfloat16 once, and D = dR . R and every
+  // dR . V use the rounded values: the gradients are then exactly those of a
+  // dout perturbed by at most one bfloat16 rounding, with no cancellation
+  // error in dp - D.
+  //
+  // Every token row is read and written whole: Q and C staged through the
+  // ring (wave w: rows 32w .. 32w+31 in bytes [8 KB w, 8 KB w + 8 KB) of the
+  // Q and C halves), E staged in the wave's quarter of the chunk-0 area, and
+  // dout, gate and R loaded in a row layout (lane l of step k: channels
+  // 8 (l % 8) .. +7 of the wave's row 8 k + l / 8), where dR, D and dgate are
+  // formed; dR and D reach the accumulator layout through the wave's Q area
+  // once Q is in registers.  Chunk 0 then loads into the chunk-0 area, each
+  // wave's part over exactly the bytes its E rows occupied.
   bf16x8_t qf[8], cf[8];
   uint2 ev[2][4], drv[2][4];
   float D, lse2;
   {
+    const int last_r = (int)(a.L - 1 - t0 < kTile - 1 ? a.L - 1 - t0 : kTile - 1);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int r = 32 * wave + 4 * k + (lane >> 4);
@@ -120,63 +157,131 @@ void sma_bwd_a_kernel(BwdAArgs a) {
       dma16(a.Q + off, s_mem + (32 * wave + 4 * k) * 256);
       dma16(a.C + off, s_mem + 32768 + (32 * wave + 4 * k) * 256);
     }
-    if (n_hist > 0) issue_mem(0);
-    const bf16_t* ep = a.E + ((row0 + tc) * a.G + g) * kP + 4 * half;
-    const int64_t orow = (row0 + tc) * a.H + h;
-    const bf16_t* dop = a.dout + orow * kP + 4 * half;
-    const float* rp = a.R + orow * kP + 4 * half;
-    const float gs = a.gate_pc ? 0.f : bf16_to_f32(a.gate[orow]);
-    float part = 0.f, gpart = 0.f;
+    {
+      // E rows 32 wave + 8 k + lane / 8 (rows past the end read zeros), pieces
+      // XOR-swizzled by the row within its 128 bytes
+      const auto rse = buf_rsrc(wave_uniform(a.E + ((row0 + t0) * a.G + g) * kP),
+                                (uint32_t)(last_r * a.G * kP + kP) * 2);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int po = 32 * rb + 8 * gq;
-        ev[rb][gq] = *(const uint2*)(ep + po);
-        const uint2 dv = *(const uint2*)(dop + po);
-        const float4 rv = *(const float4*)(rp + po);
-        float g0 = gs, g1 = gs, g2 = gs, g3 = gs;
-        if (a.gate_pc) {
-          const uint2 gv = *(const uint2*)(a.gate + orow * kP + 4 * half + po);
-          g0 = bf16lo(gv.x); g1 = bf16hi(gv.x); g2 = bf16lo(gv.y); g3 = bf16hi(gv.y);
-        }
-        const float d0 = bf16lo(dv.x), d1 = bf16hi(dv.x), d2 = bf16lo(dv.y), d3 = bf16hi(dv.y);
-        uint2 pk;
-        pk.x = pack_bf16x2(g0 * d0, g1 * d1);
-        pk.y = pack_bf16x2(g2 * d2, g3 * d3);
-        drv[rb][gq] = pk;
-        part = fmaf(bf16lo(pk.x), rv.x, part);
-        part = fmaf(bf16hi(pk.x), rv.y, part);
-        part = fmaf(bf16lo(pk.y), rv.z, part);
-        part = fmaf(bf16hi(pk.y), rv.w, part);
-        if (tok_ok) {
-          // dR for pass D, dgate = dout * R (per channel) [§3 Eq. 11]
-          *(uint2*)(a.dR + orow * kP + 4 * half + po) = pk;
-          if (a.dgate && a.gate_pc)
-            *(float4*)(a.dgate + orow * kP + 4 * half + po) =
-                make_float4(d0 * rv.x, d1 * rv.y, d2 * rv.z, d3 * rv.w);
-        }
-        gpart += d0 * rv.x + d1 * rv.y + d2 * rv.z + d3 * rv.w;
+      for (int k = 0; k < 4; ++k) {
+        const int r = 32 * wave + 8 * k + (lane >> 3);
+        buf_dma16(rse, (uint32_t)(r * a.G * kP + (((lane & 7) ^ (r & 7)) << 3)) * 2,
+                  s_e + wave * 4096 + k * 1024);
       }
-    D = halves_sum(part);
-    gpart = halves_sum(gpart);
-    if (a.dgate && !a.gate_pc && half == 0 && tok_ok) a.dgate[orow] = gpart;
+    }
+    // per-token rows [b][L][H][P] of this tile (rows past the end: zeros in,
+    // dropped out)
+    const int64_t obase = ((row0 + t0) * a.H + h) * kP;
+    const uint32_t ob16 = (uint32_t)(last_r * a.H * kP + kP) * 2;
+    const auto rs_do = buf_rsrc(wave_uniform(a.dout + obase), ob16);
+    const auto rs_g = buf_rsrc(wave_uniform(a.gate + (a.gate_pc ? obase : (int64_t)0)), a.gate_pc ? ob16 : 0u);
+    const auto rs_r = buf_rsrc(wave_uniform(a.R + obase), 2 * ob16);
+    const auto rs_gs = buf_rsrc(wave_uniform(a.gate + (row0 + t0) * a.H + h),
+                                a.gate_pc ? 0u : (uint32_t)(last_r * a.H + 1) * 2);
+    const int f = lane & 7;
+    u32x4_t dv[4], gv[4], rv[4][2];
+    uint32_t gsr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = 8 * k + (lane >> 3);
+      const uint32_t ro = (uint32_t)((32 * wave + rr) * a.H * kP + 8 * f);
+      dv[k] = __builtin_amdgcn_raw_buffer_load_b128(rs_do, ro * 2, 0, 0);
+      gv[k] = __builtin_amdgcn_raw_buffer_load_b128(rs_g, ro * 2, 0, 0);
+      rv[k][0] = __builtin_amdgcn_raw_buffer_load_b128(rs_r, ro * 4, 0, 0);
+      rv[k][1] = __builtin_amdgcn_raw_buffer_load_b128(rs_r, ro * 4 + 16, 0, 0);
+      gsr[k] = __builtin_amdgcn_raw_buffer_load_b16(rs_gs, (uint32_t)((32 * wave + rr) * a.H) * 2, 0, 0);
+    }
     lse2 = a.lse[(int64_t)bh * a.L + tc] * kLog2e;
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    // keep the E pairs from being waited for inside the loop
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // pinned here, where they have landed: left alone the compiler may use a
+    // value early and wait for every load in flight to do so
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int k = 0; k < 4; ++k) {
+      asm volatile("" : "+v"(dv[k]), "+v"(gv[k]), "+v"(rv[k][0]), "+v"(rv[k][1]), "+v"(gsr[k]));
+    }
+    {
+      const int r = 32 * wave + col;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        asm volatile("" : "+v"(ev[rb][gq].x), "+v"(ev[rb][gq].y));
-        asm volatile("" : "+v"(drv[rb][gq].x), "+v"(drv[rb][gq].y));
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
+        qf[ks] = *(const bf16x8_t*)(s_mem + o);
+        cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
       }
-    const int r = 32 * wave + col;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t o = r * 256 + (((2 * ks + half) ^ (r & 15)) << 4);
-      qf[ks] = *(const bf16x8_t*)(s_mem + o);
-      cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          ev[rb][gq] = *(const uint2*)(s_e + r * 128 + (((4 * rb + gq) ^ (r & 7)) << 4) + 8 * half);
+    }
+    // Q, C and E are in registers: the wave's Q area takes dR and D, and its
+    // E area chunk 0 (a stand-in if there is no history)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    issue_mem(0);
+    uint8_t* const s_dr = s_mem + wave * 8192;
+    const auto rs_dr = buf_rsrc(wave_uniform(a.dR + obase), ob16);
+    // dgate: [b][L][H][P] per channel, [b][L][H] for a scalar gate
+    const int64_t gbase = a.gate_pc ? obase : (row0 + t0) * a.H + h;
+    const auto rs_dg = buf_rsrc(wave_uniform(a.dgate ? a.dgate + gbase : a.dgate),
+                                a.dgate ? (a.gate_pc ? 2 * ob16 : (uint32_t)(last_r * a.H + 1) * 4) : 0u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = 8 * k + (lane >> 3);
+      const uint32_t ro = (uint32_t)((32 * wave + rr) * a.H * kP + 8 * f);
+      const uint32_t dw[4] = {dv[k].x, dv[k].y, dv[k].z, dv[k].w};
+      const uint32_t gw[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
+      const float rf[8] = {__uint_as_float(rv[k][0].x), __uint_as_float(rv[k][0].y),
+                           __uint_as_float(rv[k][0].z), __uint_as_float(rv[k][0].w),
+                           __uint_as_float(rv[k][1].x), __uint_as_float(rv[k][1].y),
+                           __uint_as_float(rv[k][1].z), __uint_as_float(rv[k][1].w)};
+      u32x4_t pk, dgl, dgh;
+      float part = 0.f, gpart = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d0 = bf16lo(dw[q]), d1 = bf16hi(dw[q]);
+        const float gs = bf16_to_f32(gsr[k]);
+        const float g0 = a.gate_pc ? bf16lo(gw[q]) : gs, g1 = a.gate_pc ? bf16hi(gw[q]) : gs;
+        const uint32_t w = pack_bf16x2(g0 * d0, g1 * d1);
+        pk[q] = w;
+        part = fmaf(bf16lo(w), rf[2 * q], fmaf(bf16hi(w), rf[2 * q + 1], part));
+        gpart += d0 * rf[2 * q] + d1 * rf[2 * q + 1];
+        // dgate = dout * R per channel  [§3 Eq. 11]
+        const float x0 = d0 * rf[2 * q], x1 = d1 * rf[2 * q + 1];
+        if (q < 2) {
+          dgl[2 * q] = __float_as_uint(x0);
+          dgl[2 * q + 1] = __float_as_uint(x1);
+        } else {
+          dgh[2 * q - 4] = __float_as_uint(x0);
+          dgh[2 * q - 3] = __float_as_uint(x1);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(pk, rs_dr, ro * 2, 0, 0);
+      *(u32x4_t*)(s_dr + rr * 128 + ((f ^ (rr & 7)) << 4)) = pk;
+      // D and the scalar gate's gradient: sums over the 8 lanes of the row
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+        part += __shfl_xor(part, m);
+        gpart += __shfl_xor(gpart, m);
+      }
+      if (f == 0) *(float*)(s_dr + 4096 + rr * 4) = part;
+      if (a.gate_pc) {
+        __builtin_amdgcn_raw_buffer_store_b128(dgl, rs_dg, ro * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(dgh, rs_dg, ro * 4 + 16, 0, 0);
+      } else {
+        // one lane per row writes the row's sum; the others fall outside
+        const uint32_t so = f == 0 ? (uint32_t)((32 * wave + rr) * a.H) * 4 : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gpart), rs_dg, so, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(0u, rs_dg, 0x80000000u, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    {
+      uint32_t ad[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ad[i] = lds_addr(s_dr + col * 128 + ((i ^ (col & 7)) << 4) + 8 * half);
+      u32x2_t o[8];
+      ld_lds_8x8_4(o, D, ad, lds_addr(s_dr + 4096 + col * 4));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) drv[i >> 2][i & 3] = make_uint2(o[i].x, o[i].y);
     }
   }
 
@@ -184,7 +289,10 @@ void sma_bwd_a_kernel(BwdAArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) de[0][r] = de[1][r] = 0.f;
 
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  // Chunk 0 has landed in every wave's part (the 12 stores issued after it
+  // may still be in flight) and no wave reads its Q area any more: slots 1
+  // and 2 go to ring buffers 0 and 1.
+  __builtin_amdgcn_s_waitcnt(0x007c);  // vmcnt(12) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   if (n_hist > 0) {
     issue_mem(1);
