@@ -145,7 +145,8 @@ void sma_bwd_a_kernel(BwdAArgs a) {
   // once Q is in registers.  Chunk 0 then loads into the chunk-0 area, each
   // wave's part over exactly the bytes its E rows occupied.
   bf16x8_t qf[8], cf[8];
-  uint2 ev[2][4], drv[2][4];
+  uint2 drv[2][4];
+  float ef[2][16];
   float D, lse2;
   {
     const int last_r = (int)(a.L - 1 - t0 < kTile - 1 ? a.L - 1 - t0 : kTile - 1);
@@ -207,11 +208,18 @@ void sma_bwd_a_kernel(BwdAArgs a) {
         qf[ks] = *(const bf16x8_t*)(s_mem + o);
         cf[ks] = *(const bf16x8_t*)(s_mem + 32768 + o);
       }
+      // E in float32, scaled by log2(e) / sqrt(N) as in the forward, so that
+      // the logit below is formed exactly as the forward formed it
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          ev[rb][gq] = *(const uint2*)(s_e + r * 128 + (((4 * rb + gq) ^ (r & 7)) << 4) + 8 * half);
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint2 v = *(const uint2*)(s_e + r * 128 + (((4 * rb + gq) ^ (r & 7)) << 4) + 8 * half);
+          ef[rb][4 * gq + 0] = bf16lo(v.x) * a.e_scale;
+          ef[rb][4 * gq + 1] = bf16hi(v.x) * a.e_scale;
+          ef[rb][4 * gq + 2] = bf16lo(v.y) * a.e_scale;
+          ef[rb][4 * gq + 3] = bf16hi(v.y) * a.e_scale;
+        }
     }
     // Q, C and E are in registers: the wave's Q area takes dR and D, and its
     // E area chunk 0 (a stand-in if there is no history)
@@ -347,26 +355,19 @@ void sma_bwd_a_kernel(BwdAArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
 
-    // logit (base 2) and dR . V, each over this half-wave's 32 p then both.
-    // The bfloat16 pairs are unpacked here, every iteration: the empty asm
-    // keeps the compiler from hoisting 64 unpacked floats out of the loop.
+    // logit (base 2, the forward's arithmetic) and dR . V, each over this
+    // half-wave's 32 p then both.  The bfloat16 pairs of dR are unpacked
+    // here, every iteration: the empty asm keeps the compiler from hoisting
+    // 32 unpacked floats out of the loop.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
-      asm volatile("" : "+v"(ev[rb][0].x), "+v"(ev[rb][0].y), "+v"(ev[rb][1].x), "+v"(ev[rb][1].y),
-                   "+v"(ev[rb][2].x), "+v"(ev[rb][2].y), "+v"(ev[rb][3].x), "+v"(ev[rb][3].y),
-                   "+v"(drv[rb][0].x), "+v"(drv[rb][0].y), "+v"(drv[rb][1].x), "+v"(drv[rb][1].y),
+      asm volatile("" : "+v"(drv[rb][0].x), "+v"(drv[rb][0].y), "+v"(drv[rb][1].x), "+v"(drv[rb][1].y),
                    "+v"(drv[rb][2].x), "+v"(drv[rb][2].y), "+v"(drv[rb][3].x), "+v"(drv[rb][3].y));
     float pl = 0.f, pv = 0.f;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      pl = fmaf(w0[4 * gq + 0], bf16lo(ev[0][gq].x), pl);
-      pl = fmaf(w0[4 * gq + 1], bf16hi(ev[0][gq].x), pl);
-      pl = fmaf(w0[4 * gq + 2], bf16lo(ev[0][gq].y), pl);
-      pl = fmaf(w0[4 * gq + 3], bf16hi(ev[0][gq].y), pl);
-      pl = fmaf(w1[4 * gq + 0], bf16lo(ev[1][gq].x), pl);
-      pl = fmaf(w1[4 * gq + 1], bf16hi(ev[1][gq].x), pl);
-      pl = fmaf(w1[4 * gq + 2], bf16lo(ev[1][gq].y), pl);
-      pl = fmaf(w1[4 * gq + 3], bf16hi(ev[1][gq].y), pl);
+    for (int r = 0; r < 16; ++r) {
+      pl = fmaf(w0[r], ef[0][r], pl);
+      pl = fmaf(w1[r], ef[1][r], pl);
     }
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -379,7 +380,7 @@ void sma_bwd_a_kernel(BwdAArgs a) {
       pv = fmaf(v1[4 * gq + 2], bf16lo(drv[1][gq].y), pv);
       pv = fmaf(v1[4 * gq + 3], bf16hi(drv[1][gq].y), pv);
     }
-    const float l2 = halves_sum(pl) * a.e_scale;
+    const float l2 = halves_sum(pl);
     const float dp = halves_sum(pv);
     const bool valid = j < my_hist;
     const float pj = valid ? fast_exp2(l2 - lse2) : 0.f;
