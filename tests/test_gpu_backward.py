@@ -273,3 +273,28 @@ def test_bwd_full_size_sampled():
             _, _, _, dd = O.sma_token_backward(Qh[t], Ch[t], Eh[t], mem[: M - 1], gh[t] * oh[t])
             acc += dd[M - 2]
         compare(dict(dH=host(ddH[bi, h, M - 2])), dict(dH=acc.T), TOL["bf16"], f"d_dH[{M - 2}] of (b={bi}, h={h})")
+
+
+@pytest.mark.parametrize("gate_pc", [True, False])
+def test_mfma_bwd_without_dgate(gate_pc):
+    """dgate is optional: without it the matrix-core backward computes the
+    same dQ, dC, dE and d_dH, bit for bit (its stores of dgate go nowhere)."""
+    cfg = dict(batch=1, nheads=2, ngroups=2, seqlen=650, chunk=128, d_state=128, d_head=64, dtype="bf16")
+    say("mfma bwd without dgate", cfg, "gate_pc", gate_pc)
+    d = synth.draw_fwd(**cfg, seed=71, gate_per_channel=gate_pc)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, 128, 64, "bf16", std=1.0, seed=72)
+    dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], 64), "bf16", 73)
+    dt = cfg["dtype"]
+    Q, C, E = dev(d["Q"], dt), dev(d["C"], dt), dev(d["E"], dt)
+    Y, g, dH = dev(d["Y"], dt), dev(d["gate"], dt), dev(mem, dt)
+    _, R, lse = dart.dart_sma_fwd(Q, C, E, dH, Y, g, cfg["chunk"], want_R=True, want_lse=True)
+    go = dev(dout, dt)
+    with_g = dart.dart_sma_bwd(Q, C, E, dH, g, R, lse, go, cfg["chunk"], want_dgate=True)
+    without = dart.dart_sma_bwd(Q, C, E, dH, g, R, lse, go, cfg["chunk"], want_dgate=False)
+    torch.cuda.synchronize()
+    assert without[4] is None
+    for name, a, b in zip(["dQ", "dC", "dE", "d_dH"], with_g[:4], without[:4]):
+        assert torch.equal(a, b), name
+    ref = oracle_bwd(d, to_oracle_mem(mem), cfg, dout, gate_pc)
+    assert err(host(with_g[4]), ref["gate"]) <= TOL["bf16"]
