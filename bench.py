@@ -274,10 +274,39 @@ def time_decode(torch, dart, synth, steps=20, warmup=3):
     res = {"workload": cfg["name"], "us_per_call": t * 1e6, "bytes_per_call": nbytes,
            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
            "traffic": traffic_record("decode", cfg["name"])}
+    res["read_probe"] = time_read_probe(torch, d["cache"], steps, warmup, gbs)
     res["state_update"] = time_state_update(torch, dart, synth, cfg, d["cache"], steps, warmup)
     del d, ws, out
     torch.cuda.empty_cache()
     return res
+
+
+def time_read_probe(torch, buf, steps, warmup, decode_gbs):
+    """What a plain streaming read of the same bytes draws from HBM on this
+    device (libdart_probe.so: 16-byte vector loads, four in flight per lane,
+    16384 blocks): the practical ceiling for a read-bound call, beside the
+    8 TB/s figure."""
+    import ctypes
+
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "libdart_probe.so"))
+    probe.dart_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    stream = ctypes.c_void_p(st.cuda_stream)
+    nbytes = buf.numel() * buf.element_size()
+    for _ in range(warmup):
+        assert probe.dart_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        assert probe.dart_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream) == 0
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    gbs = nbytes / t / 1e9
+    return {"bytes": nbytes, "us_per_call": t * 1e6, "achieved_GBs": gbs,
+            "decode_frac_of_probe": decode_gbs / gbs}
 
 
 def _state_update_inputs(torch, cfg):

@@ -1,7 +1,11 @@
-// Measurement helper, not part of the DART path: a plain device copy of a
-// known number of bytes (16-byte vector loads and stores, grid-stride), used
-// to calibrate the hardware memory-traffic counters against kernels that
-// access memory the same way.  Built as its own library, libdart_probe.so.
+// Measurement helpers, not part of the DART path, built as their own library
+// (libdart_probe.so):
+//   * a plain device copy of a known number of bytes (16-byte vector loads and
+//     stores, grid-stride), used to calibrate the hardware memory-traffic
+//     counters against kernels that access memory the same way;
+//   * a plain streaming read (16-byte vector loads, four in flight per lane,
+//     grid-stride), the yardstick for what a read-only kernel can draw from
+//     HBM on this device.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -12,6 +16,20 @@ __global__ __launch_bounds__(256) void copy16_kernel(const uint4* __restrict__ s
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
+// The loaded words are folded into one value per lane, written only if it
+// equals an impossible pattern, so that the loads are not optimised away.
+__global__ __launch_bounds__(256) void read16_kernel(const uint4* __restrict__ src, size_t n16,
+                                                     unsigned* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.w ^ b.y ^ b.z ^ c.x ^ c.w ^ d.y ^ d.z;
+  }
+  for (; i < n16; i += stride) acc ^= src[i].x;
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
 }  // namespace
 
 // Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) on `stream`.
@@ -21,5 +39,16 @@ extern "C" int dart_probe_copy(const void* src, void* dst, size_t bytes, void* s
   const size_t n16 = bytes / 16;
   if (n16 == 0) return 0;
   copy16_kernel<<<dim3(4096), dim3(256), 0, (hipStream_t)stream>>>((const uint4*)src, (uint4*)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Reads `bytes` (a multiple of 16; `src` 16-byte aligned) on `stream`;
+// `sink` (4 bytes, device) is written only in the impossible case above.
+// Returns 0, or -1 on bad arguments, or -5 if the launch failed.
+extern "C" int dart_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink || (bytes & 15) || ((uintptr_t)src & 15)) return -1;
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  read16_kernel<<<dim3(16384), dim3(256), 0, (hipStream_t)stream>>>((const uint4*)src, n16, (unsigned*)sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
