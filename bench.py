@@ -281,6 +281,38 @@ def time_decode(torch, dart, synth, steps=20, warmup=3):
     return res
 
 
+def time_mfma_probe(torch, dH, Q, steps, warmup, fwd_tflops):
+    """What back-to-back v_mfma_f32_32x32x16_bf16 sustain on this device
+    (libdart_probe.so: operands in registers, two waves per SIMD on every CU,
+    the forward's 32-MFMA burst, no memory traffic), run right after the
+    timed forward with operands taken from the workload (chunk memories as A,
+    queries as B): the practical ceiling for the forward at the clock the chip
+    holds under dense matrix load, beside the 2.5 PF figure."""
+    import ctypes
+
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "libdart_probe.so"))
+    probe.dart_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    ops = torch.cat([dH.reshape(-1)[:4096], Q.reshape(-1)[:4096]]).contiguous()
+    blocks, iters = 512, 400
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    stream = ctypes.c_void_p(st.cuda_stream)
+    for _ in range(warmup):
+        assert probe.dart_probe_mfma(ops.data_ptr(), blocks, iters, sink.data_ptr(), stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        assert probe.dart_probe_mfma(ops.data_ptr(), blocks, iters, sink.data_ptr(), stream) == 0
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    flop = blocks * 4 * iters * 32 * 32 * 32 * 16 * 2
+    tflops = flop / t / 1e12
+    return {"flop_per_launch": flop, "us_per_call": t * 1e6, "achieved_TFLOPs": tflops,
+            "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "fwd_frac_of_probe": fwd_tflops / tflops}
+
+
 def time_read_probe(torch, buf, steps, warmup, decode_gbs):
     """What a plain streaming read of the same bytes draws from HBM on this
     device (libdart_probe.so: 16-byte vector loads, four in flight per lane,
@@ -385,6 +417,16 @@ def profile_kernels(launches=3):
         for _ in range(launches):
             dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], cfg["chunk"], out=out)
         torch.cuda.synchronize()
+        if ci == 2:
+            # the matrix-core yardstick on the same operand values (time_mfma_probe)
+            probe.dart_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            ops = torch.cat([dH.reshape(-1)[:4096], d["Q"].reshape(-1)[:4096]]).contiguous()
+            sink = torch.zeros(512 * 256, dtype=torch.float32, device="cuda")
+            for _ in range(launches):
+                assert probe.dart_probe_mfma(ops.data_ptr(), 512, 400, sink.data_ptr(), stream) == 0
+            torch.cuda.synchronize()
+            del ops, sink
         del d, dH, out
         torch.cuda.empty_cache()
     cfg = dict(synth.CONFIGS[4])
@@ -586,6 +628,7 @@ def main():
         "kernels_us": {"dart_chunk_states": t_cs * 1e6, "dart_sma_fwd": t_fwd * 1e6},
         "path_mfma_frac": (f_sma + f_cs) / (t_cs + t_fwd) / 1e12 / PEAK_BF16_TFLOPS,
     }
+    result["mfma_probe"] = time_mfma_probe(torch, dH, d["Q"], args.steps, args.warmup, achieved)
     del d, dH, out
     torch.cuda.empty_cache()
     if not args.no_rms:

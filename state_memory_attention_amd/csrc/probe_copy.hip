@@ -5,10 +5,17 @@
 //     counters against kernels that access memory the same way;
 //   * a plain streaming read (16-byte vector loads, four in flight per lane,
 //     grid-stride), the yardstick for what a read-only kernel can draw from
-//     HBM on this device.
+//     HBM on this device;
+//   * a plain matrix-core loop (v_mfma_f32_32x32x16_bf16 on operands held in
+//     registers, two waves per SIMD, the forward's burst shape), the yardstick
+//     for what dense bf16 work sustains on this device at the clock it holds
+//     under that load with the given operand values.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 probe_bf16x8_t;
+typedef float probe_f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace {
 __global__ __launch_bounds__(256) void copy16_kernel(const uint4* __restrict__ src,
@@ -30,6 +37,36 @@ __global__ __launch_bounds__(256) void read16_kernel(const uint4* __restrict__ s
   for (; i < n16; i += stride) acc ^= src[i].x;
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
+// Each wave: 16 operand registers (8 A, 8 B) read once from `ops`, then
+// `iters` bursts of 32 MFMAs (8 k-steps x 4 accumulators, two A and two B
+// operands per k-step, as in the forward's per-chunk burst).  The
+// accumulators are folded and written only if the fold equals an impossible
+// value, so that the work is not optimised away.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mfma_kernel(const uint4* __restrict__ ops, int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  probe_bf16x8_t a[8], b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = __builtin_bit_cast(probe_bf16x8_t, ops[64 * k + lane]);
+    b[k] = __builtin_bit_cast(probe_bf16x8_t, ops[512 + 64 * k + lane]);
+  }
+  probe_f32x16_t w0 = {}, w1 = {}, v0 = {}, v1 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const probe_bf16x8_t a0 = a[ks], a1 = a[(ks + 1) & 7];
+      w0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[ks], w0, 0, 0, 0);
+      w1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[ks], w1, 0, 0, 0);
+      v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[(ks + 3) & 7], v0, 0, 0, 0);
+      v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[(ks + 3) & 7], v1, 0, 0, 0);
+    }
+  }
+  float f = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f += w0[r] + w1[r] + v0[r] + v1[r];
+  if (f == 1234.5f) sink[blockIdx.x * blockDim.x + threadIdx.x] = f;
+}
 }  // namespace
 
 // Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) on `stream`.
@@ -50,5 +87,16 @@ extern "C" int dart_probe_read(const void* src, size_t bytes, void* sink, void* 
   const size_t n16 = bytes / 16;
   if (n16 == 0) return 0;
   read16_kernel<<<dim3(16384), dim3(256), 0, (hipStream_t)stream>>>((const uint4*)src, n16, (unsigned*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Runs `blocks` blocks of 4 waves, each wave `iters` bursts of 32
+// v_mfma_f32_32x32x16_bf16 (32768 flop each) on operands from `ops` (16 KB,
+// 16-byte aligned: 512 pieces of A then 512 of B).  `sink` holds one float
+// per thread and is written only in the impossible case above.  Returns 0,
+// or -1 on bad arguments, or -5 if the launch failed.
+extern "C" int dart_probe_mfma(const void* ops, int blocks, int iters, void* sink, void* stream) {
+  if (!ops || !sink || blocks <= 0 || iters < 0 || ((uintptr_t)ops & 15)) return -1;
+  mfma_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((const uint4*)ops, iters, (float*)sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
