@@ -167,13 +167,16 @@ MFMA_CASES = [
     dict(batch=2, nheads=2, ngroups=2, seqlen=777, chunk=64, d_state=128, d_head=64, dtype="bf16"),
     dict(batch=1, nheads=2, ngroups=1, seqlen=1300, chunk=256, d_state=128, d_head=64, dtype="bf16"),
     dict(batch=1, nheads=3, ngroups=3, seqlen=200, chunk=50, d_state=128, d_head=64, dtype="bf16"),
+    # shorter than one wave's 32 tokens (waves 1-3 load and store nothing),
+    # scalar gate
+    dict(batch=2, nheads=2, ngroups=1, seqlen=20, chunk=8, d_state=128, d_head=64, dtype="bf16"),
 ]
 
 
 @pytest.mark.parametrize("ci", range(len(MFMA_CASES)))
 def test_mfma_bwd_against_oracle_and_general(ci):
     cfg = MFMA_CASES[ci]
-    gate_pc = ci != 1
+    gate_pc = ci not in (1, 4)
     say("mfma bwd", cfg, "gate_pc", gate_pc)
     d = synth.draw_fwd(**cfg, seed=51 + ci, gate_per_channel=gate_pc)
     M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])

@@ -85,6 +85,8 @@ def test_mfma_sharpness_sweep(qgain):
     (700, 300, 2, True),     # S > token tile
     (129, 128, 4, False),    # one token in the second chunk
     (100, 256, 4, True),     # everything in chunk 0
+    (20, 8, 2, True),        # waves 1-3 of the tile hold no token, two chunks in view
+    (40, 16, 1, False),      # the same with a shared group and the scalar gate
     (5000, 1000, 1, True),
 ])
 def test_mfma_stress_shapes(L, S, G, gate_pc):
