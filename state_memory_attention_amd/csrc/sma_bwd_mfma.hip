@@ -551,23 +551,37 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
         rp, (__attribute__((address_space(3))) void*)(dst + kMemBytes + wave * 256), 4, pd_lane, 0, 0, 0);
   };
 
-  // B operands: lane holds token `col`, p = 16 ks + 8 half + 0..7
+  // B operands: lane holds token `col`, p = 16 ks + 8 half + 0..7.  The E
+  // and dR rows of the wave's 32 tokens are staged whole (128-byte rows,
+  // 16-byte pieces XOR-swizzled by the row) in the wave's parts of ring
+  // buffers 2 and 3 while slots 0 and 1 load; slot 2 follows once they are in
+  // registers (this wave's part of it covers exactly the bytes its E rows
+  // occupied; buffer 3 takes slot 3 only after the loop's first barrier).
   bf16x8_t eop[4], rop[4];
   {
-    const bf16_t* ep = a.E + ((row0 + tc) * a.G + g) * kP + 8 * half;
-    const bf16_t* rp = a.dR + ((row0 + tc) * a.H + h) * kP + 8 * half;
+    if (0 < n_hist) issue(0);
+    if (1 < n_hist) issue(1);
+    const int last_r = (int)(a.L - 1 - t0 < kTile - 1 ? a.L - 1 - t0 : kTile - 1);
+    uint8_t* const s_se = s_ring + 2 * kSlotBC + wave * 4096;
+    uint8_t* const s_sr = s_ring + 3 * kSlotBC + wave * 4096;
+    const auto rse = buf_rsrc(wave_uniform(a.E + ((row0 + t0) * a.G + g) * kP), (uint32_t)(last_r * a.G * kP + kP) * 2);
+    const auto rsr = buf_rsrc(wave_uniform(a.dR + ((row0 + t0) * a.H + h) * kP), (uint32_t)(last_r * a.H * kP + kP) * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 32 * wave + 8 * k + (lane >> 3);
+      const uint32_t sw = (uint32_t)(((lane & 7) ^ (r & 7)) << 3);
+      buf_dma16(rse, (uint32_t)(r * a.G * kP + sw) * 2, s_se + k * 1024);
+      buf_dma16(rsr, (uint32_t)(r * a.H * kP + sw) * 2, s_sr + k * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      eop[ks] = *(const bf16x8_t*)(ep + 16 * ks);
-      rop[ks] = *(const bf16x8_t*)(rp + 16 * ks);
+      const uint32_t o = col * 128 + (((2 * ks + half) ^ (col & 7)) << 4);
+      eop[ks] = *(const bf16x8_t*)(s_se + o);
+      rop[ks] = *(const bf16x8_t*)(s_sr + o);
     }
-  }
-  for (int s = 0; s < kRing - 1 && s < n_hist; ++s) issue(s);
-  __builtin_amdgcn_s_waitcnt(kWaitAll);  // operands and the first slots
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    asm volatile("" : "+v"(eop[ks]));
-    asm volatile("" : "+v"(rop[ks]));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (2 < n_hist) issue(2);
   }
 
   // A operand (dH: rows n, k = p): lane (column j16 + 16 grp16 of row block
