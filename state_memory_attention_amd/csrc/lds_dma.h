@@ -23,6 +23,21 @@ __device__ __forceinline__ T* wave_uniform(T* p) {
   return (T*)(((uint64_t)hi << 32) | lo);
 }
 
+// Block order of the token-tile kernels (a block = one 128-token tile of one
+// (b, h); head slots padded to a multiple of 8).  Consecutive block numbers
+// go round-robin to the 8 XCDs, so head slot xcd + 8 k always lands on XCD
+// xcd; each XCD takes its heads one after another and every head's tiles
+// last first (longest history first).  The tiles in flight on an XCD then
+// share one or two heads' chunk memories, which stay in its L2 (with heads
+// interleaved, the working set of every head of the XCD exceeded it).
+struct TileItem {
+  int bh, tile;
+};
+__device__ __forceinline__ TileItem head_major_tile(int blk, int n_tiles) {
+  const int xi = blk >> 3;
+  return TileItem{(blk & 7) + 8 * (xi / n_tiles), n_tiles - 1 - xi % n_tiles};
+}
+
 // One direct global->LDS load: every lane fetches 16 bytes from `src`, and
 // lane l's bytes land at lds + 16 l (the LDS address is wave-uniform).
 __device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {

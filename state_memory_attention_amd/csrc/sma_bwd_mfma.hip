@@ -93,9 +93,10 @@ void sma_bwd_a_kernel(BwdAArgs a) {
   uint8_t* const s_e = s_lds + kRing * kMemBytes;
 
   const int blk = blockIdx.x;
-  const int bh = blk % a.BHp;
+  const TileItem item = head_major_tile(blk, a.n_tiles);
+  const int bh = item.bh;
   if (bh >= a.BH) return;
-  const int tile = a.n_tiles - 1 - blk / a.BHp;
+  const int tile = item.tile;
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
 
   const int tid = threadIdx.x;
@@ -515,9 +516,10 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing * kSlotBC];
 
   const int blk = blockIdx.x;
-  const int bh = blk % a.BHp;
+  const TileItem item = head_major_tile(blk, a.n_tiles);
+  const int bh = item.bh;
   if (bh >= a.BH) return;
-  const int tile = a.n_tiles - 1 - blk / a.BHp;
+  const int tile = item.tile;
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, half = lane >> 5;

@@ -30,10 +30,10 @@
 // run for every chunk) is almost never taken.  R = O/d and lse = m + log d are
 // unchanged by the choice of m up to rounding.
 //
-// Block order: blocks are numbered tile-major (last tile first, i.e. longest
-// history first) and head-minor over a head count padded to a multiple of 8.
-// Consecutive block numbers go round-robin to the 8 XCDs, so every tile of one
-// (b, h) lands on the same XCD and reuses that head's chunk memories in its L2.
+// Block order (head_major_tile): every tile of one (b, h) lands on the same
+// XCD, each XCD works through its heads one after another, longest history
+// first, so the tiles in flight reuse one or two heads' chunk memories from
+// that XCD's L2.
 #include "dart_internal.h"
 #include "dev_common.h"
 #include "lds_dma.h"
@@ -78,9 +78,10 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   uint8_t* const s_y = s_lds + kRing * kMemBytes;
 
   const int blk = blockIdx.x;
-  const int bh = blk % a.BHp;
+  const TileItem item = head_major_tile(blk, a.n_tiles);
+  const int bh = item.bh;
   if (bh >= a.BH) return;
-  const int tile = a.n_tiles - 1 - blk / a.BHp;
+  const int tile = item.tile;
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
 
   const int tid = threadIdx.x;

@@ -68,9 +68,10 @@ void sma_fwd_rms_mfma_kernel(FwdRmsArgs a) {
   uint8_t* const s_y = s_lds + 2 * kSlot;
 
   const int blk = blockIdx.x;
-  const int bh = blk % a.BHp;
+  const TileItem item = head_major_tile(blk, a.n_tiles);
+  const int bh = item.bh;
   if (bh >= a.BH) return;
-  const int tile = a.n_tiles - 1 - blk / a.BHp;
+  const int tile = item.tile;
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
 
   const int tid = threadIdx.x;
