@@ -25,7 +25,8 @@
 //     The float16 score memory is the only rounding the normalisation adds;
 //   * the Q and C tiles go straight to registers (no LDS staging), which
 //     frees the LDS for the wider slots; the Y tile has its own 16 KB area
-//     and the gate tile takes the ring slot freed by the second-to-last chunk.
+//     (which first stages the E tile as whole rows) and the gate tile takes
+//     the ring slot freed by the second-to-last chunk.
 #include "dart_internal.h"
 #include "dev_common.h"
 #include "lds_dma.h"
@@ -123,8 +124,21 @@ void sma_fwd_rms_mfma_kernel(FwdRmsArgs a) {
   };
 
   issue(0);
-  issue_tok(a.Y, s_y);
   issue(1);
+  // E rows of this wave staged whole in its quarter of the Y area (free
+  // until the epilogue; the Y tile follows once E is in registers)
+  {
+    const auto rse = buf_rsrc(wave_uniform(a.E + ((row0 + t0) * a.G + g) * kP),
+                              (uint32_t)(last_r * a.G * kP + kP) * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // rows past the sequence end re-read the last token (finite norms)
+      const int r = 32 * wave + 8 * k + (lane >> 3);
+      const int rr = r < last_r ? r : last_r;
+      buf_dma16(rse, (uint32_t)(rr * a.G * kP + (((lane & 7) ^ (r & 7)) << 3)) * 2,
+                s_y + wave * 32 * 128 + k * 1024);
+    }
+  }
 
   // ---- token operands straight to registers.  Q and C as MFMA B operands:
   // lane holds token `col`, n = 16 ks + 8 half + 0..7; E in the accumulator
@@ -142,12 +156,18 @@ void sma_fwd_rms_mfma_kernel(FwdRmsArgs a) {
       cv[ks] = *(const uint4*)(a.C + qrow + 16 * ks);
     }
     uint2 ev[2][4];
-    const bf16_t* ep = a.E + ((row0 + tc) * a.G + g) * kP + 4 * half;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) ev[rb][gq] = *(const uint2*)(ep + 32 * rb + 8 * gq);
     __builtin_amdgcn_s_waitcnt(kWaitAll);
+    {
+      const int tr = 32 * wave + col;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          ev[rb][gq] = *(const uint2*)(s_y + tr * 128 + (((4 * rb + gq) ^ (tr & 7)) << 4) + 8 * half);
+      // E is in registers before this wave's Y rows overwrite it
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue_tok(a.Y, s_y);
+    }
     // RMSNorm of Q_t and E_t [App. B.1 Eq. 25]: this lane holds half of each row
     float ssq = 0.f, sse = 0.f;
 #pragma unroll
@@ -203,13 +223,14 @@ void sma_fwd_rms_mfma_kernel(FwdRmsArgs a) {
   for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
   float m = -INFINITY, d = 0.f;
 
-  // every load above has drained (the wait covered the slot loads too);
-  // the barrier makes all waves' parts of slots 0 and 1 visible
+  // every load above but the Y tile has drained (the wait covered the slot
+  // loads too); the barrier makes all waves' parts of slots 0 and 1 visible
   __builtin_amdgcn_s_barrier();
 
   for (int j = 0; j < n_hist; ++j) {
     // chunk j landed in every wave's part, every wave is done with chunk
-    // j - 1: its slot takes slot j + 1 (the only load in flight)
+    // j - 1: its slot takes slot j + 1 (the only load in flight, with the
+    // Y tile until the first of these waits)
     if (j > 0) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __builtin_amdgcn_s_barrier();
