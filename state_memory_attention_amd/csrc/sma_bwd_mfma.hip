@@ -1057,6 +1057,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void chunk_states_bwd_mfma_kernel(CsBwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_g[kMemBytes];   // G^T, tr-read swizzle
   __shared__ float s_w[kGroupCS + 4];
+  // per wave: 8 KB of B rows (later the dX / dB rows on their way out) and
+  // 4 KB of X rows
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 12288];
 
   const int nh = a.H;
   const int bb = blockIdx.x / (a.M * nh);
@@ -1125,23 +1128,85 @@ void chunk_states_bwd_mfma_kernel(CsBwdArgs a) {
       __syncthreads();
     }
     for (int64_t pb = g0; pb < gend; pb += kTile) {           // 128-token passes
-      const int64_t sl = pb + 32 * wave + col;                // chunk-local token of this lane
-      const bool ok = sl < gend;
-      const int64_t tok = row0 + s0 + (ok ? sl : gend - 1);
-      // B operands: B_c^T (k = n, 8 per lane per step) and X_c^T (k = p)
-      const bf16_t* brow = a.B + (tok * a.G + g) * kN + 8 * half;
-      const bf16_t* xrow = a.X + (tok * a.H + h) * kP + 8 * half;
-      f32x16_t t0 = {}, t1 = {};
+      // This wave's 32 tokens from pb + 32 wave (nv of them hold data): the B
+      // and X rows are staged whole in the wave's area (B: 256-byte rows, X:
+      // 128-byte rows, 16-byte pieces XOR-swizzled by the row) and the MFMA
+      // operands and the epilogue's X are read from there; dX and dB (float32)
+      // leave through the B part as whole rows.  Rows past the group end read
+      // zeros and their stores fall outside the buffer resources.
+      uint8_t* const s_b = s_stage + wave * 12288;
+      uint8_t* const s_x = s_b + 8192;
+      const int64_t tw = pb + 32 * wave;  // chunk-local first token of the wave
+      const int nv = (int)(gend - tw < 32 ? (gend - tw > 0 ? gend - tw : 0) : 32);
+      const int64_t tok0 = row0 + s0 + tw;
+      const int hh = a.db_heads == a.H ? h : g;
+      const auto rsb = buf_rsrc(wave_uniform(a.B + (tok0 * a.G + g) * kN),
+                                nv > 0 ? (uint32_t)((nv - 1) * a.G * kN + kN) * 2 : 0u);
+      const auto rsx = buf_rsrc(wave_uniform(a.X + (tok0 * a.H + h) * kP),
+                                nv > 0 ? (uint32_t)((nv - 1) * a.H * kP + kP) * 2 : 0u);
+      const auto rdx = buf_rsrc(wave_uniform(a.dX + (tok0 * a.H + h) * kP),
+                                nv > 0 ? (uint32_t)((nv - 1) * a.H * kP + kP) * 4 : 0u);
+      const auto rdb = buf_rsrc(wave_uniform(a.dB + (tok0 * a.db_heads + hh) * kN),
+                                nv > 0 ? (uint32_t)((nv - 1) * a.db_heads * kN + kN) * 4 : 0u);
+      // the previous pass's reads of the area are done before the loads refill it
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t bv = *(const bf16x8_t*)(brow + 16 * ks);
-        t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt_frag(col, ks), bv, t0, 0, 0, 0);
-        t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt_frag(32 + col, ks), bv, t1, 0, 0, 0);
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4);
+        buf_dma16(rsb, (uint32_t)(r * a.G * kN + (((lane & 15) ^ (r & 15)) << 3)) * 2, s_b + k * 1024);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3);
+        buf_dma16(rsx, (uint32_t)(r * a.H * kP + (((lane & 7) ^ (r & 7)) << 3)) * 2, s_x + k * 1024);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      // T^T = G^T B_c^T first (B operand: B_c^T, k = n, 8 per lane per step),
+      // and its epilogue, then dB^T = G X_c^T: one accumulator set at a time.
+      // Lane column = token; accumulator register r of row block rb holds row
+      // 32 rb + 8 (r / 4) + 4 half + r % 4 (p for T, n for dB).
+      const float w = s_w[(int)(tw - g0) + col];
+      const int orow = lane >> 4, opc = lane & 15;
+      {
+        f32x16_t t0 = {}, t1 = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8_t bv = *(const bf16x8_t*)(s_b + col * 256 + (((2 * ks + half) ^ (col & 15)) << 4));
+          t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt_frag(col, ks), bv, t0, 0, 0, 0);
+          t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt_frag(32 + col, ks), bv, t1, 0, 0, 0);
+        }
+        // dX = w T into the B part (its B rows are all read), dw = X . T
+        float part = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16_t& tt = rb ? t1 : t0;
+            const uint2 xv = *(const uint2*)(s_x + col * 128 + (((4 * rb + q) ^ (col & 7)) << 4) + 8 * half);
+            part = fmaf(bf16lo(xv.x), tt[4 * q + 0], part);
+            part = fmaf(bf16hi(xv.x), tt[4 * q + 1], part);
+            part = fmaf(bf16lo(xv.y), tt[4 * q + 2], part);
+            part = fmaf(bf16hi(xv.y), tt[4 * q + 3], part);
+            *(float4*)(s_b + col * 256 + (((8 * rb + 2 * q + half) ^ (col & 15)) << 4)) =
+                make_float4(w * tt[4 * q + 0], w * tt[4 * q + 1], w * tt[4 * q + 2], w * tt[4 * q + 3]);
+          }
+        const float dw = halves_sum(part);
+        if (col < nv && half == 0) {
+          a.wsw[(int64_t)bh * a.L + s0 + tw + col] = w;
+          a.wsdw[(int64_t)bh * a.L + s0 + tw + col] = dw;
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = 4 * k + orow;
+          const u32x4_t v = *(const u32x4_t*)(s_b + r * 256 + ((opc ^ (r & 15)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(v, rdx, (uint32_t)(r * a.H * kP + 4 * opc) * 4, 0, 0);
+        }
       }
       f32x16_t db[4] = {{}, {}, {}, {}};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t xv = *(const bf16x8_t*)(xrow + 16 * ks);
+        const bf16x8_t xv = *(const bf16x8_t*)(s_x + col * 128 + (((2 * ks + half) ^ (col & 7)) << 4));
         uint32_t ad[8];
         uint64_t rd[8];
 #pragma unroll
@@ -1158,38 +1223,27 @@ void chunk_states_bwd_mfma_kernel(CsBwdArgs a) {
           db[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xv, db[rb], 0, 0, 0);
         }
       }
-      // epilogue: lane column = token; T rows p = 32 rb + 8 (r/4) + 4 half + r%4
-      const float w = s_w[(int)(pb - g0) + 32 * wave + col];
-      const bf16_t* xa = a.X + (tok * a.H + h) * kP + 4 * half;
-      float part = 0.f;
-      float* dxp = a.dX + (tok * a.H + h) * kP + 4 * half;
+      // dB = w dB^T, 64 n at a time through the B part
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int hb = 0; hb < 2; ++hb) {
+        // the rows above are read before this half overwrites them
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x16_t& tt = rb ? t1 : t0;
-          const uint2 xv = *(const uint2*)(xa + 32 * rb + 8 * q);
-          part = fmaf(bf16lo(xv.x), tt[4 * q + 0], part);
-          part = fmaf(bf16hi(xv.x), tt[4 * q + 1], part);
-          part = fmaf(bf16lo(xv.y), tt[4 * q + 2], part);
-          part = fmaf(bf16hi(xv.y), tt[4 * q + 3], part);
-          if (ok)
-            *(float4*)(dxp + 32 * rb + 8 * q) =
-                make_float4(w * tt[4 * q + 0], w * tt[4 * q + 1], w * tt[4 * q + 2], w * tt[4 * q + 3]);
+        for (int rbb = 0; rbb < 2; ++rbb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16_t& dd = db[2 * hb + rbb];
+            *(float4*)(s_b + col * 256 + (((8 * rbb + 2 * q + half) ^ (col & 15)) << 4)) =
+                make_float4(w * dd[4 * q + 0], w * dd[4 * q + 1], w * dd[4 * q + 2], w * dd[4 * q + 3]);
+          }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = 4 * k + orow;
+          const u32x4_t v = *(const u32x4_t*)(s_b + r * 256 + ((opc ^ (r & 15)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(v, rdb, (uint32_t)(r * a.db_heads * kN + 64 * hb + 4 * opc) * 4,
+                                                 0, 0);
         }
-      const float dw = halves_sum(part);
-      if (ok && half == 0) {
-        a.wsw[(int64_t)bh * a.L + s0 + sl] = w;
-        a.wsdw[(int64_t)bh * a.L + s0 + sl] = dw;
-      }
-      if (ok) {
-        float* dbp = a.dB + (tok * a.db_heads + (a.db_heads == a.H ? h : g)) * kN + 4 * half;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(float4*)(dbp + 32 * rb + 8 * q) = make_float4(w * db[rb][4 * q + 0], w * db[rb][4 * q + 1],
-                                                            w * db[rb][4 * q + 2], w * db[rb][4 * q + 3]);
       }
     }
   }
