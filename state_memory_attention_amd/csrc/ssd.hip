@@ -24,6 +24,7 @@ namespace dart {
 namespace {
 
 constexpr int kThreads = 256;
+typedef unsigned int u32x4_ssd_t __attribute__((ext_vector_type(4)));
 constexpr unsigned kWaitVm1 = 0x0f71;  // s_waitcnt vmcnt(1)
 
 // ---------------------------------------------------------------------------
@@ -416,15 +417,30 @@ void ssd_out_mfma_kernel(SsdArgs a) {
       ssd_intra_block(y, cq, lt, zt, tl, s_lds + kOffB + (j % 3) * kBStage, s_x, s_l, 32 * j, col, half, grp16, j16);
   }
 
-  // ---- Y^T[p][t]: register r of y[f] holds p = 32 f + 8 (r / 4) + 4 half + r % 4
-  if (act && tl < clen) {
-    bf16_t* yp = a.Y + ((row0 + s0 + tl) * a.H + h) * kP + 4 * half;
+  // ---- Y^T[p][t]: register r of y[f] holds p = 32 f + 8 (r / 4) + 4 half + r % 4.
+  // Y leaves through the X tile's area (free once every wave is past its last
+  // block of s): the wave writes its slice's 32 token rows (128 bytes, 16-byte
+  // pieces XOR-swizzled by the row) and stores them whole, eight rows per
+  // instruction; rows past the chunk end fall outside the buffer resource.
+  __builtin_amdgcn_s_barrier();
+  if (act) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      *(uint2*)(yp + 8 * jj) = make_uint2(pack_bf16x2(y[0][4 * jj], y[0][4 * jj + 1]),
-                                          pack_bf16x2(y[0][4 * jj + 2], y[0][4 * jj + 3]));
-      *(uint2*)(yp + 32 + 8 * jj) = make_uint2(pack_bf16x2(y[1][4 * jj], y[1][4 * jj + 1]),
-                                               pack_bf16x2(y[1][4 * jj + 2], y[1][4 * jj + 3]));
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *(uint2*)(s_x + tl * 128 + (((4 * f + jj) ^ (tl & 7)) << 4) + 8 * half) =
+            make_uint2(pack_bf16x2(y[f][4 * jj], y[f][4 * jj + 1]), pack_bf16x2(y[f][4 * jj + 2], y[f][4 * jj + 3]));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    const int nv = clen - 32 * sl < 32 ? clen - 32 * sl : 32;
+    const auto ry = buf_rsrc(wave_uniform(a.Y + ((row0 + s0 + 32 * sl) * a.H + h) * kP),
+                             (uint32_t)((nv - 1) * a.H * kP + kP) * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + (lane >> 3), pc = lane & 7;  // row within the slice
+      const int rt = 32 * sl + r;                          // row within the chunk
+      const uint4 v = *(const uint4*)(s_x + rt * 128 + ((pc ^ (rt & 7)) << 4));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_ssd_t, v), ry,
+                                             (uint32_t)(r * a.H * kP + 8 * pc) * 2, 0, 0);
     }
   }
 }
