@@ -207,6 +207,8 @@ def test_mfma_bwd_sharp_weights():
     dict(batch=1, nheads=4, ngroups=2, seqlen=900, chunk=300, d_state=128, d_head=64),  # 2 weight groups
     dict(batch=2, nheads=2, ngroups=2, seqlen=333, chunk=100, d_state=128, d_head=64),
     dict(batch=1, nheads=2, ngroups=1, seqlen=512, chunk=256, d_state=128, d_head=64),
+    # chunks of 40 tokens: waves 2 and 3 of every pass hold none
+    dict(batch=2, nheads=3, ngroups=3, seqlen=200, chunk=40, d_state=128, d_head=64),
 ])
 def test_chunk_states_bwd_mfma(cfg):
     """dX, dB, dA on the matrix core (d_dH rounded to bf16 as its operand)
