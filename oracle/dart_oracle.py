@@ -384,12 +384,17 @@ def sma_head_backward(Q, C, E, dH, S: int, dR, lse=None):
         g = dR[s0:s1]
         dp = np.einsum("tp,tcp->tc", g, V)
         dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-        dC[s0:s1] = np.einsum("tc,cnp,tp->tn", p, hist, g, optimize=True)
+        # dC_t = sum_c dH_c dV_tc = sum_c p_tc (dH_c dR_t)
+        G = np.einsum("cnp,tp->tcn", hist, g, optimize=True)                 # dH_c dR_t
+        dC[s0:s1] = np.einsum("tc,tcn->tn", p, G)
         dQ[s0:s1] = np.einsum("tc,tcn->tn", dl, K) * scale
         W = np.einsum("tn,cnp->tcp", Q[s0:s1], hist, optimize=True)          # Q_t dH_c
         dE[s0:s1] = np.einsum("tc,tcp->tp", dl, W) * scale
-        ddH[:i] += np.einsum("tc,tn,tp->cnp", p, C[s0:s1], g, optimize=True)
-        ddH[:i] += np.einsum("tc,tn,tp->cnp", dl, Q[s0:s1], E[s0:s1], optimize=True) * scale
+        # d dH_c = sum_t (p_tc C_t)^T dR_t + (dl_tc Q_t)^T E_t / sqrt(N)
+        pC = p[:, :, None] * C[s0:s1, None, :]                               # (t, c, n)
+        dlQ = dl[:, :, None] * Q[s0:s1, None, :]
+        ddH[:i] += np.einsum("tcn,tp->cnp", pC, g, optimize=True)
+        ddH[:i] += np.einsum("tcn,tp->cnp", dlQ, E[s0:s1], optimize=True) * scale
     return dQ, dC, dE, ddH
 
 
