@@ -395,10 +395,14 @@ hipError_t launch_sma_bwd_general(const Shape& s, bool bf16, const void* Q, cons
   return hipGetLastError();
 }
 
+// Workspace of the chunk-state backward: w_s and dw_s [b][H][L] float32 each,
+// then (grouped heads) per-head dB [b][L][H][N] float32 from the next
+// 256-byte boundary (the matrix-core kernel writes it with 16-byte stores).
+static int64_t cs_bwd_heads_offset(const Shape& s) { return (2 * s.b * s.H * s.L + 63) / 64 * 64; }
+
 size_t chunk_states_bwd_workspace_bytes(const Shape& s) {
-  const int64_t wdw = 2 * s.b * s.H * s.L;
   const int64_t heads = (s.H != s.G) ? s.b * s.L * s.H * s.N : 0;
-  return (size_t)(wdw + heads) * sizeof(float);
+  return (size_t)(cs_bwd_heads_offset(s) + heads) * sizeof(float);
 }
 
 hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, bool mfma, const void* X,
@@ -407,7 +411,7 @@ hipError_t launch_chunk_states_bwd_general(const Shape& s, bool bf16, bool mfma,
   float* wsw = ws;
   float* wsdw = ws + s.b * s.H * s.L;
   const bool grouped = s.H != s.G;
-  float* hb = grouped ? wsdw + s.b * s.H * s.L : dB;
+  float* hb = grouped ? ws + cs_bwd_heads_offset(s) : dB;
   const int64_t hs = grouped ? s.H : s.G;
   const unsigned blocks = (unsigned)(s.b * s.H * s.M);
   if (mfma) {

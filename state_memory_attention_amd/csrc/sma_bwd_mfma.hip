@@ -997,9 +997,16 @@ hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, 
 // Workspace of the MFMA backward: (p, dl) rows [b][H][M][2][L] float32, dR
 // [b][L][H][P] bfloat16 and, for grouped heads, per-head dQ, dC [b][L][H][N]
 // and dE [b][L][H][P] float32 (summed over the group at the end).
+// Every part starts on a 256-byte boundary: dR takes 16-byte stores and
+// 16-byte direct-to-LDS loads, and the per-head partials 16-byte stores.
+namespace {
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+size_t pd_bytes_of(const Shape& s) { return round256((size_t)(2 * s.b * s.H * s.M * s.L) * 4); }
+size_t dr_bytes_of(const Shape& s) { return round256((size_t)(s.b * s.L * s.H * s.P) * 2); }
+}  // namespace
+
 size_t sma_bwd_mfma_workspace_bytes(const Shape& s) {
-  size_t bytes = (size_t)(2 * s.b * s.H * s.M * s.L) * 4 + (size_t)(s.b * s.L * s.H * s.P) * 2;
-  bytes = (bytes + 255) / 256 * 256;
+  size_t bytes = pd_bytes_of(s) + dr_bytes_of(s);
   if (s.H != s.G) bytes += (size_t)(s.b * s.L * s.H * (2 * s.N + s.P)) * 4;
   return bytes;
 }
@@ -1010,9 +1017,9 @@ hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, con
                                float* ddH, float* dgate, void* ws, hipStream_t st) {
   uint8_t* w = (uint8_t*)ws;
   float* pd = (float*)w;
-  void* dR = w + (size_t)(2 * s.b * s.H * s.M * s.L) * 4;
+  void* dR = w + pd_bytes_of(s);
   const bool grouped = s.H != s.G;
-  size_t off = ((size_t)(2 * s.b * s.H * s.M * s.L) * 4 + (size_t)(s.b * s.L * s.H * s.P) * 2 + 255) / 256 * 256;
+  const size_t off = pd_bytes_of(s) + dr_bytes_of(s);
   float* hq = grouped ? (float*)(w + off) : dQ;
   float* hc = grouped ? hq + s.b * s.L * s.H * s.N : dC;
   float* he = grouped ? hc + s.b * s.L * s.H * s.N : dE;
