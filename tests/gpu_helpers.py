@@ -58,3 +58,43 @@ def to_oracle_mem(mem_gpu_layout):
 def oracle_head_states(X, B, A, b, h, G, H, S):
     g = h // (H // G)
     return O.chunk_states_head(X[b, :, h], B[b, :, g], A[b, :, h], S)
+
+
+def f64(t):
+    """torch tensor (any device, any dtype, any strides) -> numpy float64."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+class MaxErr:
+    """The max-abs-normalised error of ``err`` for one output tensor that is
+    checked in pieces (one batch row and head at a time, so that host memory
+    stays bounded): running max |gpu - ref| and max |ref| over every piece,
+    with the same -inf and finiteness rules."""
+
+    def __init__(self, name):
+        self.name, self.diff, self.scale, self.worst, self.count = name, 0.0, 0.0, None, 0
+
+    def add(self, gpu, ref, where=None):
+        gpu = np.asarray(gpu, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert gpu.shape == ref.shape, (self.name, where, gpu.shape, ref.shape)
+        ninf = np.isneginf(ref)
+        assert np.array_equal(ninf, np.isneginf(gpu)), f"{self.name}: -inf positions differ at {where}"
+        fin = ~ninf
+        self.count += int(gpu.size)
+        if not fin.any():
+            return
+        assert np.isfinite(gpu[fin]).all(), f"{self.name}: non-finite GPU value at {where}"
+        d = float(np.abs(gpu[fin] - ref[fin]).max())
+        if d > self.diff:
+            self.diff, self.worst = d, where
+        self.scale = max(self.scale, float(np.abs(ref[fin]).max()))
+
+    def err(self):
+        return self.diff / self.scale if self.scale > 0 else self.diff
+
+    def check(self, tol):
+        e = self.err()
+        say(f"  {self.name}: {e:.2e} over {self.count} entries (largest difference at {self.worst})")
+        assert e <= tol, (self.name, e, self.worst)
+        return e
