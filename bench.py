@@ -6,7 +6,10 @@ One step = dart_chunk_states + dart_sma_fwd over one batch of synthetic input
 (the long-context bf16 forward: b=2, H=24, L=16384, S=256, N=128, P=64 by
 default), inputs resident in HBM before the timed region.  Prints one JSON
 line: whole-job tokens/s, the roofline of the dominant kernel (dart_sma_fwd,
-bound by bf16 MFMA) measured with HIP events on the launch stream, the
+bound by bf16 MFMA) measured with HIP events on the launch stream; beside it
+the other forward workloads (b4 H24 L2048 and b1 H32 L65536), the chunk sizes
+64 and 32 on the headline shape, two matrix-core ceilings (a plain MFMA loop
+and the vendor GEMM), the backward, the normalised and SSM branches, the
 decode call's HBM roofline, and the fp64 oracle timed on a bounded sample on
 the host cores.
 """
@@ -63,6 +66,145 @@ def fwd_flops(cfg):
     products Q dH and C dH, plus 2SNP per chunk memory built (2 N P per token)."""
     b, H, L, S, N, P = (cfg[k] for k in ("batch", "nheads", "seqlen", "chunk", "d_state", "d_head"))
     return 4 * N * P * fwd_pairs(b, H, L, S), 2 * N * P * b * H * L
+
+
+def tile_pairs(b, H, L, S, tile=128):
+    """(token, chunk) products the forward's 128-token tiles compute: every
+    token slot of a tile (padded tail slots included) against every chunk
+    before the chunk of the tile's last token; the products of chunks a token
+    cannot see are computed and masked."""
+    n = 0
+    for t0 in range(0, L, tile):
+        t_last = min(t0 + tile, L) - 1
+        n += tile * (t_last // S)
+    return b * H * n
+
+
+def path_bytes(cfg):
+    """Compulsory HBM bytes of one step (chunk states + forward): X, B, A
+    read and the chunk memories written; Q, C, E, the memories, Y and the gate
+    read and out written."""
+    b, H, G, L, S, N, P = (cfg[k] for k in ("batch", "nheads", "ngroups", "seqlen", "chunk", "d_state", "d_head"))
+    M = -(-L // S)
+    tok_h, tok_g, mem = b * L * H * P * 2, b * L * G * N * 2, b * H * M * N * P * 2
+    return (tok_h + tok_g + b * L * H * 4 + mem) + (2 * tok_g + b * L * G * P * 2 + mem + 3 * tok_h)
+
+
+def time_step(torch, dart, synth, cfg, steps, warmup, sets=1):
+    """Events around dart_chunk_states and dart_sma_fwd of every step on the
+    launch stream; ``sets`` input draws are used in turn (two keep a working
+    set near the last-level cache size from being served from it)."""
+    b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
+    M = dart.num_chunks(L, S)
+    ds = [synth.draw_fwd_torch(**cfg, seed=k) for k in range(sets)]
+    dHs = [torch.empty((b, H, M, cfg["d_head"], cfg["d_state"]), dtype=torch.bfloat16, device="cuda")
+           for _ in range(sets)]
+    outs = [torch.empty_like(d["Y"]) for d in ds]
+
+    def cs(k):
+        d = ds[k % sets]
+        dart.dart_chunk_states(d["X"], d["B"], d["A"], S, dH=dHs[k % sets])
+
+    def fwd(k):
+        d = ds[k % sets]
+        dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dHs[k % sets], d["Y"], d["gate"], S, out=outs[k % sets])
+
+    for k in range(warmup):
+        cs(k)
+        fwd(k)
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record(st)
+        cs(k)
+        ev[k][1].record(st)
+        fwd(k)
+        ev[k][2].record(st)
+    torch.cuda.synchronize()
+    t_cs = sum(e[0].elapsed_time(e[1]) for e in ev) / steps / 1e3
+    t_fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps / 1e3
+    del ds, dHs, outs
+    torch.cuda.empty_cache()
+    return t_cs, t_fwd
+
+
+def step_record(cfg, t_cs, t_fwd):
+    b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
+    f_sma, f_cs = fwd_flops(cfg)
+    nbytes = path_bytes(cfg)
+    return {"workload": cfg["name"], "tokens_per_s": b * L / (t_cs + t_fwd),
+            "us_chunk_states": t_cs * 1e6, "us_sma_fwd": t_fwd * 1e6,
+            "sma_fwd_TFLOPs": f_sma / t_fwd / 1e12, "sma_fwd_frac": f_sma / t_fwd / 1e12 / PEAK_BF16_TFLOPS,
+            "path_mfma_frac": (f_sma + f_cs) / (t_cs + t_fwd) / 1e12 / PEAK_BF16_TFLOPS,
+            "path_bytes": nbytes, "path_GBs": nbytes / (t_cs + t_fwd) / 1e9,
+            "path_hbm_frac": nbytes / (t_cs + t_fwd) / 1e9 / PEAK_HBM_GBS}
+
+
+def time_configs(torch, dart, synth, steps, warmup, skip):
+    """The other forward workloads in the same run: the single-layer block
+    (b4 H24 L2048, HBM-bound: both fractions reported; two input sets in
+    turn, since its 0.3 GB working set is near the 256 MB last-level cache)
+    and the very long context (b1 H32 L65536), each with the step's
+    tokens/s and the forward's and the path's bf16 MFMA fractions."""
+    res = {}
+    for ci in (1, 2, 3):
+        if ci == skip:
+            continue
+        cfg = dict(synth.CONFIGS[ci])
+        t_cs, t_fwd = time_step(torch, dart, synth, cfg, steps, warmup, sets=2 if ci == 1 else 1)
+        rec = step_record(cfg, t_cs, t_fwd)
+        rec["traffic_sma_fwd"] = traffic_record("sma_fwd", cfg["name"])
+        res[cfg["name"]] = rec
+    return res
+
+
+def time_chunk_sizes(torch, dart, synth, steps, warmup):
+    """The evaluation-time chunk sizes on the long-context shape (b2 H24
+    L16384): the same step at S = 64 and S = 32.  Pairs, and so algorithmic
+    flops, grow as 1/S; a 128-token tile then spans 2 or 4 chunks and also
+    computes (and masks) the products of the chunks its earlier tokens cannot
+    see, which ``masked_frac`` counts."""
+    res = {}
+    for S in (64, 32):
+        cfg = dict(synth.CONFIGS[2], chunk=S, name=f"long_bf16_b2_h24_L16384_S{S}")
+        b, H, L = cfg["batch"], cfg["nheads"], cfg["seqlen"]
+        t_cs, t_fwd = time_step(torch, dart, synth, cfg, steps, warmup)
+        rec = step_record(cfg, t_cs, t_fwd)
+        alg, done = fwd_pairs(b, H, L, S), tile_pairs(b, H, L, S)
+        rec.update(pairs=alg, computed_pairs=done, masked_frac=1 - alg / done)
+        res[f"S{S}"] = rec
+    return res
+
+
+def time_gemm_probe(torch, steps, warmup, fwd_tflops):
+    """An independent matrix-core ceiling: the vendor bf16 GEMM behind
+    torch.matmul, (8192 x 6144) @ (6144 x 8192) with float32 accumulation
+    (8.2e11 flop, about one forward launch), contiguous operands drawn
+    N(0, 1), timed with events on the same stream."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    M_, K_, N_ = 8192, 6144, 8192
+    a = torch.randn((M_, K_), generator=gen, device="cuda").to(torch.bfloat16)
+    bm = torch.randn((K_, N_), generator=gen, device="cuda").to(torch.bfloat16)
+    c = torch.empty((M_, N_), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        torch.matmul(a, bm, out=c)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        torch.matmul(a, bm, out=c)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    flop = 2 * M_ * K_ * N_
+    tflops = flop / t / 1e12
+    del a, bm, c
+    torch.cuda.empty_cache()
+    return {"shape": [M_, K_, N_], "flop_per_call": flop, "us_per_call": t * 1e6, "achieved_TFLOPs": tflops,
+            "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "fwd_frac_of_gemm": fwd_tflops / tflops}
 
 
 def time_backward(torch, dart, synth, cfg, steps=5, warmup=1):
@@ -215,13 +357,18 @@ def traffic_record(kernel, workload, sources=None):
     return rec.get("hbm_bytes_per_launch")
 
 
-def blas_threads():
+def blas_info():
+    """BLAS library and thread count numpy uses, from threadpoolctl."""
     try:
         from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:
-        return 1
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if not libs:
+            return {"threads": 1, "backend": "none found"}
+        top = max(libs, key=lambda i: i.get("num_threads", 1))
+        return {"threads": int(top.get("num_threads", 1)),
+                "backend": f"{top.get('internal_api')} {top.get('version')} ({os.path.basename(top.get('filepath', ''))})"}
+    except Exception as exc:  # threadpoolctl missing or failing: report that
+        return {"threads": 1, "backend": f"unknown ({exc.__class__.__name__})"}
 
 
 def cpu_baseline(cfg, budget_s=12.0):
@@ -245,7 +392,12 @@ def cpu_baseline(cfg, budget_s=12.0):
         heads += 1
     # the full workload is batch * nheads such head-sequences of L tokens each
     value = heads * cfg["seqlen"] / (t_total * cfg["nheads"])
-    return {"value": value, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+    blas = blas_info()
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+           if k in os.environ}
+    return {"value": value, "unit": "tokens/s", "cores": blas["threads"], "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "host_affinity_cores": len(os.sched_getaffinity(0)),
+            "blas": blas["backend"], "thread_env": env,
             "sample": f"{heads} whole head-sequence(s) of the same workload (L={cfg['seqlen']}, "
                       f"S={cfg['chunk']}, N={cfg['d_state']}, P={cfg['d_head']}), chunk states + SMA + "
                       f"gated residual in fp64 numpy, {t_total:.1f} s; scaled by heads/(batch*nheads)"}
@@ -427,6 +579,16 @@ def profile_kernels(launches=3):
                 assert probe.dart_probe_mfma(ops.data_ptr(), 512, 400, sink.data_ptr(), stream) == 0
             torch.cuda.synchronize()
             del ops, sink
+            # the vendor GEMM of time_gemm_probe
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(5)
+            ga = torch.randn((8192, 6144), generator=gen, device="cuda").to(torch.bfloat16)
+            gb = torch.randn((6144, 8192), generator=gen, device="cuda").to(torch.bfloat16)
+            gc = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+            for _ in range(launches):
+                torch.matmul(ga, gb, out=gc)
+            torch.cuda.synchronize()
+            del ga, gb, gc
         del d, dH, out
         torch.cuda.empty_cache()
     cfg = dict(synth.CONFIGS[4])
@@ -553,6 +715,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-rms", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads and the S = 64 / 32 variants")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run each hot kernel a few times for a hardware-counter pass, then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -631,6 +795,10 @@ def main():
     result["mfma_probe"] = time_mfma_probe(torch, dH, d["Q"], args.steps, args.warmup, achieved)
     del d, dH, out
     torch.cuda.empty_cache()
+    result["gemm_probe"] = time_gemm_probe(torch, args.steps, args.warmup, achieved)
+    if not args.no_configs:
+        result["configs"] = time_configs(torch, dart, synth, args.steps, args.warmup, args.config)
+        result["chunk_sizes"] = time_chunk_sizes(torch, dart, synth, args.steps, args.warmup)
     if not args.no_rms:
         result["rms"] = time_rms(torch, dart, synth, cfg)
     if not args.no_ssd:
