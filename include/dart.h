@@ -151,6 +151,27 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
  * (0 on invalid dims; dtype does not matter). */
 size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chunks);
 
+/* dart_sma_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, results and kernels, without the workspace.  The
+ * split partials go to a scratch array of DART_DECODE_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends (its device
+ * address is looked up once per device, on the first call there).  The call
+ * allocates and frees nothing.
+ *   Limit: dart_sma_decode_workspace_bytes(dims, max_chunks) must not exceed
+ *   DART_DECODE_SCRATCH_BYTES (4 MiB: b * H up to about 15800 rows and heads
+ *   at P = 64); larger problems fail with DART_ERR_WORKSPACE before any HIP
+ *   call.
+ *   Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ *   that may overlap on one GPU (different streams, or threads without
+ *   ordering between them) race; order them on one stream or use
+ *   dart_sma_decode with a workspace each. */
+#define DART_DECODE_SCRATCH_BYTES ((size_t)4 << 20)
+int dart_sma_decode_noalloc(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                            const void* c, const void* e, const void* cache, const int32_t* n_chunks,
+                            const void* y_ssm, const void* gate, int gate_per_channel, void* out,
+                            float* R, float* lse, void* stream);
+
 /* Decode-side cache maintenance, one new token per batch row [§2 Eq. 2
  * restricted to the current chunk; §3 Eq. 5 / App. A Eq. 20; §4 "Inference
  * Cache"].  For the token at absolute position pos[b] (chunk size S =

@@ -344,12 +344,14 @@ size_t dart_sma_decode_workspace_bytes(const dart_dims_t* dims, int64_t max_chun
 
 namespace {
 
-// dart_sma_decode and dart_sma_decode_rms (rms: r_cache and the weights).
+// dart_sma_decode, dart_sma_decode_rms (rms: r_cache and the weights) and
+// dart_sma_decode_noalloc (noalloc: the library's scratch instead of the
+// caller's workspace).
 int sma_decode_impl(const dart_dims_t* dims, int dtype, int64_t max_chunks, bool rms, float eps,
                     const void* q, const void* c, const void* e, const void* cache, const float* r_cache,
                     const int32_t* n_chunks, const float* w_q, const float* w_e, const void* y_ssm,
                     const void* gate, int gate_per_channel, void* out, float* R, float* lse, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool noalloc = false) {
   t_err[0] = '\0';
   int st = check_dims(dims, dtype, false);
   if (st) return st;
@@ -386,14 +388,26 @@ int sma_decode_impl(const dart_dims_t* dims, int dtype, int64_t max_chunks, bool
   if ((st = check_opt_align(cache, "cache")) || (st = check_opt_align(R, "R")) ||
       (st = check_opt_align(lse, "lse")) || (st = check_opt_align(n_chunks, "n_chunks")))
     return st;
-  if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
-    return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
-                plan.workspace_bytes);
-  if ((st = check_opt_align(workspace, "workspace"))) return st;
+  if (noalloc) {
+    if (plan.workspace_bytes > DART_DECODE_SCRATCH_BYTES)
+      return fail(DART_ERR_WORKSPACE, "the split partials need %zu bytes, more than the %zu-byte scratch of "
+                  "dart_sma_decode_noalloc; use dart_sma_decode with a workspace", plan.workspace_bytes,
+                  (size_t)DART_DECODE_SCRATCH_BYTES);
+  } else {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+      return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                  plan.workspace_bytes);
+    if ((st = check_opt_align(workspace, "workspace"))) return st;
+  }
   const Buf bn{n_chunks, s.b * 4, "n_chunks"};
   if ((st = check_alias({bo, br, bl, bw}, {bq, bc, be, bk, by, bg, bn, brc, bwq, bwe}, out, y_ssm))) return st;
   if (prod({s.b, s.H, plan.splits}) >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "b * H is too large for one launch");
+  if (noalloc) {
+    float* scratch = nullptr;
+    if ((st = hip_status(dart::decode_scratch(&scratch), "dart_sma_decode_noalloc scratch"))) return st;
+    workspace = scratch;
+  }
   hipStream_t strm = (hipStream_t)stream;
   if (rms && use_mfma(dtype, dims))
     return hip_status(dart::launch_sma_decode_mfma(s, max_chunks, plan, q, c, e, cache, n_chunks, y_ssm, gate,
@@ -426,6 +440,14 @@ int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, cons
   return sma_decode_impl(dims, dtype, max_chunks, false, 0.f, q, c, e, cache, nullptr, n_chunks, nullptr,
                          nullptr, y_ssm, gate, gate_per_channel, out, R, lse, workspace, workspace_bytes,
                          stream);
+}
+
+int dart_sma_decode_noalloc(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
+                            const void* c, const void* e, const void* cache, const int32_t* n_chunks,
+                            const void* y_ssm, const void* gate, int gate_per_channel, void* out,
+                            float* R, float* lse, void* stream) {
+  return sma_decode_impl(dims, dtype, max_chunks, false, 0.f, q, c, e, cache, nullptr, n_chunks, nullptr,
+                         nullptr, y_ssm, gate, gate_per_channel, out, R, lse, nullptr, 0, stream, true);
 }
 
 int dart_sma_decode_rms(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,

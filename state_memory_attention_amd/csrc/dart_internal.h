@@ -114,6 +114,10 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 DecodePlan decode_plan(int64_t b, int64_t H, int64_t P, int64_t max_chunks);
+// Device address, on the current device, of the library's decode scratch
+// (DART_DECODE_SCRATCH_BYTES per GPU, for dart_sma_decode_noalloc); looked up
+// once per device.
+hipError_t decode_scratch(float** ptr);
 // r_cache non-null selects the RMS-normalised score branch (weights nullable)
 hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const DecodePlan& plan,
                                   const void* q, const void* c, const void* e, const void* cache,

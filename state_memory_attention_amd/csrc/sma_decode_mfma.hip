@@ -25,6 +25,9 @@
 // (row 2), so W = row 0 + row 2 of the product carries ~16 mantissa bits of
 // the scaled query; the two extra rows cost nothing on the 16-row matrix op.
 // RMSNorm(e) w_e and the per-token scales are folded into e once.
+#include <mutex>
+
+#include "dart.h"
 #include "dart_internal.h"
 #include "dev_common.h"
 
@@ -274,6 +277,37 @@ DecodePlan decode_plan(int64_t b, int64_t H, int64_t P, int64_t max_chunks) {
   plan.chunks_per_split = cps;
   plan.workspace_bytes = (size_t)(bh * splits * (P + 2)) * sizeof(float);
   return plan;
+}
+
+// Split partials of dart_sma_decode_noalloc.  Each GPU holds its own copy of
+// this array until the process ends.  In host code its name is a host-side
+// stand-in, not a device address: host code uses only the address that
+// hipGetSymbolAddress returns for the current device (decode_scratch below).
+// The partials need no clearing: the combine kernel reads only the ranges
+// whose blocks wrote them in the same call.
+static __device__ __align__(256) float scratch[DART_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = (float*)p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const DecodePlan& plan,

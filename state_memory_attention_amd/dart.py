@@ -28,7 +28,7 @@ STATUS = {0: "DART_OK", -1: "DART_ERR_NULL", -2: "DART_ERR_SHAPE", -3: "DART_ERR
           -4: "DART_ERR_WORKSPACE", -5: "DART_ERR_HIP", -6: "DART_ERR_ALIGN"}
 
 ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
-                "dart_sma_decode_workspace_bytes", "dart_sma_bwd", "dart_sma_bwd_workspace_bytes",
+                "dart_sma_decode_workspace_bytes", "dart_sma_decode_noalloc", "dart_sma_bwd", "dart_sma_bwd_workspace_bytes",
                 "dart_chunk_states_bwd", "dart_chunk_states_bwd_workspace_bytes",
                 "dart_decode_state_update",
                 "dart_chunk_states_rms", "dart_chunk_rms", "dart_sma_fwd_rms", "dart_sma_decode_rms",
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.dart_sma_decode.restype = i32
     L.dart_sma_decode_workspace_bytes.argtypes = [dp, i64]
     L.dart_sma_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.dart_sma_decode_noalloc.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    L.dart_sma_decode_noalloc.restype = i32
     L.dart_sma_bwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, ctypes.c_size_t, vp]
     L.dart_sma_bwd.restype = i32
@@ -220,13 +222,8 @@ def decode_workspace_bytes(batch: int, nheads: int, d_head: int, max_chunks: int
     return int(lib().dart_sma_decode_workspace_bytes(ctypes.byref(dims), max_chunks))
 
 
-def dart_sma_decode(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: torch.Tensor,
-                    y: torch.Tensor, gate: torch.Tensor, n_chunks: Optional[torch.Tensor] = None,
-                    out: Optional[torch.Tensor] = None, R: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    want_R: bool = False, want_lse: bool = False):
-    """Decode one new token per batch row against cache (b, H, Mmax, P, N).
-    Returns (out, R, lse)."""
+def _decode_args(q, c, e, cache, y, gate, n_chunks, out, R, lse, want_R, want_lse):
+    """Shape checks and output allocation shared by the decode wrappers."""
     b, G, N = q.shape
     H, Mx, P = cache.shape[1], cache.shape[2], cache.shape[3]
     dev, dt = q.device, q.dtype
@@ -245,7 +242,32 @@ def dart_sma_decode(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: to
         R = torch.empty((b, H, P), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((b, H), dtype=torch.float32, device=dev)
-    dims = Dims(b, 1, H, G, N, P, 1)
+    return Dims(b, 1, H, G, N, P, 1), Mx, gpc, out, R, lse
+
+
+def dart_sma_decode_noalloc(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: torch.Tensor,
+                            y: torch.Tensor, gate: torch.Tensor, n_chunks: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, R: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, want_R: bool = False, want_lse: bool = False):
+    """dart_sma_decode without a workspace: the library's own per-GPU scratch
+    holds the split partials (the C call allocates nothing; pass out, R and
+    lse to allocate nothing here either).  Returns (out, R, lse)."""
+    dims, Mx, gpc, out, R, lse = _decode_args(q, c, e, cache, y, gate, n_chunks, out, R, lse, want_R, want_lse)
+    _check(lib().dart_sma_decode_noalloc(ctypes.byref(dims), _code(q.dtype), Mx, _ptr(q), _ptr(c), _ptr(e),
+                                         _ptr(cache), _ptr(n_chunks), _ptr(y), _ptr(gate), int(gpc),
+                                         _ptr(out), _ptr(R), _ptr(lse), _stream(q)))
+    return out, R, lse
+
+
+def dart_sma_decode(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: torch.Tensor,
+                    y: torch.Tensor, gate: torch.Tensor, n_chunks: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, R: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    want_R: bool = False, want_lse: bool = False):
+    """Decode one new token per batch row against cache (b, H, Mmax, P, N).
+    Returns (out, R, lse)."""
+    dims, Mx, gpc, out, R, lse = _decode_args(q, c, e, cache, y, gate, n_chunks, out, R, lse, want_R, want_lse)
+    dev, dt = q.device, q.dtype
     need = int(lib().dart_sma_decode_workspace_bytes(ctypes.byref(dims), Mx))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

@@ -126,6 +126,29 @@ def test_decode_validation():
     assert dec(d, n_chunks=ctypes.c_void_p((11 << 40) + 2)) == -6
 
 
+def dec_noalloc(d, max_chunks=8, dtype=1, cache=ADDR[3], out=ADDR[6]):
+    return D.lib().dart_sma_decode_noalloc(ctypes.byref(d), dtype, max_chunks, ADDR[0], ADDR[1], ADDR[2],
+                                           cache, None, ADDR[4], ADDR[5], 1, out, None, None, None)
+
+
+def test_decode_noalloc_validation():
+    """Every failing case returns before any HIP call: bad arguments, and
+    split partials larger than the library's scratch."""
+    d = dims()
+    assert dec_noalloc(d, max_chunks=-1) == -2
+    assert dec_noalloc(d, cache=None) == -1 and "cache" in last()
+    assert dec_noalloc(d, out=ctypes.c_void_p((12 << 40) + 8)) == -6 and "out" in last()
+    assert dec_noalloc(dims(b=0)) == 0
+    # b * H = 32768 rows and heads need 32768 * 66 * 4 bytes of partials: over the 4 MiB scratch
+    big = dims(b=1024, H=32, G=32)
+    need = D.lib().dart_sma_decode_workspace_bytes(ctypes.byref(big), 256)
+    assert need > 4 << 20
+    assert dec_noalloc(big, max_chunks=256) == -4 and "scratch" in last()
+    # the largest problem that fits is checked against the same limit the header states
+    text = open(HEADER).read()
+    assert "DART_DECODE_SCRATCH_BYTES ((size_t)4 << 20)" in text
+
+
 def test_decode_workspace_size_function():
     f = D.lib().dart_sma_decode_workspace_bytes
     d = dims(b=64, H=24)
