@@ -336,6 +336,18 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
   const int64_t orow = (row0 + tc) * a.H + h;
   const float gs = a.gate_pc ? 0.f : bf16_to_f32(a.gate[orow]);
   float* rp = (a.R && tok_ok) ? a.R + orow * kP + 4 * half : nullptr;
+  // every Y and gate read is issued before the first use (a per-step branch
+  // on the gate form made each read wait for itself); with a scalar gate the
+  // gate slot holds a zero-length stand-in whose bytes are read and ignored
+  uint2 yv[2][4], gv[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const uint32_t lo = tr * 128 + (((4 * rb + gq) ^ (tr & 7)) << 4) + 8 * half;
+      yv[rb][gq] = *(const uint2*)(ybuf + lo);
+      gv[rb][gq] = *(const uint2*)(gbuf + lo);
+    }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -343,15 +355,12 @@ void sma_fwd_mfma_kernel(FwdArgs a) {
       const uint32_t lo = tr * 128 + (((4 * rb + gq) ^ (tr & 7)) << 4) + 8 * half;
       const float r0 = o[rb][4 * gq + 0] * inv, r1 = o[rb][4 * gq + 1] * inv;
       const float r2 = o[rb][4 * gq + 2] * inv, r3 = o[rb][4 * gq + 3] * inv;
-      const uint2 yv = *(const uint2*)(ybuf + lo);
-      float g0 = gs, g1 = gs, g2 = gs, g3 = gs;
-      if (a.gate_pc) {
-        const uint2 gv = *(const uint2*)(gbuf + lo);
-        g0 = bf16lo(gv.x); g1 = bf16hi(gv.x); g2 = bf16lo(gv.y); g3 = bf16hi(gv.y);
-      }
+      const uint2 y = yv[rb][gq], g = gv[rb][gq];
+      const float g0 = a.gate_pc ? bf16lo(g.x) : gs, g1 = a.gate_pc ? bf16hi(g.x) : gs;
+      const float g2 = a.gate_pc ? bf16lo(g.y) : gs, g3 = a.gate_pc ? bf16hi(g.y) : gs;
       uint2 ov;
-      ov.x = pack_bf16x2(fmaf(g0, r0, bf16lo(yv.x)), fmaf(g1, r1, bf16hi(yv.x)));
-      ov.y = pack_bf16x2(fmaf(g2, r2, bf16lo(yv.y)), fmaf(g3, r3, bf16hi(yv.y)));
+      ov.x = pack_bf16x2(fmaf(g0, r0, bf16lo(y.x)), fmaf(g1, r1, bf16hi(y.x)));
+      ov.y = pack_bf16x2(fmaf(g2, r2, bf16lo(y.y)), fmaf(g3, r3, bf16hi(y.y)));
       *(uint2*)(s_y + lo) = ov;
       if (rp) *(float4*)(rp + 32 * rb + 8 * gq) = make_float4(r0, r1, r2, r3);
     }
