@@ -79,6 +79,9 @@ __all__ = [
     "sma_head_rms",
     "sma_forward_rms",
     "sma_decode_rms",
+    "rms_norm_backward",
+    "sma_head_backward_rms",
+    "sma_backward_rms",
     "ssm_output_head",
     "ssd_chunked_head",
     "ssm_output",
@@ -602,6 +605,111 @@ def sma_forward_rms(Q, C, E, dH, S: int, eps: float, wq=None, we=None):
             R[bi, :, h], lse[bi, h] = sma_head_rms(Q[bi, :, g], C[bi, :, g], E[bi, :, g], dH[bi, h], S,
                                                    eps, wq, we)
     return R, lse
+
+
+def rms_norm_backward(x, eps: float, dy_hat):
+    """Gradient of z = x / sqrt(mean(x^2) + eps) for a gradient dy_hat on z
+    (over the last axis of size D):  with rho = (mean(x^2) + eps)^(-1/2),
+    dz_i/dx_j = rho delta_ij - rho^3 x_i x_j / D, so
+        dx = rho dy_hat - rho^3 x (x . dy_hat) / D."""
+    x, g = _f64(x), _f64(dy_hat)
+    D = x.shape[-1]
+    rho = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return rho * g - rho ** 3 * x * (x * g).sum(axis=-1, keepdims=True) / D
+
+
+def sma_head_backward_rms(Q, C, E, dH, S: int, eps: float, dR, lse=None, wq=None, we=None):
+    """Gradients of the normalised score branch of one head  [App. B.1
+    Eq. 25-27 with §3 Eq. 8-10, differentiated]; training recomputes the
+    logits and takes the weights as p = exp(l - lse) [App. C Eq. 33-35].
+
+    Forward (as ``sma_head_rms``): qn = RMSNorm(Q_t) * wq, en = RMSNorm(E_t) * we,
+    r_c = inverse RMS of dH_c along P, S_c = diag(r_c) dH_c,
+    l_tc = qn S_c en / sqrt(N), V_tc = C_t dH_c, R_t = sum_c softmax(l)_c V_tc.
+
+    Backward for dR = dLoss/dR:
+        dl_tc = p_tc (dR_t . V_tc - dR_t . R_t)           (softmax, as the plain branch)
+        d qn_t = sum_c dl_tc S_c en_t / sqrt(N)
+        d en_t = sum_c dl_tc S_c^T qn_t / sqrt(N)
+        dS_c   = sum_t dl_tc qn_t^T en_t / sqrt(N)
+        d dH_c = sum_t p_tc C_t^T dR_t                     (value readout)
+               + r_c * dS_c - (r_c^3 / P) * dH_c * rowsum_p(dS_c * dH_c)   (through S_c and r_c)
+        dC_t   = sum_c p_tc dH_c dR_t
+        dQ_t   = RMSNorm backward of Q_t for d qn_t * wq, dwq = sum_t d qn_t * z_q,t
+        dE_t   = RMSNorm backward of E_t for d en_t * we, dwe = sum_t d en_t * z_e,t
+    with z the RMSNorm outputs before the weights.  Q, C (L, N), E (L, P),
+    dH (M, N, P), dR (L, P) -> dQ, dC (L, N), dE (L, P), d_dH (M, N, P),
+    dwq (N,), dwe (P,) (zeros where no weight is given).  ``lse`` defaults to
+    the forward's."""
+    Q, C, E, dH, dR = _f64(Q), _f64(C), _f64(E), _f64(dH), _f64(dR)
+    L, N = Q.shape
+    P = E.shape[1]
+    M = num_chunks(L, S)
+    wq_ = np.ones(N) if wq is None else _f64(wq)
+    we_ = np.ones(P) if we is None else _f64(we)
+    if lse is None:
+        _, lse = sma_head_rms(Q, C, E, dH, S, eps, wq, we)
+    lse = _f64(lse)
+    scale = 1.0 / math.sqrt(N)
+    Zq, Ze = rms_norm(Q, eps), rms_norm(E, eps)              # [Eq. 25] before the weights
+    Qn, En = Zq * wq_, Ze * we_
+    r = chunk_inv_rms(dH, eps)                               # (M, N)  [Eq. 26]
+    Sm = r[:, :, None] * dH                                  # S_c = diag(r_c) dH_c
+    dQn, dC, dEn = np.zeros((L, N)), np.zeros((L, N)), np.zeros((L, P))
+    dS, ddH = np.zeros((M, N, P)), np.zeros((M, N, P))
+    for i in range(1, M):
+        s0, s1 = chunk_bounds(i, L, S)
+        hist, shist = dH[:i], Sm[:i]
+        V = np.einsum("tn,cnp->tcp", C[s0:s1], hist, optimize=True)          # C_t dH_c
+        K = np.einsum("cnp,tp->tcn", shist, En[s0:s1], optimize=True)        # S_c en_t
+        logits = np.einsum("tn,tcn->tc", Qn[s0:s1], K) * scale               # [Eq. 27]
+        p = np.exp(logits - lse[s0:s1, None])                                # [App. C Eq. 35]
+        g = dR[s0:s1]
+        dp = np.einsum("tp,tcp->tc", g, V)
+        dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        G = np.einsum("cnp,tp->tcn", hist, g, optimize=True)                 # dH_c dR_t
+        dC[s0:s1] = np.einsum("tc,tcn->tn", p, G)
+        dQn[s0:s1] = np.einsum("tc,tcn->tn", dl, K) * scale
+        W = np.einsum("tn,cnp->tcp", Qn[s0:s1], shist, optimize=True)        # qn_t S_c
+        dEn[s0:s1] = np.einsum("tc,tcp->tp", dl, W) * scale
+        pC = p[:, :, None] * C[s0:s1, None, :]
+        dlQ = dl[:, :, None] * Qn[s0:s1, None, :]
+        ddH[:i] += np.einsum("tcn,tp->cnp", pC, g, optimize=True)
+        dS[:i] += np.einsum("tcn,tp->cnp", dlQ, En[s0:s1], optimize=True) * scale
+    # through S_c = diag(r_c) dH_c and r_c = (mean_p dH_c^2 + eps)^(-1/2)
+    ddH += r[:, :, None] * dS - (r ** 3 / P)[:, :, None] * dH * (dS * dH).sum(axis=2, keepdims=True)
+    dQ = rms_norm_backward(Q, eps, dQn * wq_)
+    dE = rms_norm_backward(E, eps, dEn * we_)
+    dwq = (dQn * Zq).sum(axis=0) if wq is not None else np.zeros(N)
+    dwe = (dEn * Ze).sum(axis=0) if we is not None else np.zeros(P)
+    return dQ, dC, dE, ddH, dwq, dwe
+
+
+def sma_backward_rms(Q, C, E, dH, S: int, eps: float, dR, lse=None, wq=None, we=None):
+    """Batched sma_head_backward_rms (layouts as ``sma_backward``): gradients
+    of projections shared by a group are summed over its heads, and dwq, dwe
+    over every batch row and head."""
+    Q, C, E, dR = _f64(Q), _f64(C), _f64(E), _f64(dR)
+    b, L, G, N = Q.shape
+    H = dH.shape[1]
+    P = E.shape[3]
+    hpg = H // G
+    dQ, dC, dE = np.zeros_like(Q), np.zeros_like(C), np.zeros_like(E)
+    ddH = np.zeros(dH.shape)
+    dwq, dwe = np.zeros(N), np.zeros(P)
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            q, c, e, dd, wqg, weg = sma_head_backward_rms(
+                Q[bi, :, g], C[bi, :, g], E[bi, :, g], dH[bi, h], S, eps, dR[bi, :, h],
+                None if lse is None else lse[bi, h], wq, we)
+            dQ[bi, :, g] += q
+            dC[bi, :, g] += c
+            dE[bi, :, g] += e
+            ddH[bi, h] = dd
+            dwq += wqg
+            dwe += weg
+    return dQ, dC, dE, ddH, dwq, dwe
 
 
 def sma_decode_rms(q, c, e, cache, n_chunks, eps: float, hpg: int = 1, wq=None, we=None):
