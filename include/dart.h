@@ -294,6 +294,40 @@ int dart_decode_state_update_rms(const dart_dims_t* dims, int dtype, int64_t max
                                  const int32_t* pos, void* cache, float* r_cache, int32_t* n_chunks,
                                  void* stream);
 
+/* Backward of the normalised score branch with the gated residual [App. B.1
+ * Eq. 25-27 differentiated; §4 "Efficient Training"; App. C Eq. 33-35].  The
+ * logits are recomputed from dH_score exactly as dart_sma_fwd_rms forms them,
+ * p = exp(l - lse), and with dR_t = g_t * dout_t, D_t = dR_t . R_t,
+ * qn = RMSNorm(Q_t) (weighted), en = RMSNorm(E_t) (weighted):
+ *   dl     = p (dR_t . V_tc - D_t)                     (as dart_sma_bwd)
+ *   dqn_t  = sum_c dl r_c * (dH_c en_t) / sqrt(N)
+ *   den_t  = sum_c dl dH_c^T (r_c * qn_t) / sqrt(N)
+ *   dC_t   = sum_c p dH_c dR_t
+ *   dS_c   = sum_t dl qn_t en_t^T / sqrt(N)
+ *   d_dH_c = sum_t p C_t^T dR_t + r_c * dS_c - (r_c^3 / P) dH_c * sum_p (dS_c * dH_c)
+ *   dQ_t, dE_t: the RMSNorm backward of dqn_t * w_q, den_t * w_e,
+ *   dw_q = sum over tokens and heads of dqn_t * Q_t / rms(Q_t)   (dw_e alike),
+ * with r_c recomputed from dH as stored.
+ *   Inputs: the forward's Q, C, E, dH, dH_score (from dart_chunk_states_rms
+ *           or dart_chunk_rms with the same w_q, w_e, eps), gate, its outputs
+ *           R and lse (float32), dout (dtype); eps and the RMSNorm weights
+ *           w_q [N], w_e [P] (float32, NULL = 1, 4-byte alignment).
+ *   Outputs, float32, fully overwritten: dQ, dC, dE, d_dH and dgate as for
+ *           dart_sma_bwd; dw_q [N] and dw_e [P], each the gradient with
+ *           respect to the weight at its value (1 where w_q or w_e is NULL);
+ *           NULL skips dgate, dw_q or dw_e.  4-byte alignment for dw_q, dw_e.
+ *   workspace: at least dart_sma_bwd_rms_workspace_bytes() bytes, 16-byte
+ *           aligned; contents on entry are ignored.
+ * Every result is deterministic: sums over heads, tokens and chunks run in a
+ * fixed order. */
+int dart_sma_bwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const void* C,
+                     const void* E, const void* dH, const void* dH_score, const void* gate,
+                     int gate_per_channel, float eps, const float* w_q, const float* w_e,
+                     const float* R, const float* lse, const void* dout, float* dQ, float* dC,
+                     float* dE, float* d_dH, float* dgate, float* dw_q, float* dw_e,
+                     void* workspace, size_t workspace_bytes, void* stream);
+size_t dart_sma_bwd_rms_workspace_bytes(const dart_dims_t* dims);
+
 /* The SSM branch of the block by the Mamba-2 chunked scan [§2 Eq. 2; App. A
  * Eq. 15-24]:  Y_t = C_t H_t,  H_t = a_t H_{t-1} + B_t^T X_t,  H_{-1} = H0,
  * computed per chunk c as the chunk state memory dH_[c] (Eq. 20, exactly

@@ -625,6 +625,70 @@ int dart_sma_bwd(const dart_dims_t* dims, int dtype, const void* Q, const void* 
                     "dart_sma_bwd");
 }
 
+size_t dart_sma_bwd_rms_workspace_bytes(const dart_dims_t* dims) {
+  t_err[0] = '\0';
+  if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;
+  const dart::Shape s = make_shape(dims);
+  if (prod({2, s.b, s.H, s.M, s.L}) < 0 || prod({3, s.b, s.L, s.H, s.N + s.P}) < 0 ||
+      prod({2, s.b, s.H, s.M, s.P, s.N}) < 0)
+    return 0;
+  return dart::sma_bwd_rms_workspace_bytes(s);
+}
+
+int dart_sma_bwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const void* C,
+                     const void* E, const void* dH, const void* dH_score, const void* gate,
+                     int gate_per_channel, float eps, const float* w_q, const float* w_e,
+                     const float* R, const float* lse, const void* dout, float* dQ, float* dC,
+                     float* dE, float* d_dH, float* dgate, float* dw_q, float* dw_e,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  t_err[0] = '\0';
+  int st = check_dims(dims, dtype, true);
+  if (st) return st;
+  if (!(eps >= 0.f && eps < INFINITY)) return fail(DART_ERR_SHAPE, "eps must be finite and >= 0");
+  const dart::Shape s = make_shape(dims);
+  if (s.b == 0 || s.L == 0) return DART_OK;
+  const int64_t es = dtype == DART_BF16 ? 2 : 4;
+  const int gpc = gate_per_channel ? 1 : 0;
+  const Buf bq{Q, prod({s.b, s.L, s.G, s.N}) * es, "Q"};
+  const Buf bc{C, prod({s.b, s.L, s.G, s.N}) * es, "C"};
+  const Buf be{E, prod({s.b, s.L, s.G, s.P}) * es, "E"};
+  const Buf bd{dH, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH"};
+  const Buf bs{dH_score, prod({s.b, s.H, s.M, s.P, s.N}) * es, "dH_score"};
+  const Buf bg{gate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * es, "gate"};
+  const Buf bwq{w_q, s.N * 4, "w_q"};
+  const Buf bwe{w_e, s.P * 4, "w_e"};
+  const Buf br{R, prod({s.b, s.L, s.H, s.P}) * 4, "R"};
+  const Buf bl{lse, prod({s.b, s.H, s.L}) * 4, "lse"};
+  const Buf bo{dout, prod({s.b, s.L, s.H, s.P}) * es, "dout"};
+  const Buf gq{dQ, prod({s.b, s.L, s.G, s.N}) * 4, "dQ"};
+  const Buf gc{dC, prod({s.b, s.L, s.G, s.N}) * 4, "dC"};
+  const Buf ge{dE, prod({s.b, s.L, s.G, s.P}) * 4, "dE"};
+  const Buf gd{d_dH, prod({s.b, s.H, s.M, s.P, s.N}) * 4, "d_dH"};
+  const Buf gg{dgate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * 4, "dgate"};
+  const Buf gwq{dw_q, s.N * 4, "dw_q"};
+  const Buf gwe{dw_e, s.P * 4, "dw_e"};
+  const size_t need = dart::sma_bwd_rms_workspace_bytes(s);
+  const Buf bw{workspace, (int64_t)need, "workspace"};
+  if ((st = check_ptrs({bq, bc, be, bd, bs, bg, br, bl, bo, gq, gc, ge, gd}))) return st;
+  if ((st = check_opt_align(dgate, "dgate"))) return st;
+  if ((st = check_weight(w_q, "w_q")) || (st = check_weight(w_e, "w_e")) || (st = check_weight(dw_q, "dw_q")) ||
+      (st = check_weight(dw_e, "dw_e")))
+    return st;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DART_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((st = check_opt_align(workspace, "workspace"))) return st;
+  if ((st = check_alias({gq, gc, ge, gd, gg, gwq, gwe, bw}, {bq, bc, be, bd, bs, bg, bwq, bwe, br, bl, bo},
+                        nullptr, nullptr)))
+    return st;
+  if (prod({s.b, s.H, s.M, (s.N * s.P + 255) / 256}) >= kMaxIndex || prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex ||
+      prod({s.b, s.H, s.M, s.N}) / 256 >= kMaxIndex || prod({s.b, s.L, s.G}) / 4 >= kMaxIndex)
+    return fail(DART_ERR_SHAPE, "b * H * M or b * H * L is too large for one launch");
+  return hip_status(dart::launch_sma_bwd_rms_general(s, dtype == DART_BF16, eps, Q, C, E, dH, dH_score, w_q,
+                                                     w_e, gate, gpc, R, lse, dout, dQ, dC, dE, d_dH, dgate,
+                                                     dw_q, dw_e, (float*)workspace, (hipStream_t)stream),
+                    "dart_sma_bwd_rms");
+}
+
 size_t dart_chunk_states_bwd_workspace_bytes(const dart_dims_t* dims) {
   t_err[0] = '\0';
   if (dims == nullptr || check_dims(dims, DART_F32, true) != DART_OK) return 0;

@@ -45,6 +45,16 @@ hipError_t launch_sma_decode_rms_general(const Shape& s, bool bf16, int64_t max_
                                          const void* y, const void* gate, int gate_pc, void* out,
                                          float* R, float* lse, hipStream_t st);
 
+// ---- backward of the normalised score branch (general kernels; dHs as the
+// forward consumed it; dwq, dwe nullable) -------------------------------------
+size_t sma_bwd_rms_workspace_bytes(const Shape& s);
+hipError_t launch_sma_bwd_rms_general(const Shape& s, bool bf16, float eps, const void* Q, const void* C,
+                                      const void* E, const void* dH, const void* dHs, const float* wq,
+                                      const float* we, const void* gate, int gate_pc, const float* R,
+                                      const float* lse, const void* dout, float* dQ, float* dC, float* dE,
+                                      float* ddH, float* dgate, float* dwq, float* dwe, float* ws,
+                                      hipStream_t st);
+
 // ---- backward, general kernels -------------------------------------------
 size_t sma_bwd_workspace_bytes(const Shape& s);
 hipError_t launch_sma_bwd_general(const Shape& s, bool bf16, const void* Q, const void* C,

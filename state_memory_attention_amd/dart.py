@@ -32,7 +32,8 @@ ENTRY_POINTS = ("dart_chunk_states", "dart_sma_fwd", "dart_sma_decode",
                 "dart_chunk_states_bwd", "dart_chunk_states_bwd_workspace_bytes",
                 "dart_decode_state_update",
                 "dart_chunk_states_rms", "dart_chunk_rms", "dart_sma_fwd_rms", "dart_sma_decode_rms",
-                "dart_decode_state_update_rms", "dart_ssd_fwd", "dart_ssd_fwd_workspace_bytes",
+                "dart_decode_state_update_rms", "dart_sma_bwd_rms", "dart_sma_bwd_rms_workspace_bytes",
+                "dart_ssd_fwd", "dart_ssd_fwd_workspace_bytes",
                 "dart_status_string", "dart_last_error", "dart_abi_version", "dart_set_path")
 
 
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
     L.dart_chunk_rms.restype = i32
     L.dart_sma_fwd_rms.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     L.dart_sma_fwd_rms.restype = i32
+    L.dart_sma_bwd_rms.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp,
+                                   vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dart_sma_bwd_rms.restype = i32
+    L.dart_sma_bwd_rms_workspace_bytes.argtypes = [dp]
+    L.dart_sma_bwd_rms_workspace_bytes.restype = ctypes.c_size_t
     L.dart_sma_decode_rms.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp,
                                       vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.dart_sma_decode_rms.restype = i32
@@ -481,6 +487,52 @@ def dart_sma_fwd_rms(Q: torch.Tensor, C: torch.Tensor, E: torch.Tensor, dH: torc
                                   _ptr(dH_score), _ptr(Y), _ptr(gate), int(gpc), float(eps), _ptr(out),
                                   _ptr(R), _ptr(lse), _stream(Q)))
     return out, R, lse
+
+
+def dart_sma_bwd_rms(Q: torch.Tensor, C: torch.Tensor, E: torch.Tensor, dH: torch.Tensor,
+                     dH_score: torch.Tensor, gate: torch.Tensor, R: torch.Tensor, lse: torch.Tensor,
+                     dout: torch.Tensor, chunk: int, eps: float, w_q: Optional[torch.Tensor] = None,
+                     w_e: Optional[torch.Tensor] = None, want_dgate: bool = True,
+                     want_dw: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Gradients of out = Y + gate * R for the normalised score branch, from
+    the forward's R and lse and the score memory it consumed.  Returns float32
+    (dQ, dC, dE, d_dH, dgate, dw_q, dw_e); dgate is None unless want_dgate,
+    dw_q (N,) and dw_e (P,) None unless want_dw (the gradient with respect to
+    each RMSNorm weight at its value, 1 where it is not given)."""
+    b, L, G, N = Q.shape
+    H, P = dout.shape[2], dout.shape[3]
+    M = num_chunks(L, chunk)
+    dev, dt = Q.device, Q.dtype
+    f32 = torch.float32
+    _need(C, "C", (b, L, G, N), dt, dev)
+    _need(E, "E", (b, L, G, P), dt, dev)
+    _need(dH, "dH", (b, H, M, P, N), dt, dev)
+    _need(dH_score, "dH_score", (b, H, M, P, N), score_dtype(dt), dev)
+    gpc = gate.dim() == 4
+    _need(gate, "gate", (b, L, H, P) if gpc else (b, L, H), dt, dev)
+    _need(R, "R", (b, L, H, P), f32, dev)
+    _need(lse, "lse", (b, H, L), f32, dev)
+    _need(dout, "dout", (b, L, H, P), dt, dev)
+    if w_q is not None:
+        _need(w_q, "w_q", (N,), f32, dev)
+    if w_e is not None:
+        _need(w_e, "w_e", (P,), f32, dev)
+    dQ = torch.empty((b, L, G, N), dtype=f32, device=dev)
+    dC = torch.empty((b, L, G, N), dtype=f32, device=dev)
+    dE = torch.empty((b, L, G, P), dtype=f32, device=dev)
+    ddH = torch.empty((b, H, M, P, N), dtype=f32, device=dev)
+    dgate = torch.empty(gate.shape, dtype=f32, device=dev) if want_dgate else None
+    dwq = torch.empty((N,), dtype=f32, device=dev) if want_dw else None
+    dwe = torch.empty((P,), dtype=f32, device=dev) if want_dw else None
+    dims = Dims(b, L, H, G, N, P, chunk)
+    need = int(lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(dims)))
+    workspace = _workspace(need, dev, workspace)
+    _check(lib().dart_sma_bwd_rms(ctypes.byref(dims), _code(dt), _ptr(Q), _ptr(C), _ptr(E), _ptr(dH),
+                                  _ptr(dH_score), _ptr(gate), int(gpc), float(eps), _ptr(w_q), _ptr(w_e),
+                                  _ptr(R), _ptr(lse), _ptr(dout), _ptr(dQ), _ptr(dC), _ptr(dE), _ptr(ddH),
+                                  _ptr(dgate), _ptr(dwq), _ptr(dwe), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(Q)))
+    return dQ, dC, dE, ddH, dgate, dwq, dwe
 
 
 def dart_sma_decode_rms(q: torch.Tensor, c: torch.Tensor, e: torch.Tensor, cache: torch.Tensor,

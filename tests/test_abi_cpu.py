@@ -316,6 +316,54 @@ def test_rms_validation():
     assert upd_rms(dims(b=0)) == 0
 
 
+MORE = [ctypes.c_void_p((k + 1) << 40) for k in range(24)]
+
+
+def bwd_rms(d, dtype=1, eps=1e-6, ws=MORE[23], ws_bytes=1 << 40, over=None):
+    p = list(MORE[:20])
+    p[12] = p[13] = p[14] = None  # w_q, w_e unweighted; dgate skipped
+    for k, v in (over or {}).items():
+        p[k] = v
+    # Q C E dH dHs gate | R lse dout dQ dC dE | w_q w_e dgate | d_dH dw_q dw_e
+    return D.lib().dart_sma_bwd_rms(ctypes.byref(d), dtype, p[0], p[1], p[2], p[3], p[4], p[5], 1, eps,
+                                    p[12], p[13], p[6], p[7], p[8], p[9], p[10], p[11], p[15], p[14],
+                                    p[16], p[17], ws, ws_bytes, None)
+
+
+def test_rms_backward_validation():
+    d = dims()
+    b, L, H, G, N, P, S = 2, 512, 4, 2, 128, 64, 256
+    M = 2
+    up = lambda n: -(-n // 64) * 64
+    split = min(1024, max(1, -(-(b * L * G) // 512)))
+    want = 4 * (up(2 * b * H * M * L) + up(b * L * H * N) + up(b * L * H * P) + up(b * L * H * N)
+                + up(2 * b * L * G) + up(b * H * M * P * N) + up(b * L * G * N) + up(b * L * G * P)
+                + up(split * (N + P)))
+    need = D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(d))
+    assert need == want
+    # ungrouped heads: no per-head dC partials
+    G1 = 4
+    split1 = min(1024, max(1, -(-(b * L * G1) // 512)))
+    want1 = 4 * (up(2 * b * H * M * L) + up(b * L * H * N) + up(b * L * H * P) + up(2 * b * L * G1)
+                 + up(b * H * M * P * N) + up(b * L * G1 * N) + up(b * L * G1 * P) + up(split1 * (N + P)))
+    assert D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(dims(G=G1))) == want1
+    assert bwd_rms(d, ws=None) == -4 and "workspace" in last()
+    assert bwd_rms(d, ws_bytes=need - 1) == -4
+    assert bwd_rms(d, over={4: None}) == -1 and "dH_score" in last()
+    assert bwd_rms(d, over={15: None}) == -1 and "d_dH" in last()
+    assert bwd_rms(d, eps=-1.0) == -2 and "eps" in last()
+    assert bwd_rms(d, eps=float("nan")) == -2
+    assert bwd_rms(d, over={12: ctypes.c_void_p(MORE[12].value + 2)}) == -6 and "w_q" in last()
+    assert bwd_rms(d, over={16: ctypes.c_void_p(MORE[16].value + 2)}) == -6 and "dw_q" in last()
+    assert bwd_rms(d, over={9: ctypes.c_void_p(MORE[9].value + 4)}) == -6 and "dQ" in last()
+    # a gradient overlapping an input, and a weight gradient overlapping a weight
+    assert bwd_rms(d, over={9: ctypes.c_void_p(MORE[4].value)}) == -2 and "overlaps" in last()
+    assert bwd_rms(d, over={12: MORE[12], 16: MORE[12]}) == -2 and "overlaps" in last()
+    assert bwd_rms(d, dtype=3) == -3
+    assert bwd_rms(dims(L=0)) == 0 and bwd_rms(dims(b=0)) == 0
+    assert D.lib().dart_sma_bwd_rms_workspace_bytes(None) == 0
+
+
 def ssd(d, dtype=1, over=None, ws_bytes=1 << 40):
     p = list(ADDR[:10])  # X B C A H0 Y dH Hfin ws
     p[4] = None
