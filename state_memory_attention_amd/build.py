@@ -33,6 +33,7 @@ SOURCES = [
     "rms_general.hip",
     "sma_fwd_rms_mfma.hip",
     "rms_backward.hip",
+    "sma_bwd_rms_mfma.hip",
     "ssd.hip",
 ]
 # A plain 16-byte-vector copy kernel in its own library, used only to

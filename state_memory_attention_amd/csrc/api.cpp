@@ -632,7 +632,8 @@ size_t dart_sma_bwd_rms_workspace_bytes(const dart_dims_t* dims) {
   if (prod({2, s.b, s.H, s.M, s.L}) < 0 || prod({3, s.b, s.L, s.H, s.N + s.P}) < 0 ||
       prod({2, s.b, s.H, s.M, s.P, s.N}) < 0)
     return 0;
-  return dart::sma_bwd_rms_workspace_bytes(s);
+  const size_t g = dart::sma_bwd_rms_workspace_bytes(s), m = dart::sma_bwd_rms_mfma_workspace_bytes(s);
+  return g > m ? g : m;
 }
 
 int dart_sma_bwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const void* C,
@@ -667,7 +668,8 @@ int dart_sma_bwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const vo
   const Buf gg{dgate, prod({s.b, s.L, s.H, gpc ? s.P : 1}) * 4, "dgate"};
   const Buf gwq{dw_q, s.N * 4, "dw_q"};
   const Buf gwe{dw_e, s.P * 4, "dw_e"};
-  const size_t need = dart::sma_bwd_rms_workspace_bytes(s);
+  const size_t gneed = dart::sma_bwd_rms_workspace_bytes(s), mneed = dart::sma_bwd_rms_mfma_workspace_bytes(s);
+  const size_t need = gneed > mneed ? gneed : mneed;
   const Buf bw{workspace, (int64_t)need, "workspace"};
   if ((st = check_ptrs({bq, bc, be, bd, bs, bg, br, bl, bo, gq, gc, ge, gd}))) return st;
   if ((st = check_opt_align(dgate, "dgate"))) return st;
@@ -683,6 +685,11 @@ int dart_sma_bwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const vo
   if (prod({s.b, s.H, s.M, (s.N * s.P + 255) / 256}) >= kMaxIndex || prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex ||
       prod({s.b, s.H, s.M, s.N}) / 256 >= kMaxIndex || prod({s.b, s.L, s.G}) / 4 >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "b * H * M or b * H * L is too large for one launch");
+  if (use_mfma(dtype, dims))
+    return hip_status(dart::launch_sma_bwd_rms_mfma(s, eps, Q, C, E, dH, dH_score, w_q, w_e, gate, gpc, R, lse,
+                                                    dout, dQ, dC, dE, d_dH, dgate, dw_q, dw_e, workspace,
+                                                    (hipStream_t)stream),
+                      "dart_sma_bwd_rms");
   return hip_status(dart::launch_sma_bwd_rms_general(s, dtype == DART_BF16, eps, Q, C, E, dH, dH_score, w_q,
                                                      w_e, gate, gpc, R, lse, dout, dQ, dC, dE, d_dH, dgate,
                                                      dw_q, dw_e, (float*)workspace, (hipStream_t)stream),

@@ -55,6 +55,19 @@ hipError_t launch_sma_bwd_rms_general(const Shape& s, bool bf16, float eps, cons
                                       float* ddH, float* dgate, float* dwq, float* dwe, float* ws,
                                       hipStream_t st);
 
+// Column sums out[k] = sum_r in[r][k] in a fixed order (two passes through
+// part, col_sum_split(rows) * K floats).
+int64_t col_sum_split(int64_t rows);
+hipError_t launch_col_sum(const float* in, float* part, float* out, int64_t rows, int K, hipStream_t st);
+
+// The same on the matrix core (bf16, N = 128, P = 64).
+size_t sma_bwd_rms_mfma_workspace_bytes(const Shape& s);
+hipError_t launch_sma_bwd_rms_mfma(const Shape& s, float eps, const void* Q, const void* C, const void* E,
+                                   const void* dH, const void* dHs, const float* wq, const float* we,
+                                   const void* gate, int gate_pc, const float* R, const float* lse,
+                                   const void* dout, float* dQ, float* dC, float* dE, float* ddH, float* dgate,
+                                   float* dwq, float* dwe, void* ws, hipStream_t st);
+
 // ---- backward, general kernels -------------------------------------------
 size_t sma_bwd_workspace_bytes(const Shape& s);
 hipError_t launch_sma_bwd_general(const Shape& s, bool bf16, const void* Q, const void* C,
@@ -96,11 +109,18 @@ hipError_t launch_sma_bwd_a_mfma(const Shape& s, const void* Q, const void* C, c
                                  const void* dH, const void* gate, int gate_pc, const void* dout,
                                  const float* R, const float* lse, float* dE, int dE_heads,
                                  float* pd, void* dR, float* dgate, hipStream_t st);
-hipError_t launch_sma_bwd_bc_mfma(const Shape& s, const void* E, const void* dR, const void* dH,
-                                  const float* pd, float* dQ, float* dC, int out_heads,
-                                  hipStream_t st);
+// Pass BC modes: both gradients from dH; the Q side only, from the float16
+// score memory of the normalised branch (rho: [b][L][G][2] RMSNorm factors;
+// Q_norm: Q when each group has one head, and dQ then goes through the
+// RMSNorm backward in the epilogue, else NULL); the C side only.
+constexpr int kBcBoth = 0, kBcScoreQ = 1, kBcC = 2;
+hipError_t launch_sma_bwd_bc_mfma(const Shape& s, int mode, const void* E, const void* dR, const void* mem,
+                                  const float* pd, const float* rho, const void* Q_norm, float* dQ, float* dC,
+                                  int out_heads, hipStream_t st);
+// ddH_score: nullptr (both terms into ddH) or a buffer for the score term
 hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, const void* C,
-                                 const void* Q, const float* pd, float* ddH, hipStream_t st);
+                                 const void* Q, const float* pd, float* ddH, float* ddH_score,
+                                 hipStream_t st);
 hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, const void* E,
                                const void* dH, const void* gate, int gate_pc, const float* R,
                                const float* lse, const void* dout, float* dQ, float* dC, float* dE,

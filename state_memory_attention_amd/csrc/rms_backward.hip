@@ -47,13 +47,6 @@ struct RmsBwdWs {
   int64_t pd, hq, he, hc, rho, ds, wpq, wpe, part, total;
 };
 
-constexpr int64_t kColSplitMax = 1024;
-
-int64_t col_split(int64_t rows) {
-  const int64_t n = (rows + 511) / 512;
-  return n < 1 ? 1 : (n > kColSplitMax ? kColSplitMax : n);
-}
-
 RmsBwdWs rms_bwd_layout(const Shape& s) {
   auto up = [](int64_t n) { return (n + 63) / 64 * 64; };
   RmsBwdWs w;
@@ -66,7 +59,7 @@ RmsBwdWs rms_bwd_layout(const Shape& s) {
   w.ds = o;  o += up(s.b * s.H * s.M * s.P * s.N);
   w.wpq = o; o += up(s.b * s.L * s.G * s.N);
   w.wpe = o; o += up(s.b * s.L * s.G * s.P);
-  w.part = o; o += up(col_split(s.b * s.L * s.G) * (s.N + s.P));
+  w.part = o; o += up(col_sum_split(s.b * s.L * s.G) * (s.N + s.P));
   w.total = o;
   return w;
 }
@@ -366,15 +359,6 @@ __global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* __restri
   if (wave == 0 && k < K) out[split * K + k] = ((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane];
 }
 
-hipError_t col_sum(const float* in, float* part, float* out, int64_t rows, int K, hipStream_t st) {
-  const int64_t split = col_split(rows);
-  const int64_t chunk = (rows + split - 1) / split;
-  const unsigned cols = (unsigned)((K + 63) / 64);
-  col_sum_kernel<<<dim3(cols, (unsigned)split), dim3(kThreads), 0, st>>>(in, part, rows, K, chunk);
-  col_sum_kernel<<<dim3(cols, 1), dim3(kThreads), 0, st>>>(part, out, split, K, split);
-  return hipGetLastError();
-}
-
 template <typename T, typename TS>
 hipError_t launch_rms_bwd(const Shape& s, float eps, const void* Qv, const void* Cv, const void* Ev,
                           const void* dHv, const void* dHsv, const float* wq, const float* we,
@@ -407,13 +391,27 @@ hipError_t launch_rms_bwd(const Shape& s, float eps, const void* Qv, const void*
       dwe ? ws + w.wpe : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dwq && (e = col_sum(ws + w.wpq, ws + w.part, dwq, tgs, (int)s.N, st)) != hipSuccess) return e;
-  if (dwe && (e = col_sum(ws + w.wpe, ws + w.part, dwe, tgs, (int)s.P, st)) != hipSuccess) return e;
+  if (dwq && (e = launch_col_sum(ws + w.wpq, ws + w.part, dwq, tgs, (int)s.N, st)) != hipSuccess) return e;
+  if (dwe && (e = launch_col_sum(ws + w.wpe, ws + w.part, dwe, tgs, (int)s.P, st)) != hipSuccess) return e;
   if (grouped) return launch_group_sum(hc, dC, s.b * s.L, s.G, s.H / s.G, s.N, st);
   return hipSuccess;
 }
 
 }  // namespace
+
+int64_t col_sum_split(int64_t rows) {
+  const int64_t n = (rows + 511) / 512;
+  return n < 1 ? 1 : (n > 1024 ? 1024 : n);
+}
+
+hipError_t launch_col_sum(const float* in, float* part, float* out, int64_t rows, int K, hipStream_t st) {
+  const int64_t split = col_sum_split(rows);
+  const int64_t chunk = (rows + split - 1) / split;
+  const unsigned cols = (unsigned)((K + 63) / 64);
+  col_sum_kernel<<<dim3(cols, (unsigned)split), dim3(kThreads), 0, st>>>(in, part, rows, K, chunk);
+  col_sum_kernel<<<dim3(cols, 1), dim3(kThreads), 0, st>>>(part, out, split, K, split);
+  return hipGetLastError();
+}
 
 size_t sma_bwd_rms_workspace_bytes(const Shape& s) { return (size_t)rms_bwd_layout(s).total * sizeof(float); }
 

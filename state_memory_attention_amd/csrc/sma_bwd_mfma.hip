@@ -463,8 +463,11 @@ constexpr int kSlotBC = kMemBytes + kPdBytes;     // one chunk memory + its weig
 struct BwdBCArgs {
   const bf16_t* E;
   const bf16_t* dR;    // [b][L][H][P], from pass A
-  const bf16_t* dH;
+  const void* mem;     // chunk memories: dH (bf16), or the float16 score memory (Q side only)
   const float* pd;     // [b][H][M][2][L], from pass A (p, dl / sqrt(N))
+  const float* rho;    // [b][L][G][2] (Q side on the score memory): RMSNorm factors of Q_t, E_t
+  const bf16_t* Qn;    // score-memory mode with one head per group: Q, and dQ is written
+                       // through the RMSNorm backward (else NULL: the gradient of RMSNorm(Q_t))
   float* dQ;           // [b][L][out_heads][N]
   float* dC;
   int64_t L;
@@ -500,6 +503,23 @@ __device__ __forceinline__ void ld_tr8(uint64_t (&o)[8], const uint32_t (&ad)[8]
       : "memory");
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// 8 bf16 scaled by s in float32 and rounded to float16.
+__device__ __forceinline__ f16x8_t scale8h(bf16x8_t x, float s) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  f16x8_t r;
+  r[0] = (_Float16)(bf16lo(u.x) * s);
+  r[1] = (_Float16)(bf16hi(u.x) * s);
+  r[2] = (_Float16)(bf16lo(u.y) * s);
+  r[3] = (_Float16)(bf16hi(u.y) * s);
+  r[4] = (_Float16)(bf16lo(u.z) * s);
+  r[5] = (_Float16)(bf16hi(u.z) * s);
+  r[6] = (_Float16)(bf16lo(u.w) * s);
+  r[7] = (_Float16)(bf16hi(u.w) * s);
+  return r;
+}
+
 // 8 bf16 scaled by s in float32 and rounded back.
 __device__ __forceinline__ bf16x8_t scale8(bf16x8_t x, float s) {
   const uint4 u = __builtin_bit_cast(uint4, x);
@@ -511,8 +531,15 @@ __device__ __forceinline__ bf16x8_t scale8(bf16x8_t x, float s) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// kMode: kBcBoth (dQ and dC from dH), kBcScoreQ (dQ only, from the float16
+// score memory of the normalised branch, whose Q-side gradient
+// sum_c dHs_c (E_t rho_e,t dl_tc / sqrt(N)) takes the E operand scaled by the
+// token's RMSNorm factor: the pd row then holds dl / sqrt(N) rho_q rho_e and is
+// divided by rho_q here), kBcC (dC only, from dH).
+template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sma_bwd_bc_kernel(BwdBCArgs a) {
+  constexpr bool kDoQ = kMode != kBcC, kDoC = kMode != kBcScoreQ;
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing * kSlotBC];
 
   const int blk = blockIdx.x;
@@ -536,7 +563,7 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
   // loaded by wave w, 4 loads) and the (p, dl) pair of the wave's 32 tokens
   // (one 4-byte-per-lane load: lanes 0-31 p, lanes 32-63 dl).  Five loads per
   // wave per slot.
-  const uint8_t* mem_head = (const uint8_t*)(a.dH + (int64_t)bh * a.M * (kP * kN));
+  const uint8_t* mem_head = (const uint8_t*)a.mem + (int64_t)bh * a.M * kMemBytes;
   const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
   const uint32_t pd_lane = (uint32_t)((half ? a.L : 0) + t0 + 32 * wave + col) * 4;
   auto issue = [&](int s) {
@@ -560,6 +587,13 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
   // registers (this wave's part of it covers exactly the bytes its E rows
   // occupied; buffer 3 takes slot 3 only after the loop's first barrier).
   bf16x8_t eop[4], rop[4];
+  // score-memory mode: 1 / rho_q of this lane's token (the pd row's dl
+  // carries rho_q rho_e; the Q-side operand needs rho_e only)
+  float rq = 1.f, irq = 1.f;
+  if (kMode == kBcScoreQ) {
+    rq = a.rho[2 * ((row0 + tc) * a.G + g)];
+    irq = 1.f / rq;
+  }
   {
     if (0 < n_hist) issue(0);
     if (1 < n_hist) issue(1);
@@ -572,15 +606,15 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
     for (int k = 0; k < 4; ++k) {
       const int r = 32 * wave + 8 * k + (lane >> 3);
       const uint32_t sw = (uint32_t)(((lane & 7) ^ (r & 7)) << 3);
-      buf_dma16(rse, (uint32_t)(r * a.G * kP + sw) * 2, s_se + k * 1024);
-      buf_dma16(rsr, (uint32_t)(r * a.H * kP + sw) * 2, s_sr + k * 1024);
+      if (kDoQ) buf_dma16(rse, (uint32_t)(r * a.G * kP + sw) * 2, s_se + k * 1024);
+      if (kDoC) buf_dma16(rsr, (uint32_t)(r * a.H * kP + sw) * 2, s_sr + k * 1024);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const uint32_t o = col * 128 + (((2 * ks + half) ^ (col & 7)) << 4);
-      eop[ks] = *(const bf16x8_t*)(s_se + o);
-      rop[ks] = *(const bf16x8_t*)(s_sr + o);
+      if (kDoQ) eop[ks] = *(const bf16x8_t*)(s_se + o);
+      if (kDoC) rop[ks] = *(const bf16x8_t*)(s_sr + o);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (2 < n_hist) issue(2);
@@ -634,16 +668,23 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ks = 2 * kp + q;
-        const bf16x8_t be = scale8(eop[ks], dls);
-        const bf16x8_t br = scale8(rop[ks], ps);
+        f16x8_t beh;
+        bf16x8_t be, br;
+        if (kMode == kBcScoreQ) beh = scale8h(eop[ks], dls * irq);
+        if (kMode == kBcBoth) be = scale8(eop[ks], dls);
+        if (kDoC) br = scale8(rop[ks], ps);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int i = 4 * q + rb;
-          const bf16x8_t af = __builtin_bit_cast(
-              bf16x8_t, make_uint4((uint32_t)rd[i], (uint32_t)(rd[i] >> 32), (uint32_t)rd2[i],
-                                   (uint32_t)(rd2[i] >> 32)));
-          dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, be, dq[rb], 0, 0, 0);
-          dc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, br, dc[rb], 0, 0, 0);
+          const uint4 av = make_uint4((uint32_t)rd[i], (uint32_t)(rd[i] >> 32), (uint32_t)rd2[i],
+                                      (uint32_t)(rd2[i] >> 32));
+          if (kMode == kBcScoreQ) {
+            dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, av), beh, dq[rb], 0, 0, 0);
+          } else {
+            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
+            if (kDoQ) dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, be, dq[rb], 0, 0, 0);
+            if (kDoC) dc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, br, dc[rb], 0, 0, 0);
+          }
         }
       }
     }
@@ -652,6 +693,36 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
 
   // dQ^T, dC^T: lane column = token, register r of row block rb is
   // n = 32 rb + 8 (r / 4) + 4 half + r % 4
+  if (kMode == kBcScoreQ && a.Qn) {
+    // RMSNorm backward of Q_t [App. B.1 Eq. 25]: dQ = rho dz - rho^3 Q (Q . dz) / N,
+    // the dot product over this half-wave's 64 n and then both halves
+    const bf16_t* qr = a.Qn + ((row0 + tc) * a.G + g) * kN + 4 * half;
+    uint2 qv[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) qv[rb][q] = *(const uint2*)(qr + 32 * rb + 8 * q);
+    float part = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        part = fmaf(bf16lo(qv[rb][q].x), dq[rb][4 * q], part);
+        part = fmaf(bf16hi(qv[rb][q].x), dq[rb][4 * q + 1], part);
+        part = fmaf(bf16lo(qv[rb][q].y), dq[rb][4 * q + 2], part);
+        part = fmaf(bf16hi(qv[rb][q].y), dq[rb][4 * q + 3], part);
+      }
+    const float c3 = rq * rq * rq * halves_sum(part) * (1.f / kN);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dq[rb][4 * q] = fmaf(rq, dq[rb][4 * q], -c3 * bf16lo(qv[rb][q].x));
+        dq[rb][4 * q + 1] = fmaf(rq, dq[rb][4 * q + 1], -c3 * bf16hi(qv[rb][q].x));
+        dq[rb][4 * q + 2] = fmaf(rq, dq[rb][4 * q + 2], -c3 * bf16lo(qv[rb][q].y));
+        dq[rb][4 * q + 3] = fmaf(rq, dq[rb][4 * q + 3], -c3 * bf16hi(qv[rb][q].y));
+      }
+  }
   if (tok_ok) {
     const int64_t orow = ((row0 + t) * a.out_heads + (a.out_heads == a.H ? h : g)) * kN + 4 * half;
 #pragma unroll
@@ -659,22 +730,26 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = 32 * rb + 8 * q;
-        *(float4*)(a.dQ + orow + n) = make_float4(dq[rb][4 * q], dq[rb][4 * q + 1], dq[rb][4 * q + 2], dq[rb][4 * q + 3]);
-        *(float4*)(a.dC + orow + n) = make_float4(dc[rb][4 * q], dc[rb][4 * q + 1], dc[rb][4 * q + 2], dc[rb][4 * q + 3]);
+        if (kDoQ)
+          *(float4*)(a.dQ + orow + n) = make_float4(dq[rb][4 * q], dq[rb][4 * q + 1], dq[rb][4 * q + 2], dq[rb][4 * q + 3]);
+        if (kDoC)
+          *(float4*)(a.dC + orow + n) = make_float4(dc[rb][4 * q], dc[rb][4 * q + 1], dc[rb][4 * q + 2], dc[rb][4 * q + 3]);
       }
   }
 }
 
 }  // namespace
 
-hipError_t launch_sma_bwd_bc_mfma(const Shape& s, const void* E, const void* dR, const void* dH,
-                                  const float* pd, float* dQ, float* dC, int out_heads,
-                                  hipStream_t st) {
+hipError_t launch_sma_bwd_bc_mfma(const Shape& s, int mode, const void* E, const void* dR, const void* mem,
+                                  const float* pd, const float* rho, const void* Q_norm, float* dQ, float* dC,
+                                  int out_heads, hipStream_t st) {
   BwdBCArgs a;
   a.E = (const bf16_t*)E;
   a.dR = (const bf16_t*)dR;
-  a.dH = (const bf16_t*)dH;
+  a.mem = mem;
   a.pd = pd;
+  a.rho = rho;
+  a.Qn = (const bf16_t*)Q_norm;
   a.dQ = dQ;
   a.dC = dC;
   a.L = s.L;
@@ -690,7 +765,12 @@ hipError_t launch_sma_bwd_bc_mfma(const Shape& s, const void* E, const void* dR,
   a.inv_sqrt_n = 1.f / sqrtf((float)kN);
   const int64_t blocks = (int64_t)a.BHp * a.n_tiles;
   if (blocks == 0) return hipSuccess;
-  sma_bwd_bc_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  if (mode == kBcScoreQ)
+    sma_bwd_bc_kernel<kBcScoreQ><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  else if (mode == kBcC)
+    sma_bwd_bc_kernel<kBcC><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
+  else
+    sma_bwd_bc_kernel<kBcBoth><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -713,7 +793,8 @@ struct BwdDArgs {
   const bf16_t* C;    // [b][L][G][N]
   const bf16_t* Q;
   const float* pd;    // [b][H][M][2][L]: p, dl / sqrt(N)
-  float* ddH;         // [b][H][M][P][N]
+  float* ddH;         // [b][H][M][P][N]: the readout term (term 0)
+  float* ddH1;        // where the score term (term 1) goes: ddH, or a buffer of its own
   int64_t L;
   int H, G, hpg, S, M, n_groups, BH, BHp;
   float inv_sqrt_n;
@@ -947,7 +1028,7 @@ void sma_bwd_d_kernel(BwdDArgs a) {
   for (int e = 0; e < 2; ++e) {
     const int c = c0 + 2 * cp + e;
     if (c >= a.M) continue;
-    float* outp = a.ddH + ((int64_t)bh * a.M + c) * (kP * kN) + (lane & 31);
+    float* outp = (term ? a.ddH1 : a.ddH) + ((int64_t)bh * a.M + c) * (kP * kN) + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int p = 32 * ph + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -966,7 +1047,8 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float4* p, int64_t n4) {
 }  // namespace
 
 hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, const void* C,
-                                 const void* Q, const float* pd, float* ddH, hipStream_t st) {
+                                 const void* Q, const float* pd, float* ddH, float* ddH_score,
+                                 hipStream_t st) {
   BwdDArgs a;
   a.dR = (const bf16_t*)dR;
   a.E = (const bf16_t*)E;
@@ -974,6 +1056,7 @@ hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, 
   a.Q = (const bf16_t*)Q;
   a.pd = pd;
   a.ddH = ddH;
+  a.ddH1 = ddH_score ? ddH_score : ddH;
   a.L = s.L;
   a.H = (int)s.H;
   a.G = (int)s.G;
@@ -989,7 +1072,9 @@ hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, 
   // every d_dH entry is a sum of the two terms' blocks (kP * kN floats per
   // chunk memory: a whole number of float4)
   const int64_t n4 = s.b * s.H * s.M * (kP * kN) / 4;
-  zero_f32_kernel<<<dim3((unsigned)(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096)), dim3(256), 0, st>>>((float4*)ddH, n4);
+  const unsigned zb = (unsigned)(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
+  zero_f32_kernel<<<dim3(zb), dim3(256), 0, st>>>((float4*)ddH, n4);
+  if (a.ddH1 != ddH) zero_f32_kernel<<<dim3(zb), dim3(256), 0, st>>>((float4*)a.ddH1, n4);
   sma_bwd_d_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
@@ -1027,9 +1112,9 @@ hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, con
   hipError_t e = launch_sma_bwd_a_mfma(s, Q, C, E, dH, gate, gate_pc, dout, R, lse, he, heads, pd, dR,
                                        dgate, st);
   if (e != hipSuccess) return e;
-  e = launch_sma_bwd_bc_mfma(s, E, dR, dH, pd, hq, hc, heads, st);
+  e = launch_sma_bwd_bc_mfma(s, kBcBoth, E, dR, dH, pd, nullptr, nullptr, hq, hc, heads, st);
   if (e != hipSuccess) return e;
-  e = launch_sma_bwd_d_mfma(s, dR, E, C, Q, pd, ddH, st);
+  e = launch_sma_bwd_d_mfma(s, dR, E, C, Q, pd, ddH, nullptr, st);
   if (e != hipSuccess || !grouped) return e;
   const int64_t rows = s.b * s.L, hpg = s.H / s.G;
   if ((e = launch_group_sum(hq, dQ, rows, s.G, hpg, s.N, st)) != hipSuccess) return e;

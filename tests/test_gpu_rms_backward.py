@@ -186,3 +186,64 @@ def test_bwd_rms_deterministic():
     b, _ = gpu_chain(d, cfg, mem_t, s, dout, wq, we)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+# bf16, N = 128, P = 64: the matrix-core backward.  Shapes as for the plain
+# branch's matrix-core backward: tiles spanning several chunks (S < 128),
+# chunk starts inside a 64-token sub-block of the d_dH pass (S % 64 != 0),
+# grouped heads, ragged tails, a sequence shorter than one wave's 32 tokens,
+# odd b*H*M*L, chunks of 1 and 3 tokens, the evaluation-time size 32, both
+# gate forms, with and without RMSNorm weights.
+MFMA_CASES = [
+    (dict(batch=1, nheads=4, ngroups=2, seqlen=1000, chunk=96), True, True),
+    (dict(batch=2, nheads=2, ngroups=2, seqlen=777, chunk=64), False, True),
+    (dict(batch=1, nheads=2, ngroups=1, seqlen=1300, chunk=256), True, False),
+    (dict(batch=2, nheads=2, ngroups=1, seqlen=20, chunk=8), False, True),
+    (dict(batch=1, nheads=3, ngroups=1, seqlen=777, chunk=64), True, True),
+    (dict(batch=1, nheads=2, ngroups=1, seqlen=151, chunk=1), True, True),
+    (dict(batch=1, nheads=3, ngroups=3, seqlen=403, chunk=3), False, False),
+    (dict(batch=2, nheads=2, ngroups=2, seqlen=1061, chunk=32), True, True),
+]
+
+
+def run_path(path, *args):
+    prev = dart.set_path(path)
+    try:
+        return gpu_chain(*args)[0]
+    finally:
+        dart.set_path(prev)
+
+
+@pytest.mark.parametrize("ci", range(len(MFMA_CASES)))
+def test_mfma_bwd_rms_against_oracle_and_general(ci):
+    base, gpc, wts = MFMA_CASES[ci]
+    cfg = dict(base, d_state=128, d_head=64, dtype="bf16")
+    say("mfma sma_bwd_rms", cfg, "gpc", gpc, "weights", wts)
+    d = synth.draw_fwd(**cfg, seed=151 + ci, gate_per_channel=gpc)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(cfg["batch"], cfg["nheads"], M, 128, 64, "bf16", seed=161 + ci)
+    dout = synth.draw_grad((cfg["batch"], cfg["seqlen"], cfg["nheads"], 64), "bf16", 171 + ci)
+    wq, we = weights(128, 64, 181 + ci, wts)
+    mem_t = dev(mem, "bf16")
+    _, s = dart.dart_chunk_rms(mem_t, cfg["seqlen"], cfg["chunk"], EPS, tw(wq), tw(we), want_r=False)
+    got = run_path(dart.DART_PATH_AUTO, d, cfg, mem_t, s, dout, wq, we)
+    gen = run_path(dart.DART_PATH_GENERAL, d, cfg, mem_t, s, dout, wq, we)
+    ref = oracle_chain(d, cfg, to_oracle_mem(mem), dout, wq, we)
+    compare(got, ref, TOL["bf16"], "mfma vs oracle")
+    compare(got, gen, TOL["bf16"], "mfma vs general")
+
+
+def test_mfma_bwd_rms_deterministic():
+    base, gpc, wts = MFMA_CASES[0]
+    cfg = dict(base, d_state=128, d_head=64, dtype="bf16")
+    d = synth.draw_fwd(**cfg, seed=191, gate_per_channel=gpc)
+    M = dart.num_chunks(cfg["seqlen"], cfg["chunk"])
+    mem = synth.draw_memories(1, 4, M, 128, 64, "bf16", seed=192)
+    dout = synth.draw_grad((1, cfg["seqlen"], 4, 64), "bf16", 193)
+    wq, we = weights(128, 64, 194, True)
+    mem_t = dev(mem, "bf16")
+    _, s = dart.dart_chunk_rms(mem_t, cfg["seqlen"], cfg["chunk"], EPS, tw(wq), tw(we), want_r=False)
+    runs = [gpu_chain(d, cfg, mem_t, s, dout, wq, we)[0] for _ in range(3)]
+    for r in runs[1:]:
+        for k in runs[0]:
+            assert np.array_equal(runs[0][k], r[k]), k
