@@ -42,6 +42,8 @@ KERNEL_SOURCES = {
     "sma_fwd_rms": [_CSRC + "sma_fwd_rms_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "chunk_states_rms": [_CSRC + "chunk_states_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "ssd": [_CSRC + "ssd.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
+    "sma_bwd_rms": [_CSRC + "sma_bwd_rms_mfma.hip", _CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h",
+                    _CSRC + "lds_dma.h"],
 }
 
 
@@ -262,7 +264,10 @@ def time_rms(torch, dart, synth, cfg, steps=10, warmup=2, eps=1e-6):
     """The hot path with the RMS-normalised score branch on the same
     workload: dart_chunk_states_rms (chunk memories plus the float16 score
     memory) and dart_sma_fwd_rms.  Same algorithmic flops as the plain
-    forward (4NP per pair; the normalisation is O(L (N + P)) per head)."""
+    forward (4NP per pair; the normalisation is O(L (N + P)) per head).
+    Then its backward, dart_sma_bwd_rms (with the RMSNorm weight gradients),
+    from the forward's R and lse: 12NP per pair as the plain backward (the
+    chain through r_c and the RMSNorms is O(M N P + L (N + P)) per head)."""
     b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
     N, P = cfg["d_state"], cfg["d_head"]
     d = synth.draw_fwd_torch(**cfg, seed=0)
@@ -298,7 +303,44 @@ def time_rms(torch, dart, synth, cfg, steps=10, warmup=2, eps=1e-6):
            "achieved_TFLOPs": f_sma / t_fwd / 1e12, "peak_TFLOPs": PEAK_BF16_TFLOPS,
            "frac": f_sma / t_fwd / 1e12 / PEAK_BF16_TFLOPS, "chunk_states_rms_us": t_cs * 1e6,
            "tokens_per_s": b * L / (t_cs + t_fwd)}
-    del d, dH, dHs, out
+    # backward: R and lse of the forward, RMSNorm weights, a synthetic dout
+    _, R, lse = dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["Y"], d["gate"], S, eps, out=out,
+                                      want_R=True, want_lse=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    wq = torch.rand(N, generator=gen, device="cuda") + 0.5
+    we = torch.rand(P, generator=gen, device="cuda") + 0.5
+    dout = synth.draw_grad_torch((b, L, H, P), "bf16", seed=3)
+    import ctypes
+
+    from state_memory_attention_amd import dart as D
+    dims = D.Dims(b, L, H, cfg["ngroups"], N, P, S)
+    ws = torch.empty(int(D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8,
+                     device="cuda")
+
+    def bwd():
+        return dart.dart_sma_bwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["gate"], R, lse, dout, S, eps, wq, we,
+                                     want_dw=True, workspace=ws)
+
+    for _ in range(warmup):
+        g = bwd()
+    bsteps = max(steps // 2, 1)
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(bsteps)]
+    torch.cuda.synchronize()
+    for k in range(bsteps):
+        evb[k][0].record(st)
+        g = bwd()
+        evb[k][1].record(st)
+    torch.cuda.synchronize()
+    t_bwd = sum(e[0].elapsed_time(e[1]) for e in evb) / bsteps / 1e3
+    fb = 12 * N * P * fwd_pairs(b, H, L, S)
+    res["backward"] = {"kernel": "dart_sma_bwd_rms", "us_per_call": t_bwd * 1e6, "flop_per_call": fb,
+                       "achieved_TFLOPs": fb / t_bwd / 1e12, "peak_TFLOPs": PEAK_BF16_TFLOPS,
+                       "frac": fb / t_bwd / 1e12 / PEAK_BF16_TFLOPS, "grad_dtype": "f32",
+                       "traffic": {k: traffic_record(k, cfg["name"], "sma_bwd_rms")
+                                   for k in ("sma_bwd_rms_a", "sma_bwd_rms_bc_q", "sma_bwd_rms_bc_c",
+                                             "sma_bwd_rms_d")}}
+    del d, dH, dHs, out, R, lse, dout, ws, g
     torch.cuda.empty_cache()
     return res
 
@@ -628,6 +670,17 @@ def profile_kernels(launches=3):
     for _ in range(launches):
         dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["Y"], d["gate"], S, 1e-6, out=out)
     torch.cuda.synchronize()
+    # its backward (after the plain backward's passes, which come first in
+    # dispatch order among the kernels both use)
+    _, R, lse = dart.dart_sma_fwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["Y"], d["gate"], S, 1e-6, out=out,
+                                      want_R=True, want_lse=True)
+    dout = synth.draw_grad_torch((cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["d_head"]), "bf16", seed=3)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        g = dart.dart_sma_bwd_rms(d["Q"], d["C"], d["E"], dH, dHs, d["gate"], R, lse, dout, S, 1e-6,
+                                  want_dw=True)
+    torch.cuda.synchronize()
+    del g, R, lse, dout
     for _ in range(launches):
         dart.dart_ssd_fwd(d["X"], d["B"], d["C"], d["A"], S, Y=out, dH=dH)
     torch.cuda.synchronize()
@@ -688,6 +741,10 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
             ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w2, 0),
             ("chunk_states_rms", "chunk_states_rms", "chunk_states_mfma_kernel<true>", w2, 0),
             ("sma_fwd_rms", "sma_fwd_rms", "sma_fwd_rms_mfma_kernel", w2, 0),
+            ("sma_bwd_rms_a", "sma_bwd_rms", "sma_bwd_rms_a_kernel", w2, 0),
+            ("sma_bwd_rms_bc_q", "sma_bwd_rms", "sma_bwd_bc_kernel<1>", w2, 0),
+            ("sma_bwd_rms_bc_c", "sma_bwd_rms", "sma_bwd_bc_kernel<2>", w2, 0),
+            ("sma_bwd_rms_d", "sma_bwd_rms", "sma_bwd_d_kernel", w2, launches),
             ("ssd_out", "ssd", "ssd_out_mfma_kernel", w2, 0),
             ("ssd_state_pass", "ssd", "state_pass_kernel", w2, 0)]
     for label, kernel, sym, workload, first in plan:
