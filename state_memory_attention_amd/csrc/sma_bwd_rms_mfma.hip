@@ -321,9 +321,11 @@ void sma_bwd_rms_a_kernel(BwdRmsAArgs a) {
 
   for (int j = 0; j < n_hist; ++j) {
     // chunk j landed in every wave's part and every wave is done with chunk
-    // j - 1, whose slot takes chunk j + 1
+    // j - 1, whose slot takes chunk j + 1.  In flight here: chunk j's loads
+    // (issued during chunk j - 1), then chunk j - 1's two (p, dl) stores;
+    // vector-memory operations complete in order, so vmcnt(2) covers the loads.
     if (j > 0) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
       __builtin_amdgcn_s_barrier();
       issue(j + 1);
     }
