@@ -10,10 +10,14 @@ row, head) at a time so that host memory stays bounded.
   dE, d_dH and dgate from the GPU forward's R and lse and the seed-3 loss
   gradient, then dX, dB, dA from the GPU's d_dH;
 * the RMS-normalised score branch [App. B.1 Eq. 25-27] on the GPU's own
-  chunk memories (eps = 1e-6, no norm weights);
+  chunk memories (eps = 1e-6, no norm weights), and its backward: dQ, dC,
+  dE, d_dH, dgate and the gradients of the RMSNorm weights (at weight 1),
+  those of each batch row alone from a call on that row, and the call on
+  both rows equal to their sum;
 * the SSM branch by the chunked scan [App. A Eq. 15-24] against the step
   recurrence, its chunk memories bit for bit against dart_chunk_states.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -56,6 +60,19 @@ def run():
         d["Q"], d["C"], d["E"], dHr, score, d["Y"], d["gate"], S, EPS, want_R=True, want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(dHr, g["dH"]), "dart_chunk_states_rms memories differ from dart_chunk_states"
+    # its backward, the benchmark's call, then each batch row alone for the
+    # weight gradients (sums over every row and head)
+    (g["dQ_rms"], g["dC_rms"], g["dE_rms"], g["ddH_rms"], g["dgate_rms"], g["dwq"], g["dwe"]) = \
+        dart.dart_sma_bwd_rms(d["Q"], d["C"], d["E"], dHr, score, d["gate"], g["R_rms"], g["lse_rms"], g["dout"],
+                              S, EPS, want_dw=True)
+    for bi in range(b):
+        row = lambda t: t[bi:bi + 1].contiguous()
+        res = dart.dart_sma_bwd_rms(row(d["Q"]), row(d["C"]), row(d["E"]), row(dHr), row(score), row(d["gate"]),
+                                    row(g["R_rms"]), row(g["lse_rms"]), row(g["dout"]), S, EPS,
+                                    want_dgate=False, want_dw=True)
+        g[f"dwq{bi}"], g[f"dwe{bi}"] = res[5], res[6]
+        del res
+    torch.cuda.synchronize()
     del dHr, score
     # SSM branch
     g["Y_ssm"], dH_ssd, g["H_final"] = dart.dart_ssd_fwd(d["X"], d["B"], d["C"], d["A"], S, want_final=True)
@@ -161,6 +178,45 @@ def test_long_normalised_branch(run):
     acc["r"].check(TOL_SAME_INPUT["bf16"])
     for k in ("out", "R", "lse"):
         acc[k].check(TOL["bf16"])
+
+
+@pytest.mark.parametrize("bi", [0, 1])
+def test_long_normalised_backward(run, bi):
+    """Every gradient of the normalised branch for batch row bi, on the
+    GPU's chunk memories with the oracle's own R and lse; the weight
+    gradients against the GPU call on that row alone."""
+    cfg, h = run
+    S, N, P = cfg["chunk"], cfg["d_state"], cfg["d_head"]
+    acc = {k: MaxErr(k) for k in ("dQ", "dC", "dE", "d_dH", "dgate", "dw_q", "dw_e")}
+    dwq, dwe = np.zeros(N), np.zeros(P)
+    for hh in range(cfg["nheads"]):
+        x = head_inputs(cfg, h, bi, hh)
+        mem = to_oracle_mem(f64(h["dH"][bi, hh]))
+        R, lse = O.sma_head_rms(x["Q"], x["C"], x["E"], mem, S, EPS)
+        _, dR, dg = O.gated_residual_backward(f64(h["dout"][bi, :, hh]), x["gate"], R)
+        dQ, dC, dE, ddH, wq, we = O.sma_head_backward_rms(x["Q"], x["C"], x["E"], mem, S, EPS, dR, lse,
+                                                          np.ones(N), np.ones(P))
+        gi = hh // (cfg["nheads"] // cfg["ngroups"])   # G = H here: no group sums
+        acc["dQ"].add(f64(h["dQ_rms"][bi, :, gi]), dQ, hh)
+        acc["dC"].add(f64(h["dC_rms"][bi, :, gi]), dC, hh)
+        acc["dE"].add(f64(h["dE_rms"][bi, :, gi]), dE, hh)
+        acc["d_dH"].add(to_oracle_mem(f64(h["ddH_rms"][bi, hh])), ddH, hh)
+        acc["dgate"].add(f64(h["dgate_rms"][bi, :, hh]), dg, hh)
+        dwq += wq
+        dwe += we
+    acc["dw_q"].add(f64(h[f"dwq{bi}"]), dwq)
+    acc["dw_e"].add(f64(h[f"dwe{bi}"]), dwe)
+    for a in acc.values():
+        a.check(TOL["bf16"])
+
+
+def test_long_normalised_weight_gradients_sum_over_rows(run):
+    """The call on both batch rows gives the sum of the per-row calls (up
+    to float32 rounding of the fixed-order sums)."""
+    cfg, h = run
+    for k in ("dwq", "dwe"):
+        both, parts = f64(h[k]), f64(h[k + "0"]) + f64(h[k + "1"])
+        assert np.abs(both - parts).max() <= 1e-5 * np.abs(parts).max(), k
 
 
 @pytest.mark.parametrize("bi", [0, 1])
