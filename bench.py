@@ -482,7 +482,7 @@ def time_mfma_probe(torch, dH, Q, steps, warmup, fwd_tflops):
     holds under dense matrix load, beside the 2.5 PF figure."""
     import ctypes
 
-    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "libdart_probe.so"))
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "probes", "libdart_probe.so"))
     probe.dart_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     ops = torch.cat([dH.reshape(-1)[:4096], Q.reshape(-1)[:4096]]).contiguous()
     blocks, iters = 512, 400
@@ -512,7 +512,7 @@ def time_read_probe(torch, buf, steps, warmup, decode_gbs):
     8 TB/s figure."""
     import ctypes
 
-    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "libdart_probe.so"))
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "probes", "libdart_probe.so"))
     probe.dart_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
@@ -589,7 +589,7 @@ def profile_kernels(launches=3):
 
     import ctypes
 
-    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "libdart_probe.so"))
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_memory_attention_amd", "probes", "libdart_probe.so"))
     probe.dart_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)

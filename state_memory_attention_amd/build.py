@@ -36,10 +36,12 @@ SOURCES = [
     "sma_bwd_rms_mfma.hip",
     "ssd.hip",
 ]
-# A plain 16-byte-vector copy kernel in its own library, used only to
-# calibrate hardware memory-traffic counters (bench.py --profile-kernels).
-PROBE_SOURCE = "probe_copy.hip"
-PROBE_LIB = os.path.join(PKG, "libdart_probe.so")
+# Measurement support, not part of the library: a plain 16-byte-vector copy
+# (calibrates the hardware memory-traffic counters), a streaming read and a
+# matrix-core loop (two yardsticks), in a library of their own under probes/.
+PROBE_DIR = os.path.join(PKG, "probes")
+PROBE_SOURCE = os.path.join(PROBE_DIR, "probe_copy.hip")
+PROBE_LIB = os.path.join(PROBE_DIR, "libdart_probe.so")
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for every HIP source.
@@ -55,7 +57,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [hipcc(), f"--offload-arch={ARCH}", *COMMON_FLAGS, "-I", INCLUDE, "-I", CSRC,
            *lang, "-c", os.path.join(CSRC, src), "-o", obj]
