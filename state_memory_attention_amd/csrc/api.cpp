@@ -683,7 +683,8 @@ int dart_sma_bwd_rms(const dart_dims_t* dims, int dtype, const void* Q, const vo
                         nullptr, nullptr)))
     return st;
   if (prod({s.b, s.H, s.M, (s.N * s.P + 255) / 256}) >= kMaxIndex || prod({s.b, s.H, (s.L + 3) / 4}) >= kMaxIndex ||
-      prod({s.b, s.H, s.M, s.N}) / 256 >= kMaxIndex || prod({s.b, s.L, s.G}) / 4 >= kMaxIndex)
+      prod({s.b, s.H, s.M}) >= kMaxIndex || prod({s.b, s.H, s.M, s.N}) / 256 >= kMaxIndex ||
+      prod({s.b, s.L, s.G}) / 4 >= kMaxIndex)
     return fail(DART_ERR_SHAPE, "b * H * M or b * H * L is too large for one launch");
   if (use_mfma(dtype, dims))
     return hip_status(dart::launch_sma_bwd_rms_mfma(s, eps, Q, C, E, dH, dH_score, w_q, w_e, gate, gpc, R, lse,

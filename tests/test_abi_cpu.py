@@ -362,6 +362,16 @@ def test_rms_backward_validation():
     assert bwd_rms(d, dtype=3) == -3
     assert bwd_rms(dims(L=0)) == 0 and bwd_rms(dims(b=0)) == 0
     assert D.lib().dart_sma_bwd_rms_workspace_bytes(None) == 0
+    # 2^31 chunk memories (one block each in the chain kernel): refused on the
+    # host (addresses spaced far enough apart for these buffer sizes)
+    far = [ctypes.c_void_p((k + 1) << 55) for k in range(24)]
+    big = D.Dims(1, 1 << 15, 1 << 16, 1 << 16, 128, 64, 1)
+    p = list(far[:20])
+    p[12] = p[13] = p[14] = None
+    st = D.lib().dart_sma_bwd_rms(ctypes.byref(big), 1, p[0], p[1], p[2], p[3], p[4], p[5], 1, 1e-6, p[12], p[13],
+                                  p[6], p[7], p[8], p[9], p[10], p[11], p[15], p[14], p[16], p[17], far[23],
+                                  1 << 62, None)
+    assert st == -2 and "too large" in last()
 
 
 def ssd(d, dtype=1, over=None, ws_bytes=1 << 40):
