@@ -133,6 +133,14 @@ FWD_CASES = [
     (dict(batch=2, seqlen=1100, nheads=4, ngroups=2, d_state=128, d_head=64, chunk=128, dtype="bf16"), True, True),
     (dict(batch=1, seqlen=2048, nheads=2, ngroups=1, d_state=128, d_head=64, chunk=256, dtype="bf16"), False, False),
     (dict(batch=1, seqlen=600, nheads=2, ngroups=2, d_state=32, d_head=48, chunk=64, dtype="bf16"), True, False),
+    # the matrix-core forward at chunks of 1 and 3 tokens, the evaluation-time
+    # size 32 (a 128-token tile spans four chunks), 96 (chunk starts inside a
+    # wave's 32 tokens) and a sequence shorter than one wave
+    (dict(batch=1, seqlen=151, nheads=2, ngroups=1, d_state=128, d_head=64, chunk=1, dtype="bf16"), True, True),
+    (dict(batch=1, seqlen=403, nheads=3, ngroups=3, d_state=128, d_head=64, chunk=3, dtype="bf16"), False, False),
+    (dict(batch=2, seqlen=1061, nheads=2, ngroups=2, d_state=128, d_head=64, chunk=32, dtype="bf16"), True, True),
+    (dict(batch=1, seqlen=1000, nheads=4, ngroups=2, d_state=128, d_head=64, chunk=96, dtype="bf16"), False, True),
+    (dict(batch=2, seqlen=20, nheads=2, ngroups=1, d_state=128, d_head=64, chunk=8, dtype="bf16"), True, False),
 ]
 
 
