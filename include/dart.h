@@ -49,7 +49,8 @@
  *     fully overwritten.  `out` may alias `Y_ssm` (same pointer, same layout);
  *     no other aliasing is allowed.
  *   - Every pointer must be 16-byte aligned (dart_decode_state_update
- *     relaxes this for its per-token inputs, see there).
+ *     relaxes this for its per-token inputs, and the decode calls for a
+ *     scalar gate; see there).
  *
  * Errors:
  *   - Calls return DART_OK (0) or a negative dart_status_t.  On failure the
@@ -141,6 +142,8 @@ int dart_sma_fwd(const dart_dims_t* dims, int dtype, const void* Q, const void* 
  *   R [b][H][P] float32 (optional), lse [b][H] float32 (optional)
  *   workspace: device scratch of at least dart_sma_decode_workspace_bytes()
  *              bytes; contents on entry are ignored.
+ * A scalar gate ([b][H]) needs only its element's alignment, so the gate of
+ * one token sliced from a [b][L][H] tensor is accepted as it is.
  * n_b = 0 gives R = 0, lse = -inf, out = y_ssm. */
 int dart_sma_decode(const dart_dims_t* dims, int dtype, int64_t max_chunks, const void* q,
                     const void* c, const void* e, const void* cache, const int32_t* n_chunks,

@@ -384,7 +384,15 @@ int sma_decode_impl(const dart_dims_t* dims, int dtype, int64_t max_chunks, bool
   if (rms && ((st = check_opt_align(r_cache, "r_cache")) || (st = check_weight(w_q, "w_q")) ||
               (st = check_weight(w_e, "w_e"))))
     return st;
-  if ((st = check_ptrs({bq, bc, be, by, bg, bo}))) return st;
+  // a scalar gate is read one element at a time: its element's alignment suffices
+  if ((st = check_ptrs({bq, bc, be, by}))) return st;
+  if (gpc && (st = check_ptrs({bg}))) return st;
+  if (!gpc) {
+    if (gate == nullptr) return fail(DART_ERR_NULL, "gate is NULL");
+    if (((uintptr_t)gate % (uintptr_t)es) != 0)
+      return fail(DART_ERR_ALIGN, "gate is not aligned to its element size");
+  }
+  if ((st = check_ptrs({bo}))) return st;
   if ((st = check_opt_align(cache, "cache")) || (st = check_opt_align(R, "R")) ||
       (st = check_opt_align(lse, "lse")) || (st = check_opt_align(n_chunks, "n_chunks")))
     return st;

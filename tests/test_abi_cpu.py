@@ -126,6 +126,23 @@ def test_decode_validation():
     assert dec(d, n_chunks=ctypes.c_void_p((11 << 40) + 2)) == -6
 
 
+def test_decode_scalar_gate_alignment():
+    # a scalar gate ([b][H]) needs only its element's alignment: a 2-byte
+    # offset passes the gate check and the call stops at the NULL output
+    # (nothing launches); a 1-byte offset, or a per-channel gate off a
+    # 16-byte boundary, is refused
+    d = dims()
+
+    def call(gate, gpc, out=None):
+        return D.lib().dart_sma_decode(ctypes.byref(d), 1, 8, ADDR[0], ADDR[1], ADDR[2], ADDR[3], None, ADDR[4],
+                                       gate, gpc, out, None, None, ADDR[10], GiB, None)
+
+    assert call(ctypes.c_void_p(ADDR[5].value + 2), 0) == -1 and "out" in last()
+    assert call(ctypes.c_void_p(ADDR[5].value + 1), 0) == -6 and "gate" in last()
+    assert call(ctypes.c_void_p(ADDR[5].value + 2), 1) == -6 and "gate" in last()
+    assert call(None, 0, ADDR[6]) == -1 and "gate" in last()
+
+
 def dec_noalloc(d, max_chunks=8, dtype=1, cache=ADDR[3], out=ADDR[6]):
     return D.lib().dart_sma_decode_noalloc(ctypes.byref(d), dtype, max_chunks, ADDR[0], ADDR[1], ADDR[2],
                                            cache, None, ADDR[4], ADDR[5], 1, out, None, None, None)

@@ -110,3 +110,27 @@ def test_mfma_matches_general_kernel():
     a = run_dec(d, "bf16", [70, 3, 0, 33], path=dart.DART_PATH_AUTO)
     b = run_dec(d, "bf16", [70, 3, 0, 33], path=dart.DART_PATH_GENERAL)
     assert err(a[1], b[1]) <= 1e-4 and err(a[2], b[2]) <= 1e-4
+
+
+@pytest.mark.parametrize("dt,N,P", [("bf16", 128, 64), ("f32", 16, 16)])
+def test_decode_scalar_gate_token_slice(dt, N, P):
+    """A scalar gate sliced for one token from a [1][L][H] tensor (here a
+    30-byte offset: H = 5, token 3) is accepted, and gives exactly what an
+    aligned copy of it gives, plain and normalised branch."""
+    b, H, G, Mx, L, tok = 1, 5, 5, 9, 7, 3
+    d = synth.draw_decode(batch=b, nheads=H, ngroups=G, max_chunks=Mx, d_state=N, d_head=P, dtype=dt, seed=61,
+                          gate_per_channel=False)
+    seq = torch.rand((b, L, H), device="cuda").to(torch.bfloat16 if dt == "bf16" else torch.float32)
+    gate = seq[:, tok]
+    assert gate.is_contiguous() and gate.data_ptr() % 16 != 0
+    args = (dev(d["q"], dt), dev(d["c"], dt), dev(d["e"], dt), dev(d["cache"], dt))
+    y = dev(d["y"], dt)
+    n = torch.tensor([6], dtype=torch.int32, device="cuda")
+    a = dart.dart_sma_decode(*args, y, gate, n_chunks=n, want_R=True, want_lse=True)
+    c = dart.dart_sma_decode(*args, y, gate.clone(), n_chunks=n, want_R=True, want_lse=True)
+    r_cache, _ = dart.dart_chunk_rms(args[3].reshape(b, H, Mx, P, N), Mx, 1, 1e-6, want_score=False)
+    an = dart.dart_sma_decode_rms(*args, r_cache, y, gate, 1e-6, n_chunks=n, want_R=True, want_lse=True)
+    cn = dart.dart_sma_decode_rms(*args, r_cache, y, gate.clone(), 1e-6, n_chunks=n, want_R=True, want_lse=True)
+    torch.cuda.synchronize()
+    for x, z in zip(a + an, c + cn):
+        assert torch.equal(x, z)
