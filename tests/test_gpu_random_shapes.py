@@ -1,6 +1,6 @@
 """Seeded random-shape sweep of every entry point against the fp64 oracle.
 
-Each case draws its shape from a fixed seed: half of the cases at the
+Each of the 64 cases draws its shape from a fixed seed: half of them at the
 matrix-core shape (bf16, N = 128, P = 64), the rest at any N, P <= 256 in
 float32 or bf16 (general kernels); H in 1..4 with every divisor for G, b in
 {1, 2}, S in {1, 3, 8, 32, 64, 96, 128, 256}, L up to 600 (up to 150 for
@@ -32,7 +32,7 @@ from gpu_helpers import TOL, TOL_SAME_INPUT, dev, err, host, say, to_oracle_mem
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-6
-N_CASES = 24
+N_CASES = 64
 
 
 def draw_case(i):
