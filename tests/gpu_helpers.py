@@ -98,3 +98,18 @@ class MaxErr:
         say(f"  {self.name}: {e:.2e} over {self.count} entries (largest difference at {self.worst})")
         assert e <= tol, (self.name, e, self.worst)
         return e
+
+
+def same(x, y, what):
+    """Bitwise equality of two GPU results; on a mismatch, say how many
+    elements differ, where (the first three indices of the differing
+    elements, up to twelve of them) and by how much."""
+    if torch.equal(x, y):
+        return
+    diff = x != y
+    idx = diff.nonzero()
+    n = int(diff.sum())
+    where = sorted(set(tuple(r) for r in idx[:, :3].tolist()))[:12]
+    md = float((x.float() - y.float()).abs().max())
+    raise AssertionError(f"{what}: {n} of {x.numel()} elements differ, first (i0, i1, i2) {where}, "
+                         f"max |diff| {md:.3e}")

@@ -25,7 +25,7 @@ import oracle as O
 import state_memory_attention_amd as dart
 from state_memory_attention_amd import synth
 
-from gpu_helpers import TOL, TOL_SAME_INPUT, MaxErr, f64, say, to_oracle_mem
+from gpu_helpers import TOL, TOL_SAME_INPUT, MaxErr, f64, same, say, to_oracle_mem
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def run():
     g["out"], g["R"], g["lse"] = dart.dart_sma_fwd(d["Q"], d["C"], d["E"], g["dH"], d["Y"], d["gate"], S,
                                                    want_R=True, want_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out_bench, g["out"])
+    same(out_bench, g["out"], "out of the two forward launches (b, t, h)")
     del out_bench
     # backward
     g["dout"] = synth.draw_grad_torch((b, L, H, P), "bf16", seed=3)
@@ -59,7 +59,7 @@ def run():
     g["out_rms"], g["R_rms"], g["lse_rms"] = dart.dart_sma_fwd_rms(
         d["Q"], d["C"], d["E"], dHr, score, d["Y"], d["gate"], S, EPS, want_R=True, want_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(dHr, g["dH"]), "dart_chunk_states_rms memories differ from dart_chunk_states"
+    same(dHr, g["dH"], "dart_chunk_states_rms memories against dart_chunk_states (b, h, c)")
     # its backward, the benchmark's call, then each batch row alone for the
     # weight gradients (sums over every row and head)
     (g["dQ_rms"], g["dC_rms"], g["dE_rms"], g["ddH_rms"], g["dgate_rms"], g["dwq"], g["dwe"]) = \
@@ -77,7 +77,7 @@ def run():
     # SSM branch
     g["Y_ssm"], dH_ssd, g["H_final"] = dart.dart_ssd_fwd(d["X"], d["B"], d["C"], d["A"], S, want_final=True)
     torch.cuda.synchronize()
-    assert torch.equal(dH_ssd, g["dH"]), "dart_ssd_fwd memories differ from dart_chunk_states"
+    same(dH_ssd, g["dH"], "dart_ssd_fwd memories against dart_chunk_states (b, h, c)")
     del dH_ssd
     for k, v in g.items():
         assert not torch.isnan(v).any(), k

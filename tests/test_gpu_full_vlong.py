@@ -10,7 +10,7 @@ import oracle as O
 import state_memory_attention_amd as dart
 from state_memory_attention_amd import synth
 
-from gpu_helpers import TOL, MaxErr, f64, say, to_oracle_mem
+from gpu_helpers import TOL, MaxErr, f64, same, say, to_oracle_mem
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def run():
     out, R, lse = dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S,
                                     want_R=True, want_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out_bench, out)
+    same(out_bench, out, "out of the two forward launches (b, t, h)")
     for t in (dH, out, R, lse):
         assert not torch.isnan(t).any()
     host = {k: v.cpu() for k, v in d.items()}
