@@ -4,7 +4,9 @@
 
 Each source is compiled to an object under ``_build/`` in parallel, then
 linked into ``state_memory_attention_amd/libdart.so``.  The library is always
-rebuilt: objects are not reused between calls.
+rebuilt: objects are not reused between calls.  The measurement probes go
+into a library of their own, and a plain C program that calls libdart.so
+through ``include/dart.h`` (``tests/c_abi/``) is built with gcc last.
 """
 from __future__ import annotations
 
@@ -84,6 +86,29 @@ def _link(objs, out, verbose):
     os.replace(tmp, out)
 
 
+# A plain C program that uses libdart.so through include/dart.h and the HIP
+# runtime only (tests/test_gpu_c_abi.py runs it on the GPU).
+C_SMOKE_SOURCE = os.path.join(ROOT, "tests", "c_abi", "dart_c_smoke.c")
+C_SMOKE_BIN = os.path.join(ROOT, "tests", "c_abi", "dart_c_smoke.bin")
+
+
+def _build_c_smoke(verbose: bool) -> None:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for tests/c_abi/dart_c_smoke.c")
+    rel = os.path.relpath(PKG, os.path.dirname(C_SMOKE_BIN))
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I",
+           os.path.join(rocm, "include"), C_SMOKE_SOURCE, "-L", PKG, "-ldart", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-lm", f"-Wl,-rpath,$ORIGIN/{rel}", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}",
+           "-o", C_SMOKE_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C program failed to build:\n{r.stdout}{r.stderr}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + [PROBE_SOURCE]
@@ -91,6 +116,7 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     _link(objs[:-1], LIB, verbose)
     _link(objs[-1:], PROBE_LIB, verbose)
+    _build_c_smoke(verbose)
     return LIB
 
 
