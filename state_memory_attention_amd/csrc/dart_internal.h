@@ -112,11 +112,17 @@ hipError_t launch_sma_bwd_a_mfma(const Shape& s, const void* Q, const void* C, c
 // Pass BC modes: both gradients from dH; the Q side only, from the float16
 // score memory of the normalised branch (rho: [b][L][G][2] RMSNorm factors;
 // Q_norm: Q when each group has one head, and dQ then goes through the
-// RMSNorm backward in the epilogue, else NULL); the C side only.
+// RMSNorm backward in the epilogue, else NULL); the C side only.  memT: the
+// memories transposed by launch_mem_transpose ([b][H][M][N][P]).
 constexpr int kBcBoth = 0, kBcScoreQ = 1, kBcC = 2;
-hipError_t launch_sma_bwd_bc_mfma(const Shape& s, int mode, const void* E, const void* dR, const void* mem,
+hipError_t launch_sma_bwd_bc_mfma(const Shape& s, int mode, const void* E, const void* dR, const void* memT,
                                   const float* pd, const float* rho, const void* Q_norm, float* dQ, float* dC,
                                   int out_heads, hipStream_t st);
+// out[m][n][p] = in[m][p][n] for `count` memories of P = 64 rows of N = 128
+// two-byte entries (16-byte aligned)
+hipError_t launch_mem_transpose(const void* in, void* out, int64_t count, hipStream_t st);
+// byte offset of the transposed memories in the MFMA backward's workspace
+size_t sma_bwd_memt_offset(const Shape& s);
 // ddH_score: nullptr (both terms into ddH) or a buffer for the score term
 hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, const void* C,
                                  const void* Q, const float* pd, float* ddH, float* ddH_score,

@@ -463,7 +463,8 @@ constexpr int kSlotBC = kMemBytes + kPdBytes;     // one chunk memory + its weig
 struct BwdBCArgs {
   const bf16_t* E;
   const bf16_t* dR;    // [b][L][H][P], from pass A
-  const void* mem;     // chunk memories: dH (bf16), or the float16 score memory (Q side only)
+  const void* memT;    // chunk memories transposed, [b][H][M][N][P]: dH (bf16), or the
+                       // float16 score memory (Q side only)
   const float* pd;     // [b][H][M][2][L], from pass A (p, dl / sqrt(N))
   const float* rho;    // [b][L][G][2] (Q side on the score memory): RMSNorm factors of Q_t, E_t
   const bf16_t* Qn;    // score-memory mode with one head per group: Q, and dQ is written
@@ -476,31 +477,12 @@ struct BwdBCArgs {
   float inv_sqrt_n;
 };
 
-// Byte offset of bf16 entry (row p, column n) of a chunk memory staged for the
-// transposing reads: 256-byte rows of 16-byte pieces, piece ^ ((p & 3) << 2).
-__device__ __forceinline__ uint32_t tr_off(int p, int n) {
-  return (uint32_t)(p * 256 + ((((n >> 3) ^ ((p & 3) << 2))) << 4) + (n & 7) * 2);
-}
-
-// Eight transposing reads (4 bf16 = 8 bytes each) that return together; the
-// tiles read are complete by construction (explicit wait + barrier), and the
-// asm waits for its own results (the compiler's form of this read would drain
-// every direct-to-LDS load in flight first).
-__device__ __forceinline__ void ld_tr8(uint64_t (&o)[8], const uint32_t (&ad)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
-        "=&v"(o[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
-      : "memory");
+// Byte offset of 16-byte piece `piece` (0..7, p = 8 piece .. +7) of row n of a
+// staged transposed memory: 128-byte rows, pieces XOR-swizzled by (n >> 1) & 7,
+// so that the operand reads below (16 lanes at a time on 16 consecutive rows,
+// or 8 at a time) touch every bank once.
+__device__ __forceinline__ uint32_t memt_off(int n, int piece) {
+  return (uint32_t)(n * 128 + ((piece ^ ((n >> 1) & 7)) << 4));
 }
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -536,11 +518,24 @@ __device__ __forceinline__ bf16x8_t scale8(bf16x8_t x, float s) {
 // sum_c dHs_c (E_t rho_e,t dl_tc / sqrt(N)) takes the E operand scaled by the
 // token's RMSNorm factor: the pd row then holds dl / sqrt(N) rho_q rho_e and is
 // divided by rho_q here), kBcC (dC only, from dH).
+//
+// The memories arrive transposed (rows n, p contiguous), so the MFMA A
+// operand (rows n, k = p) is one plain 16-byte LDS read per lane, issued one
+// k-step ahead of the MFMAs that use it.  Both gradients (two accumulator sets)
+// keep two waves per SIMD and a 4-deep ring; one gradient needs fewer than 168
+// registers, and a 3-deep ring (51 KB) fits three blocks per CU.
 template <int kMode>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+constexpr int bc_ring() { return kMode == kBcBoth ? 4 : 3; }
+
+template <int kMode>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kMode == kBcBoth ? 2 : 3, kMode == kBcBoth ? 2 : 3)))
 void sma_bwd_bc_kernel(BwdBCArgs a) {
   constexpr bool kDoQ = kMode != kBcC, kDoC = kMode != kBcScoreQ;
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing * kSlotBC];
+  constexpr int kR = bc_ring<kMode>();
+  // One LDS object: with a single object the compiler adds no wait of its own
+  // for the direct-to-LDS loads in flight before the ring's plain reads.
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kR * kSlotBC];
 
   const int blk = blockIdx.x;
   const TileItem item = head_major_tile(blk, a.n_tiles);
@@ -550,7 +545,6 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
   const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int grp16 = (lane >> 4) & 1, j16 = lane & 15;
   const int64_t t0 = (int64_t)tile * kTile;
   const int64_t t_last = (t0 + kTile < a.L ? t0 + kTile : a.L) - 1;
   const int n_hist = (int)(t_last / a.S);
@@ -559,21 +553,22 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
   const int64_t tc = tok_ok ? t : a.L - 1;
   const int64_t row0 = (int64_t)b * a.L;
 
-  // Slot s = chunk s in ring buffer s % 4: the memory (rows p = 16w .. 16w+15
-  // loaded by wave w, 4 loads) and the (p, dl) pair of the wave's 32 tokens
-  // (one 4-byte-per-lane load: lanes 0-31 p, lanes 32-63 dl).  Five loads per
-  // wave per slot.
-  const uint8_t* mem_head = (const uint8_t*)a.mem + (int64_t)bh * a.M * kMemBytes;
-  const uint32_t mem_dma = (16 * wave + (lane >> 4)) * 256;
+  // Slot s = chunk s in ring buffer s % kR: the transposed memory (rows
+  // n = 32w .. 32w+31 loaded by wave w, 4 loads of 8 rows; one load writes
+  // 1 KB contiguously, so the swizzle is applied on the global side: the lane
+  // that fills physical piece f of row n fetches logical piece
+  // f ^ ((n >> 1) & 7)) and the (p, dl) pair of the wave's 32 tokens (one
+  // 4-byte-per-lane load: lanes 0-31 p, lanes 32-63 dl).  Five loads per wave
+  // per slot.
+  const uint8_t* mem_head = (const uint8_t*)a.memT + (int64_t)bh * a.M * kMemBytes;
   const uint32_t pd_lane = (uint32_t)((half ? a.L : 0) + t0 + 32 * wave + col) * 4;
   auto issue = [&](int s) {
-    uint8_t* dst = s_ring + (s % kRing) * kSlotBC;
+    uint8_t* dst = s_ring + (s % kR) * kSlotBC;
     const auto rs = buf_rsrc(mem_head + (int64_t)s * kMemBytes, kMemBytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wave + 4 * i + (lane >> 4);
-      buf_dma16(rs, mem_dma + i * 1024 + (((lane & 15) ^ ((row & 3) << 2)) << 4),
-                dst + wave * 16 * 256 + i * 4 * 256);
+      const int row = 32 * wave + 8 * i + (lane >> 3);
+      buf_dma16(rs, (uint32_t)(row * 128 + (((lane & 7) ^ ((row >> 1) & 7)) << 4)), dst + wave * 4096 + i * 1024);
     }
     const auto rp = buf_rsrc(a.pd + ((int64_t)bh * a.M + s) * 2 * a.L, (uint32_t)(2 * a.L * 4));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -583,9 +578,11 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
   // B operands: lane holds token `col`, p = 16 ks + 8 half + 0..7.  The E
   // and dR rows of the wave's 32 tokens are staged whole (128-byte rows,
   // 16-byte pieces XOR-swizzled by the row) in the wave's parts of ring
-  // buffers 2 and 3 while slots 0 and 1 load; slot 2 follows once they are in
-  // registers (this wave's part of it covers exactly the bytes its E rows
-  // occupied; buffer 3 takes slot 3 only after the loop's first barrier).
+  // buffer 2 (E, or dR with one gradient) and 3 (dR with both) while slots 0
+  // and 1 load.  This wave's part of slot 2 and 3 covers exactly the bytes its
+  // staged rows occupied; slot 2 follows once they are in registers (with
+  // both gradients; with one, slot 2 and buffer 3 come in the loop, after its
+  // first barrier).
   bf16x8_t eop[4], rop[4];
   // score-memory mode: 1 / rho_q of this lane's token (the pd row's dl
   // carries rho_q rho_e; the Q-side operand needs rho_e only)
@@ -599,7 +596,7 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
     if (1 < n_hist) issue(1);
     const int last_r = (int)(a.L - 1 - t0 < kTile - 1 ? a.L - 1 - t0 : kTile - 1);
     uint8_t* const s_se = s_ring + 2 * kSlotBC + wave * 4096;
-    uint8_t* const s_sr = s_ring + 3 * kSlotBC + wave * 4096;
+    uint8_t* const s_sr = s_ring + (kDoQ ? 3 : 2) * kSlotBC + wave * 4096;
     const auto rse = buf_rsrc(wave_uniform(a.E + ((row0 + t0) * a.G + g) * kP), (uint32_t)(last_r * a.G * kP + kP) * 2);
     const auto rsr = buf_rsrc(wave_uniform(a.dR + ((row0 + t0) * a.H + h) * kP), (uint32_t)(last_r * a.H * kP + kP) * 2);
 #pragma unroll
@@ -617,76 +614,74 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
       if (kDoC) rop[ks] = *(const bf16x8_t*)(s_sr + o);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    if (2 < n_hist) issue(2);
+    if (kR == 4 && 2 < n_hist) issue(2);
   }
 
-  // A operand (dH: rows n, k = p): lane (column j16 + 16 grp16 of row block
-  // rb, k-octet `half`) addresses row p = 16 ks + 8 half + 4 hh + j16/4 at
-  // column n = 32 rb + 16 grp16 + 4 (j16 % 4).  The swizzle term depends only
-  // on p & 3 = (j16 / 4) & 3, so each row block has one per-lane base.
-  uint32_t abase[4];
+  // A operand (rows n, k = p): lane reads row n = 32 rb + col, logical piece
+  // 2 ks + half; the swizzle term depends on col only, so one per-lane offset
+  // per k-step and the row block as an immediate.
+  uint32_t aoff[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) abase[rb] = tr_off(8 * half + (j16 >> 2), 32 * rb + 16 * grp16 + 4 * (j16 & 3));
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = memt_off(col, 2 * ks + half);
 
   f32x16_t dq[4], dc[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) dq[rb] = dc[rb] = f32x16_t{};
 
   for (int j = 0; j < n_hist; ++j) {
-    // slot j landed (its 5 loads) in every wave's part; slot j-1 free
+    // slot j landed (its 5 loads) in every wave's part; slot j-1 free.  Slots
+    // j+1 .. j+kR-2 that exist may stay in flight.
     asm volatile("" ::: "memory");
-    if (n_hist - 1 - j >= 2)
+    if (kR == 4 && n_hist - 1 - j >= 2)
       __builtin_amdgcn_s_waitcnt(0x0f7a);      // vmcnt(10)
-    else if (n_hist - 1 - j == 1)
+    else if (n_hist - 1 - j >= 1)
       __builtin_amdgcn_s_waitcnt(0x0f75);      // vmcnt(5)
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (j + kRing - 1 < n_hist) issue(j + kRing - 1);
+    if (j + kR - 1 < n_hist) issue(j + kR - 1);
 
-    const uint8_t* slot = s_ring + (j % kRing) * kSlotBC;
+    const uint8_t* slot = s_ring + (j % kR) * kSlotBC;
     const float* wpd = (const float*)(slot + kMemBytes + wave * 256);
     const float ps = wpd[col], dls = wpd[32 + col];
-    const uint32_t sb = lds_addr(slot);
+    // The burst runs at raised priority, and a wave whose burst is under way
+    // outranks one about to start its own (as in the forward), so the waves
+    // sharing a SIMD take the matrix core in turns.
     __builtin_amdgcn_s_setprio(1);
+    bf16x8_t nx[4];
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {           // two k-steps per read batch
-      uint32_t ad[8];
-      uint64_t rd[8];
+    for (int rb = 0; rb < 4; ++rb) nx[rb] = *(const bf16x8_t*)(slot + aoff[0] + rb * 4096);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ks = 2 * kp + (i >> 2), rb = i & 3;
-        ad[i] = sb + abase[rb] + (uint32_t)(16 * ks) * 256;  // hh = 0 half of the fragment
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t av[4], be, br;
+      f16x8_t beh;
+      if (kMode == kBcScoreQ) beh = scale8h(eop[ks], dls * irq);
+      if (kMode == kBcBoth) be = scale8(eop[ks], dls);
+      if (kDoC) br = scale8(rop[ks], ps);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) av[rb] = nx[rb];
+      if (ks < 3) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) nx[rb] = *(const bf16x8_t*)(slot + aoff[ks + 1] + rb * 4096);
       }
-      ld_tr8(rd, ad);
-      uint32_t ad2[8];
-      uint64_t rd2[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ad2[i] = ad[i] + 4 * 256;   // hh = 1: rows + 4
-      ld_tr8(rd2, ad2);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int ks = 2 * kp + q;
-        f16x8_t beh;
-        bf16x8_t be, br;
-        if (kMode == kBcScoreQ) beh = scale8h(eop[ks], dls * irq);
-        if (kMode == kBcBoth) be = scale8(eop[ks], dls);
-        if (kDoC) br = scale8(rop[ks], ps);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int i = 4 * q + rb;
-          const uint4 av = make_uint4((uint32_t)rd[i], (uint32_t)(rd[i] >> 32), (uint32_t)rd2[i],
-                                      (uint32_t)(rd2[i] >> 32));
-          if (kMode == kBcScoreQ) {
-            dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, av), beh, dq[rb], 0, 0, 0);
-          } else {
-            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
-            if (kDoQ) dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, be, dq[rb], 0, 0, 0);
-            if (kDoC) dc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, br, dc[rb], 0, 0, 0);
-          }
+      for (int rb = 0; rb < 4; ++rb) {
+        if (kMode == kBcScoreQ) {
+          dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, av[rb]), beh, dq[rb], 0, 0, 0);
+        } else {
+          if (kDoQ) dq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[rb], be, dq[rb], 0, 0, 0);
+          if (kDoC) dc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[rb], br, dc[rb], 0, 0, 0);
         }
       }
+      if (ks == 0) __builtin_amdgcn_s_setprio(2);
+    }
+    // burst order: [4 LDS reads for step k+1][the MFMAs of step k], k = 0..3
+    // (left alone, the scheduler sinks each read to just before its use)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, (kDoQ && kDoC) ? 8 : 4, 0);       // MFMA
     }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -740,13 +735,13 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
 
 }  // namespace
 
-hipError_t launch_sma_bwd_bc_mfma(const Shape& s, int mode, const void* E, const void* dR, const void* mem,
+hipError_t launch_sma_bwd_bc_mfma(const Shape& s, int mode, const void* E, const void* dR, const void* memT,
                                   const float* pd, const float* rho, const void* Q_norm, float* dQ, float* dC,
                                   int out_heads, hipStream_t st) {
   BwdBCArgs a;
   a.E = (const bf16_t*)E;
   a.dR = (const bf16_t*)dR;
-  a.mem = mem;
+  a.memT = memT;
   a.pd = pd;
   a.rho = rho;
   a.Qn = (const bf16_t*)Q_norm;
@@ -1082,18 +1077,64 @@ hipError_t launch_sma_bwd_d_mfma(const Shape& s, const void* dR, const void* E, 
 // Workspace of the MFMA backward: (p, dl) rows [b][H][M][2][L] float32, dR
 // [b][L][H][P] bfloat16 and, for grouped heads, per-head dQ, dC [b][L][H][N]
 // and dE [b][L][H][P] float32 (summed over the group at the end).
+// ---------------------------------------------------------------------------
+// Chunk memories transposed for pass BC: out[m][n][p] = in[m][p][n], 64 x 128
+// two-byte entries per memory.  A thread moves an 8 x 8 tile (eight 16-byte
+// rows in, eight out), two memories per block of 256 threads.
+// ---------------------------------------------------------------------------
+namespace {
+
+__global__ __launch_bounds__(256) void mem_transpose_kernel(const uint4* in, uint4* out, int64_t count) {
+  const int64_t m = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (m >= count) return;
+  const int t = threadIdx.x & 127, nb = t & 15, pb = t >> 4;   // n = 8 nb .. +7, p = 8 pb .. +7
+  const uint4* src = in + m * (kMemBytes / 16) + (pb * 8) * 16 + nb;
+  uint4 r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = src[i * 16];   // row p = 8 pb + i
+  // entry c (n = 8 nb + c) of row i: 16-bit half c % 2 of word c / 2
+  auto el = [&](int i, int c) -> uint32_t {
+    const uint32_t w = (c >> 1) == 0 ? r[i].x : (c >> 1) == 1 ? r[i].y : (c >> 1) == 2 ? r[i].z : r[i].w;
+    return (c & 1) ? (w >> 16) : (w & 0xffffu);
+  };
+  uint4* dst = out + m * (kMemBytes / 16) + (nb * 8) * 8 + pb;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint4 o;
+    o.x = el(0, c) | (el(1, c) << 16);
+    o.y = el(2, c) | (el(3, c) << 16);
+    o.z = el(4, c) | (el(5, c) << 16);
+    o.w = el(6, c) | (el(7, c) << 16);
+    dst[c * 8] = o;                                   // row n = 8 nb + c
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mem_transpose(const void* in, void* out, int64_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  mem_transpose_kernel<<<dim3((unsigned)((count + 1) / 2)), dim3(256), 0, st>>>((const uint4*)in, (uint4*)out,
+                                                                                 count);
+  return hipGetLastError();
+}
+
 // Every part starts on a 256-byte boundary: dR takes 16-byte stores and
-// 16-byte direct-to-LDS loads, and the per-head partials 16-byte stores.
+// 16-byte direct-to-LDS loads, the per-head partials 16-byte stores, and the
+// transposed memories 16-byte stores and direct-to-LDS loads.
 namespace {
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 size_t pd_bytes_of(const Shape& s) { return round256((size_t)(2 * s.b * s.H * s.M * s.L) * 4); }
 size_t dr_bytes_of(const Shape& s) { return round256((size_t)(s.b * s.L * s.H * s.P) * 2); }
+size_t part_bytes_of(const Shape& s) {
+  return s.H != s.G ? round256((size_t)(s.b * s.L * s.H * (2 * s.N + s.P)) * 4) : 0;
+}
 }  // namespace
 
+// Layout: (p, dl) rows | dR | per-head partials (grouped heads) | dH transposed.
+size_t sma_bwd_memt_offset(const Shape& s) { return pd_bytes_of(s) + dr_bytes_of(s) + part_bytes_of(s); }
+
 size_t sma_bwd_mfma_workspace_bytes(const Shape& s) {
-  size_t bytes = pd_bytes_of(s) + dr_bytes_of(s);
-  if (s.H != s.G) bytes += (size_t)(s.b * s.L * s.H * (2 * s.N + s.P)) * 4;
-  return bytes;
+  return sma_bwd_memt_offset(s) + round256((size_t)(s.b * s.H * s.M) * kMemBytes);
 }
 
 hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, const void* E,
@@ -1109,10 +1150,12 @@ hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, con
   float* hc = grouped ? hq + s.b * s.L * s.H * s.N : dC;
   float* he = grouped ? hc + s.b * s.L * s.H * s.N : dE;
   const int heads = grouped ? (int)s.H : (int)s.G;
+  void* memT = w + sma_bwd_memt_offset(s);
   hipError_t e = launch_sma_bwd_a_mfma(s, Q, C, E, dH, gate, gate_pc, dout, R, lse, he, heads, pd, dR,
                                        dgate, st);
   if (e != hipSuccess) return e;
-  e = launch_sma_bwd_bc_mfma(s, kBcBoth, E, dR, dH, pd, nullptr, nullptr, hq, hc, heads, st);
+  if ((e = launch_mem_transpose(dH, memT, s.b * s.H * s.M, st)) != hipSuccess) return e;
+  e = launch_sma_bwd_bc_mfma(s, kBcBoth, E, dR, memT, pd, nullptr, nullptr, hq, hc, heads, st);
   if (e != hipSuccess) return e;
   e = launch_sma_bwd_d_mfma(s, dR, E, C, Q, pd, ddH, nullptr, st);
   if (e != hipSuccess || !grouped) return e;
@@ -1131,6 +1174,33 @@ hipError_t launch_sma_bwd_mfma(const Shape& s, const void* Q, const void* C, con
 namespace {
 
 constexpr int kGroupCS = 256;   // tokens per decay-weight group (one per thread)
+
+// Byte offset of bf16 entry (row p, column n) of a chunk memory staged for the
+// transposing reads: 256-byte rows of 16-byte pieces, piece ^ ((p & 3) << 2).
+__device__ __forceinline__ uint32_t tr_off(int p, int n) {
+  return (uint32_t)(p * 256 + ((((n >> 3) ^ ((p & 3) << 2))) << 4) + (n & 7) * 2);
+}
+
+// Eight transposing reads (4 bf16 = 8 bytes each) that return together; the
+// tiles read are complete by construction (explicit wait + barrier), and the
+// asm waits for its own results (the compiler's form of this read would drain
+// every direct-to-LDS load in flight first).
+__device__ __forceinline__ void ld_tr8(uint64_t (&o)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+        "=&v"(o[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+      : "memory");
+}
 
 struct CsBwdArgs {
   const bf16_t* X;

@@ -539,11 +539,15 @@ __global__ __launch_bounds__(256) void rms_norm_rows_kernel(int64_t rows, int K,
 // 256-byte boundary.
 size_t r256(size_t n) { return (n + 255) / 256 * 256; }
 struct RmsMfmaWs {
-  size_t rho, dT, wpq, wpe, part, total;
+  size_t memTs, rho, dT, wpq, wpe, part, total;
 };
+// The plain backward's workspace (with dH transposed at its end), then the
+// score memory transposed, the RMSNorm factors, dT, the weight-gradient rows
+// and the column-sum partials.
 RmsMfmaWs rms_mfma_layout(const Shape& s) {
   RmsMfmaWs w;
   size_t o = r256(sma_bwd_mfma_workspace_bytes(s));
+  w.memTs = o; o += r256((size_t)(s.b * s.H * s.M * s.P * s.N) * 2);
   w.rho = o;  o += r256((size_t)(2 * s.b * s.L * s.G) * 4);
   w.dT = o;   o += r256((size_t)(s.b * s.H * s.M * s.P * s.N) * 4);
   w.wpq = o;  o += r256((size_t)(s.b * s.H * s.M * s.N) * 4);
@@ -615,13 +619,17 @@ hipError_t launch_sma_bwd_rms_mfma(const Shape& s, float eps, const void* Q, con
   sma_bwd_rms_a_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = launch_sma_bwd_bc_mfma(s, kBcScoreQ, E, dR, dHs, pd, rho, grouped ? nullptr : Q, hq, nullptr, heads,
+  void* memT = w + sma_bwd_memt_offset(s);
+  void* memTs = w + lay.memTs;
+  const int64_t n_mem = s.b * s.H * s.M;
+  if ((e = launch_mem_transpose(dHs, memTs, n_mem, st)) != hipSuccess) return e;
+  if ((e = launch_mem_transpose(dH, memT, n_mem, st)) != hipSuccess) return e;
+  if ((e = launch_sma_bwd_bc_mfma(s, kBcScoreQ, E, dR, memTs, pd, rho, grouped ? nullptr : Q, hq, nullptr, heads,
                                   st)) != hipSuccess)
     return e;
-  if ((e = launch_sma_bwd_bc_mfma(s, kBcC, E, dR, dH, pd, nullptr, nullptr, nullptr, hc, heads, st)) != hipSuccess)
+  if ((e = launch_sma_bwd_bc_mfma(s, kBcC, E, dR, memT, pd, nullptr, nullptr, nullptr, hc, heads, st)) != hipSuccess)
     return e;
   if ((e = launch_sma_bwd_d_mfma(s, dR, E, C, Q, pd, ddH, dT, st)) != hipSuccess) return e;
-  const int64_t n_mem = s.b * s.H * s.M;
   rms_chain_kernel<<<dim3((unsigned)n_mem), dim3(kN), 0, st>>>(kN, kP, eps, (const bf16_t*)dH, dT, wq, we, ddH,
                                                                wpq, wpe);
   if ((e = hipGetLastError()) != hipSuccess) return e;

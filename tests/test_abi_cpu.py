@@ -216,9 +216,11 @@ def test_backward_validation():
     M = 2
     # the larger of the two layouts: (p, dl) per (chunk, token) and head, plus
     # per-head partials when heads are grouped; the MFMA path also keeps dR
-    # in bfloat16 (a 256-byte aligned section)
+    # in bfloat16 and the chunk memories transposed (256-byte aligned sections)
+    r256 = lambda n: -(-n // 256) * 256
     general = 4 * (2 * b * H * M * L + b * L * H * (2 * N + P))
-    mfma = -(-(4 * 2 * b * H * M * L + 2 * b * L * H * P) // 256) * 256 + 4 * b * L * H * (2 * N + P)
+    mfma = (r256(4 * 2 * b * H * M * L) + r256(2 * b * L * H * P) + r256(4 * b * L * H * (2 * N + P))
+            + r256(2 * b * H * M * P * N))
     assert need == max(general, mfma)
     assert bwd(d, ws=None) == -4 and "workspace" in last()
     assert bwd(d, ws_bytes=need - 1) == -4
@@ -234,7 +236,7 @@ def test_backward_validation():
     # ungrouped heads need no per-head partials
     d1 = dims(G=4)
     assert D.lib().dart_sma_bwd_workspace_bytes(ctypes.byref(d1)) == max(
-        4 * 2 * b * H * M * L, -(-(4 * 2 * b * H * M * L + 2 * b * L * H * P) // 256) * 256)
+        4 * 2 * b * H * M * L, r256(4 * 2 * b * H * M * L) + r256(2 * b * L * H * P) + r256(2 * b * H * M * P * N))
     assert D.lib().dart_sma_bwd_workspace_bytes(None) == 0
 
 
@@ -356,14 +358,25 @@ def test_rms_backward_validation():
     want = 4 * (up(2 * b * H * M * L) + up(b * L * H * N) + up(b * L * H * P) + up(b * L * H * N)
                 + up(2 * b * L * G) + up(b * H * M * P * N) + up(b * L * G * N) + up(b * L * G * P)
                 + up(split * (N + P)))
+    # the matrix-core layout: the plain backward's (with dH transposed), the
+    # score memory transposed, RMSNorm factors, dT, weight-gradient rows and
+    # column-sum partials (256-byte aligned sections)
+    r256 = lambda n: -(-n // 256) * 256
+
+    def mfma_rms(G):
+        part = r256(4 * b * L * H * (2 * N + P)) if G != H else 0
+        plain = r256(4 * 2 * b * H * M * L) + r256(2 * b * L * H * P) + part + r256(2 * b * H * M * P * N)
+        msplit = min(1024, max(1, -(-(b * H * M) // 512)))
+        return (r256(plain) + r256(2 * b * H * M * P * N) + r256(4 * 2 * b * L * G) + r256(4 * b * H * M * P * N)
+                + r256(4 * b * H * M * N) + r256(4 * b * H * M * P) + r256(4 * msplit * (N + P)))
     need = D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(d))
-    assert need == want
+    assert need == max(want, mfma_rms(G))
     # ungrouped heads: no per-head dC partials
     G1 = 4
     split1 = min(1024, max(1, -(-(b * L * G1) // 512)))
     want1 = 4 * (up(2 * b * H * M * L) + up(b * L * H * N) + up(b * L * H * P) + up(2 * b * L * G1)
                  + up(b * H * M * P * N) + up(b * L * G1 * N) + up(b * L * G1 * P) + up(split1 * (N + P)))
-    assert D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(dims(G=G1))) == want1
+    assert D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(dims(G=G1))) == max(want1, mfma_rms(G1))
     assert bwd_rms(d, ws=None) == -4 and "workspace" in last()
     assert bwd_rms(d, ws_bytes=need - 1) == -4
     assert bwd_rms(d, over={4: None}) == -1 and "dH_score" in last()
