@@ -577,12 +577,13 @@ void sma_bwd_bc_kernel(BwdBCArgs a) {
 
   // B operands: lane holds token `col`, p = 16 ks + 8 half + 0..7.  The E
   // and dR rows of the wave's 32 tokens are staged whole (128-byte rows,
-  // 16-byte pieces XOR-swizzled by the row) in the wave's parts of ring
-  // buffer 2 (E, or dR with one gradient) and 3 (dR with both) while slots 0
-  // and 1 load.  This wave's part of slot 2 and 3 covers exactly the bytes its
-  // staged rows occupied; slot 2 follows once they are in registers (with
-  // both gradients; with one, slot 2 and buffer 3 come in the loop, after its
-  // first barrier).
+  // 16-byte pieces XOR-swizzled by the row) in the wave's part of ring
+  // buffer 2 (E, or dR when only dC is computed) and of buffer 3 (dR when
+  // both are) while slots 0 and 1 load.  A wave's part of a slot covers
+  // exactly the bytes of its staged rows, so a buffer takes its slot once
+  // the wave's own reads of it are done: with both gradients slot 2 is issued
+  // right after them and slot 3 in the loop; with one (3-deep ring) slot 2 is
+  // issued in the loop, after its first barrier.
   bf16x8_t eop[4], rop[4];
   // score-memory mode: 1 / rho_q of this lane's token (the pd row's dl
   // carries rho_q rho_e; the Q-side operand needs rho_e only)
