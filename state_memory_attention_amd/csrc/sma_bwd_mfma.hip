@@ -11,13 +11,14 @@
 //     dQ_t = sum_c dl dH_c E_t / sqrt(N),      dC_t = sum_c p dH_c dR_t
 //     d_dH_c = sum_{t: chunk(t) > c} p C_t^T dR_t + dl Q_t^T E_t / sqrt(N).
 //
-// Three passes, each sized to the register file (two waves per SIMD):
+// Three passes, each sized to the register file (two waves per SIMD, three
+// for pass BC with one product):
 //   A  token tiles x chunks: recompute W and V on the matrix core exactly as
 //      the forward does, then p, dl (stored per (chunk, token)), dE, dgate
 //      and dR (stored in bfloat16 for pass D);
 //   BC token tiles x chunks: dQ^T += dH_c (E * dl/sqrt(N))^T and
-//      dC^T += dH_c (dR * p)^T, the chunk memory as the A operand read with
-//      the transposing LDS read;
+//      dC^T += dH_c (dR * p)^T, the chunk memory as the A operand, read from
+//      a copy transposed to N x P by a small kernel;
 //   D  chunks x later token tiles: the two token contractions of d_dH, the
 //      per-token weights scaling one operand (the chunk-state kernel's form).
 #include "dart_internal.h"
@@ -1257,7 +1258,7 @@ void chunk_states_bwd_mfma_kernel(CsBwdArgs a) {
   auto gt_frag = [&](int prow, int ks) -> bf16x8_t {
     return *(const bf16x8_t*)(s_g + tr_off(prow, 16 * ks + 8 * half));
   };
-  // A operand of dB^T: G rows n (k = p) by transposing reads (see pass BC)
+  // A operand of dB^T: G rows n (k = p) by transposing reads (ld_tr8)
   uint32_t abase[4];
   const uint32_t sgb = lds_addr(s_g);
 #pragma unroll

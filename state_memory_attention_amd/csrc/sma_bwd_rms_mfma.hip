@@ -21,8 +21,8 @@
 //       the float16 matrix core from Q_t 2^k, V on the bfloat16 one) with
 //       pass A's epilogue: p, dl, d ze, dgate, dR; the pd rows hold p and
 //       dls rho_q rho_e, and rho_q, rho_e go to the workspace;
-//   BC  twice: the Q side on the score memory (E scaled by rho_e per token),
-//       the C side on dH;
+//   BC  twice, each memory transposed first: the Q side on the score memory
+//       (E scaled by rho_e per token), the C side on dH;
 //   D   unchanged: its readout term into d_dH, its score term (weights
 //       dls rho_q rho_e on E, Q rows as they are) into dT;
 //   then the chain through r_c and the weight-gradient terms per chunk
