@@ -456,52 +456,72 @@ void sma_bwd_rms_a_kernel(BwdRmsAArgs a) {
   }
 }
 
-// Through S_c = diag(r_c) dH_c, one block per chunk memory, one thread per
-// key row n (N <= blockDim): with dS = w_q[n] w_e[p] dT[p][n] and
-// u_n = sum_p w_e[p] dT[p][n] dH[p][n],
+// Through S_c = diag(r_c) dH_c, one block per chunk memory: with
+// dS = w_q[n] w_e[p] dT[p][n] and u_n = sum_p w_e[p] dT[p][n] dH[p][n],
 //   d_dH[p][n] += r_n dS[p][n] - (r_n^3 / P) dH[p][n] w_q[n] u_n,
 //   wpq[mem][n] = r_n u_n,   wpe[mem][p] = sum_n w_q[n] r_n dH[p][n] dT[p][n].
-__global__ __launch_bounds__(256) void rms_chain_kernel(int N, int P, float eps, const bf16_t* __restrict__ dH,
+// Four waves; wave w owns rows p = 16 w .. 16 w + 15 and lane l the columns
+// n = 2 l, 2 l + 1 (4- and 8-byte loads, a wave covers whole rows), keeping
+// its dH and dT values in registers between the two passes.  The sums over p
+// (r_n, u_n) add the four waves' parts in wave order through LDS; the sum
+// over n (wpe) is one wave sum per row.
+__global__ __launch_bounds__(256) void rms_chain_kernel(float eps, const bf16_t* __restrict__ dH,
                                                         const float* __restrict__ dT, const float* __restrict__ wq,
                                                         const float* __restrict__ we, float* __restrict__ ddh,
                                                         float* __restrict__ wpq, float* __restrict__ wpe) {
-  __shared__ float s_red[4][256];
+  constexpr int kRows = kP / 4;
+  __shared__ float s_ss[4][kN], s_u[4][kN];
   const int64_t mem = blockIdx.x;
-  const int n = threadIdx.x, wave = n >> 6, lane = n & 63;
-  const bool on = n < N;
-  const int64_t base = mem * (int64_t)P * N + (on ? n : 0);
-  const float wqn = on ? (wq ? wq[n] : 1.f) : 0.f;
-  float ss = 0.f, u = 0.f;
-  if (on)
-    for (int p = 0; p < P; ++p) {
-      const float x = bf16_to_f32(dH[base + (int64_t)p * N]);
-      ss = fmaf(x, x, ss);
-      u = fmaf((we ? we[p] : 1.f) * dT[base + (int64_t)p * N], x, u);
-    }
-  const float r = 1.f / sqrtf(ss / (float)P + eps);  // [Eq. 26]
-  const float k3 = r * r * r / (float)P * wqn * u;
-  if (wpq && on) wpq[mem * N + n] = r * u;
-  const float rw = r * wqn;
-  for (int p = 0; p < P; ++p) {
-    const int64_t o = base + (int64_t)p * N;
-    float x = 0.f, tv = 0.f;
-    if (on) {
-      x = bf16_to_f32(dH[o]);
-      tv = dT[o];
-      ddh[o] = fmaf(rw * (we ? we[p] : 1.f), tv, fmaf(-k3, x, ddh[o]));
-    }
-    if (wpe) {
-      const float s = wave_sum(rw * x * tv);
-      if (lane == 0) s_red[wave][p] = s;
-    }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n0 = 2 * lane, p0 = kRows * wave;
+  const int64_t base = mem * (int64_t)(kP * kN) + (int64_t)p0 * kN + n0;
+  uint32_t xv[kRows];
+  float2 tv[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    xv[i] = *(const uint32_t*)(dH + base + i * kN);
+    tv[i] = *(const float2*)(dT + base + i * kN);
   }
-  if (!wpe) return;
+  float ss0 = 0.f, ss1 = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const float x0 = bf16lo(xv[i]), x1 = bf16hi(xv[i]);
+    const float wp = we ? we[p0 + i] : 1.f;
+    ss0 = fmaf(x0, x0, ss0);
+    ss1 = fmaf(x1, x1, ss1);
+    u0 = fmaf(wp * tv[i].x, x0, u0);
+    u1 = fmaf(wp * tv[i].y, x1, u1);
+  }
+  s_ss[wave][n0] = ss0;
+  s_ss[wave][n0 + 1] = ss1;
+  s_u[wave][n0] = u0;
+  s_u[wave][n0 + 1] = u1;
   __syncthreads();
-  const int nw = (int)((blockDim.x + 63) / 64);
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    float acc = 0.f;
-    for (int w = 0; w < nw; ++w) acc += s_red[w][p];
-    wpe[mem * P + p] = acc;
+  ss0 = ss1 = u0 = u1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    ss0 += s_ss[w][n0];
+    ss1 += s_ss[w][n0 + 1];
+    u0 += s_u[w][n0];
+    u1 += s_u[w][n0 + 1];
+  }
+  const float r0 = 1.f / sqrtf(ss0 / (float)kP + eps), r1 = 1.f / sqrtf(ss1 / (float)kP + eps);  // [Eq. 26]
+  const float wq0 = wq ? wq[n0] : 1.f, wq1 = wq ? wq[n0 + 1] : 1.f;
+  const float k30 = r0 * r0 * r0 / (float)kP * wq0 * u0, k31 = r1 * r1 * r1 / (float)kP * wq1 * u1;
+  if (wpq && wave == 0) *(float2*)(wpq + mem * kN + n0) = make_float2(r0 * u0, r1 * u1);
+  const float rw0 = r0 * wq0, rw1 = r1 * wq1;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const float x0 = bf16lo(xv[i]), x1 = bf16hi(xv[i]);
+    const float wp = we ? we[p0 + i] : 1.f;
+    float2* o = (float2*)(ddh + base + i * kN);
+    float2 d = *o;
+    d.x = fmaf(rw0 * wp, tv[i].x, fmaf(-k30, x0, d.x));
+    d.y = fmaf(rw1 * wp, tv[i].y, fmaf(-k31, x1, d.y));
+    *o = d;
+    if (wpe) {
+      const float sv = wave_sum(fmaf(rw0 * x0, tv[i].x, rw1 * x1 * tv[i].y));
+      if (lane == 0) wpe[mem * kP + p0 + i] = sv;
+    }
   }
 }
 
@@ -630,8 +650,7 @@ hipError_t launch_sma_bwd_rms_mfma(const Shape& s, float eps, const void* Q, con
   if ((e = launch_sma_bwd_bc_mfma(s, kBcC, E, dR, memT, pd, nullptr, nullptr, nullptr, hc, heads, st)) != hipSuccess)
     return e;
   if ((e = launch_sma_bwd_d_mfma(s, dR, E, C, Q, pd, ddH, dT, st)) != hipSuccess) return e;
-  rms_chain_kernel<<<dim3((unsigned)n_mem), dim3(kN), 0, st>>>(kN, kP, eps, (const bf16_t*)dH, dT, wq, we, ddH,
-                                                               wpq, wpe);
+  rms_chain_kernel<<<dim3((unsigned)n_mem), dim3(256), 0, st>>>(eps, (const bf16_t*)dH, dT, wq, we, ddH, wpq, wpe);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = s.b * s.L, hpg = s.H / s.G;
   if (grouped) {
