@@ -400,7 +400,7 @@ hipError_t launch_rms_bwd(const Shape& s, float eps, const void* Qv, const void*
 }  // namespace
 
 int64_t col_sum_split(int64_t rows) {
-  const int64_t n = (rows + 511) / 512;
+  const int64_t n = (rows + 63) / 64;  // parts of 64 rows (16 per wave), at most 1024
   return n < 1 ? 1 : (n > 1024 ? 1024 : n);
 }
 

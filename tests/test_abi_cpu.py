@@ -354,7 +354,7 @@ def test_rms_backward_validation():
     b, L, H, G, N, P, S = 2, 512, 4, 2, 128, 64, 256
     M = 2
     up = lambda n: -(-n // 64) * 64
-    split = min(1024, max(1, -(-(b * L * G) // 512)))
+    split = min(1024, max(1, -(-(b * L * G) // 64)))
     want = 4 * (up(2 * b * H * M * L) + up(b * L * H * N) + up(b * L * H * P) + up(b * L * H * N)
                 + up(2 * b * L * G) + up(b * H * M * P * N) + up(b * L * G * N) + up(b * L * G * P)
                 + up(split * (N + P)))
@@ -366,14 +366,14 @@ def test_rms_backward_validation():
     def mfma_rms(G):
         part = r256(4 * b * L * H * (2 * N + P)) if G != H else 0
         plain = r256(4 * 2 * b * H * M * L) + r256(2 * b * L * H * P) + part + r256(2 * b * H * M * P * N)
-        msplit = min(1024, max(1, -(-(b * H * M) // 512)))
+        msplit = min(1024, max(1, -(-(b * H * M) // 64)))
         return (r256(plain) + r256(2 * b * H * M * P * N) + r256(4 * 2 * b * L * G) + r256(4 * b * H * M * P * N)
                 + r256(4 * b * H * M * N) + r256(4 * b * H * M * P) + r256(4 * msplit * (N + P)))
     need = D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(d))
     assert need == max(want, mfma_rms(G))
     # ungrouped heads: no per-head dC partials
     G1 = 4
-    split1 = min(1024, max(1, -(-(b * L * G1) // 512)))
+    split1 = min(1024, max(1, -(-(b * L * G1) // 64)))
     want1 = 4 * (up(2 * b * H * M * L) + up(b * L * H * N) + up(b * L * H * P) + up(2 * b * L * G1)
                  + up(b * H * M * P * N) + up(b * L * G1 * N) + up(b * L * G1 * P) + up(split1 * (N + P)))
     assert D.lib().dart_sma_bwd_rms_workspace_bytes(ctypes.byref(dims(G=G1))) == max(want1, mfma_rms(G1))
