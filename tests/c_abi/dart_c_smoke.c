@@ -14,6 +14,9 @@
  *   - decode of the last token against the chunk memories before it equals
  *     the forward's row of that token (R, lse within 1e-3);
  *   - on the same memories the two families agree on R within 1e-3;
+ *   - backward with gate = 0: dQ, dC, dE, d_dH exactly 0, dgate = dout * R;
+ *     the chunk-state backward of d_dH = 0 exactly 0; with gate = 1 the two
+ *     kernel families agree on dQ and dC at the bf16 bar (2e-2);
  *   - a NULL input is refused with DART_ERR_NULL and a message naming it.
  * Prints "c abi smoke ok" and exits 0 on success. */
 #include <hip/hip_runtime_api.h>
@@ -211,6 +214,76 @@ int main(void) {
   for (int h = 0; h < H; ++h)
     CHECK(fabsf(hld[h] - hl[h * L + t]) <= 1e-3f * fabsf(hl[h * L + t]), "decode lse %g, forward %g", hld[h],
           hl[h * L + t]);
+
+  /* backward [§4 "Efficient Training"; App. C Eq. 33-35]: with gate = 0,
+   * dR = g * dout = 0, so dQ, dC, dE and d_dH are exactly 0 and
+   * dgate = dout * R; the chunk-state backward of d_dH = 0 is exactly 0.
+   * With gate = 1 the two kernel families agree on dQ and dC at the bf16
+   * bar (the matrix-core passes round their scaled operands to bf16). */
+  {
+    const size_t nqf = nq, nef = ne, nhf = nh;
+    uint16_t* hd = bf16_array(nx, 1.0f);
+    void* dout = dev_copy(hd, nx * 2);
+    float *dQ = (float*)dev_alloc(nqf * 4), *dC = (float*)dev_alloc(nqf * 4), *dE = (float*)dev_alloc(nef * 4);
+    float *ddH = (float*)dev_alloc(nhf * 4), *dg = (float*)dev_alloc(nx * 4);
+    const size_t wb = dart_sma_bwd_workspace_bytes(&dims);
+    void* wsb = dev_alloc(wb);
+    CHECK(dart_sma_bwd(&dims, DART_BF16, Q, C, E, dH, g0, 1, R, lse, dout, dQ, dC, dE, ddH, dg, wsb, wb, NULL) ==
+              DART_OK,
+          "bwd: %s", dart_last_error());
+    CHECK_HIP(hipDeviceSynchronize());
+    float* hb = (float*)malloc(nhf * 4);
+    const struct { float* d; size_t n; const char* name; } zeros[] = {
+        {dQ, nqf, "dQ"}, {dC, nqf, "dC"}, {dE, nef, "dE"}, {ddH, nhf, "d_dH"}};
+    for (int z = 0; z < 4; ++z) {
+      to_host(hb, zeros[z].d, zeros[z].n * 4);
+      for (size_t i = 0; i < zeros[z].n; ++i) CHECK(hb[i] == 0.f, "gate 0: %s[%zu] = %g", zeros[z].name, i, hb[i]);
+    }
+    float* hR = (float*)malloc(nx * 4);
+    to_host(hR, R, nx * 4);
+    to_host(hb, dg, nx * 4);
+    float gmax = 0.f, gerr = 0.f;
+    for (size_t i = 0; i < nx; ++i) {
+      const float ref = from_bf16(hd[i]) * hR[i];
+      gmax = fmaxf(gmax, fabsf(ref));
+      gerr = fmaxf(gerr, fabsf(hb[i] - ref));
+    }
+    CHECK(gmax > 0.f && gerr <= 1e-6f * gmax, "dgate differs from dout * R by %g of %g", gerr, gmax);
+
+    const size_t cwb = dart_chunk_states_bwd_workspace_bytes(&dims);
+    void* cws = dev_alloc(cwb ? cwb : 16);
+    float *dX = (float*)dev_alloc(nx * 4), *dB = (float*)dev_alloc(nqf * 4), *dA = (float*)dev_alloc(na * 4);
+    CHECK(dart_chunk_states_bwd(&dims, DART_BF16, X, Bm, A, ddH, dX, dB, dA, cws, cwb, NULL) == DART_OK,
+          "chunk states bwd: %s", dart_last_error());
+    CHECK_HIP(hipDeviceSynchronize());
+    const struct { float* d; size_t n; const char* name; } czeros[] = {{dX, nx, "dX"}, {dB, nqf, "dB"}, {dA, na, "dA"}};
+    for (int z = 0; z < 3; ++z) {
+      to_host(hb, czeros[z].d, czeros[z].n * 4);
+      for (size_t i = 0; i < czeros[z].n; ++i) CHECK(hb[i] == 0.f, "d_dH 0: %s[%zu] = %g", czeros[z].name, i, hb[i]);
+    }
+
+    float* h2 = (float*)malloc(nqf * 4);
+    float* hgen = (float*)malloc(nqf * 4);
+    for (int which = 0; which < 2; ++which) {
+      float* gout = which == 0 ? dQ : dC;
+      for (int path = DART_PATH_AUTO; path <= DART_PATH_GENERAL; ++path) {
+        dart_set_path(path);
+        CHECK(dart_sma_bwd(&dims, DART_BF16, Q, C, E, dH, g1, 1, R, lse, dout, dQ, dC, dE, ddH, NULL, wsb, wb,
+                           NULL) == DART_OK,
+              "bwd: %s", dart_last_error());
+        CHECK_HIP(hipDeviceSynchronize());
+        to_host(path == DART_PATH_AUTO ? h2 : hgen, gout, nqf * 4);
+      }
+      dart_set_path(DART_PATH_AUTO);
+      float dmax = 0.f, vmax = 0.f;
+      for (size_t i = 0; i < nqf; ++i) {
+        dmax = fmaxf(dmax, fabsf(h2[i] - hgen[i]));
+        vmax = fmaxf(vmax, fabsf(hgen[i]));
+      }
+      CHECK(vmax > 0.f && dmax <= 2e-2f * vmax, "%s: matrix-core and general backward differ by %g of %g",
+            which == 0 ? "dQ" : "dC", dmax, vmax);
+    }
+  }
 
   /* argument errors: nothing launches, the message names the argument */
   CHECK(dart_sma_fwd(&dims, DART_BF16, NULL, C, E, dH, Y, g1, 1, out, NULL, NULL, NULL) == DART_ERR_NULL,

@@ -6,8 +6,11 @@ The program checks properties fixed by the definitions on both kernel
 families [DART §3 Eq. 5, 8-11; §4 "Inference Cache"]: gate 0 leaves Y_ssm
 unchanged bit for bit, gate 1 gives bf16(Y_ssm + R) bit for bit, tokens of
 chunk 0 see no chunk (R = 0, lse = -inf), repeated launches agree bit for
-bit, decode of the last token reproduces the forward's row, and a NULL input
-is refused with DART_ERR_NULL."""
+bit, decode of the last token reproduces the forward's row, the backward
+with gate 0 gives exactly zero gradients and dgate = dout * R [App. C
+Eq. 33-35], the chunk-state backward of a zero d_dH is exactly zero, the two
+kernel families' backward agree at the bf16 bar, and a NULL input is refused
+with DART_ERR_NULL."""
 import os
 import subprocess
 
