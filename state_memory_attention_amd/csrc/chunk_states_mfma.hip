@@ -214,10 +214,13 @@ __global__ __launch_bounds__(kThreads) void chunk_states_mfma_kernel(CsArgs a) {
   f32x16_t acc0 = {}, acc1 = {};
   for (int q = 0; q < nblk; ++q) {
     const int ib = nblk - 1 - q;
-    // Sub-block q has landed once at most the loads of q+1, q+2 remain; the
-    // barrier makes every wave's part visible and frees stage (q-1) % 3.
-    const int after = nblk - 1 - q;
-    barrier_loads(after >= 2 ? 12 : after == 1 ? 6 : 0);
+    // Sub-block q has landed once at most the loads issued after it remain:
+    // before the first, the prologue's sub-blocks 1 and 2 (real or
+    // zero-length); later only q + 1, which the prologue issued (q + 1 <= 2)
+    // or iteration q - 1 did if it exists -- q + 2 is issued below, after
+    // the wait.  The barrier makes every wave's part visible and frees stage
+    // (q - 1) % 3.
+    barrier_loads(q == 0 ? 12 : (q + 1 <= 2 || q + 1 < nblk) ? 6 : 0);
     if (q >= 1 && q + 2 < nblk) issue(q + 2);
     // Chunks longer than one group: the next group's weights (its decays
     // are loaded here, so this wait does drain the loads in flight).

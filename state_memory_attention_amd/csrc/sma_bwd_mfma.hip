@@ -983,12 +983,15 @@ void sma_bwd_d_kernel(BwdDArgs a) {
   }
 
   for (int q = 0; q < n_steps; ++q) {
-    const int after = n_steps - 1 - q;
+    // Step q has landed once at most the loads issued after it remain:
+    // before the first, the prologue's steps 1 and 2 (real or zero-length);
+    // later only q + 1, which the prologue issued (q + 1 <= 2) or iteration
+    // q - 1 did if it exists -- q + 2 is issued below, after the wait.
     asm volatile("" ::: "memory");
-    if (after >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0f7e);      // vmcnt(14): steps q+1, q+2 in flight
-    else if (after == 1)
-      __builtin_amdgcn_s_waitcnt(0x0f77);      // vmcnt(7)
+    if (q == 0)
+      __builtin_amdgcn_s_waitcnt(0x0f7e);      // vmcnt(14): steps 1 and 2 in flight
+    else if (q + 1 <= 2 || q + 1 < n_steps)
+      __builtin_amdgcn_s_waitcnt(0x0f77);      // vmcnt(7): step q + 1 in flight
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_s_barrier();

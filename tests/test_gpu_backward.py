@@ -17,7 +17,7 @@ import oracle as O
 import state_memory_attention_amd as dart
 from state_memory_attention_amd import synth
 
-from gpu_helpers import TOL, TOL_SAME_INPUT, dev, err, host, say, to_oracle_mem
+from gpu_helpers import TOL, TOL_SAME_INPUT, dev, err, host, same, say, to_oracle_mem
 
 pytestmark = pytest.mark.gpu
 
@@ -156,6 +156,26 @@ def test_mfma_bwd_deterministic_many_chunk_groups():
     for r in runs[1:]:
         for k in runs[0]:
             assert np.array_equal(runs[0][k], r[k]), k
+
+
+def test_mfma_bwd_repeat_bitwise_full_size():
+    """Three backward calls at b2 H24 L16384 agree bit for bit: the d_dH
+    pass streams up to 256 token sub-blocks per block through its LDS ring,
+    each waited for before it is read."""
+    cfg = dict(synth.CONFIGS[2])
+    S = cfg["chunk"]
+    d = synth.draw_fwd_torch(**cfg, seed=12)
+    dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)
+    _, R, lse = dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], S, want_R=True, want_lse=True)
+    dout = synth.draw_grad_torch(tuple(d["Y"].shape), "bf16", 13)
+    first = dart.dart_sma_bwd(d["Q"], d["C"], d["E"], dH, d["gate"], R, lse, dout, S)
+    for _ in range(2):
+        again = dart.dart_sma_bwd(d["Q"], d["C"], d["E"], dH, d["gate"], R, lse, dout, S)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dQ", "dC", "dE", "d_dH", "dgate"), first, again):
+            same(x, y, f"{name} of repeated backward calls")
+        del again
+    say("backward repeat at full size: bitwise")
 
 
 # bf16, N = 128, P = 64: the matrix-core backward.  Shapes chosen to exercise

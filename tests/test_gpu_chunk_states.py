@@ -7,7 +7,7 @@ import oracle as O
 import state_memory_attention_amd as dart
 from state_memory_attention_amd import synth
 
-from gpu_helpers import TOL, dev, err, host, say, to_oracle_mem
+from gpu_helpers import TOL, dev, err, host, same, say, to_oracle_mem
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,23 @@ def test_mfma_matches_general_kernel():
     gen = run_cs(d, cfg, dart.DART_PATH_GENERAL)
     # both round the same float32 sums (in different orders) once to bf16
     assert err(fast, gen) <= 1e-2
+
+
+def test_repeat_launches_bitwise_full_size():
+    """Three launches at b1 H32 L65536 agree bit for bit, with S = 256 (4
+    sub-blocks of 64 tokens per chunk) and S = 1024 (16): each sub-block of
+    the LDS ring is waited for before it is read, whatever the timing of the
+    loads still in flight."""
+    for S in (256, 1024):
+        cfg = dict(synth.CONFIGS[3], chunk=S)
+        d = synth.draw_fwd_torch(**cfg, seed=11)
+        runs = [dart.dart_chunk_states(d["X"], d["B"], d["A"], S) for _ in range(3)]
+        torch.cuda.synchronize()
+        say("chunk states repeat, S =", S)
+        for r in runs[1:]:
+            same(runs[0], r, f"dH of repeated launches, S = {S} (b, h, c)")
+        del runs, d
+        torch.cuda.empty_cache()
 
 
 def test_deterministic():
