@@ -427,3 +427,20 @@ def test_ssd_validation():
     assert ssd(d, over={5: ctypes.c_void_p(ADDR[0].value)}) == -2 and "overlaps" in last()
     assert ssd(dims(L=0)) == 0
     assert ssd(d, dtype=7) == -3
+
+def test_c_program_links_the_in_tree_library():
+    """The build step's plain C consumer of include/dart.h
+    (tests/c_abi/dart_c_smoke.c) resolves libdart.so to the package's copy
+    and needs no Python or torch library; it runs on the GPU in
+    tests/test_gpu_c_abi.py."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    binp = os.path.join(root, "tests", "c_abi", "dart_c_smoke.bin")
+    if not os.path.exists(binp):
+        pytest.skip("the C program is built by state_memory_attention_amd.build (not run here)")
+    out = subprocess.run(["ldd", binp], capture_output=True, text=True, timeout=60).stdout
+    libs = {line.split()[0]: line for line in out.splitlines() if "=>" in line}
+    assert "libdart.so" in libs, out
+    assert os.path.realpath(libs["libdart.so"].split("=>")[1].split()[0]) == \
+        os.path.realpath(os.path.join(root, "state_memory_attention_amd", "libdart.so"))
+    assert "not found" not in out, out
+    assert not any("python" in k or "torch" in k for k in libs), out
