@@ -67,3 +67,45 @@ def test_two_streams_two_threads_match_serial_runs():
             for name, x, y in zip(NAMES, alone[i], res):
                 same(x, y, f"input {i}, concurrent run {rep}: {name}")
     say("two streams, two threads, 3 runs each: bitwise equal to the serial runs")
+
+
+def test_ring_kernels_under_memory_contention():
+    """The kernels that stream through an LDS ring give the same bits while
+    another stream saturates HBM with 1 GiB copies (longer and more varied
+    load latencies): chunk states at b1 H32 L65536 with S = 1024 (16 ring
+    stages per chunk) and the backward (its d_dH pass) at b2 H24 L16384,
+    each against a run on a quiet GPU.  A guard on run-to-run equality under
+    load, not a detector of every wait error: a stage issued two iterations
+    before it is read has almost always landed."""
+    cfg3 = dict(synth.CONFIGS[3], chunk=1024)
+    d3 = synth.draw_fwd_torch(**cfg3, seed=41)
+    cfg2 = dict(synth.CONFIGS[2])
+    S2 = cfg2["chunk"]
+    d2 = synth.draw_fwd_torch(**cfg2, seed=42)
+    dH2 = dart.dart_chunk_states(d2["X"], d2["B"], d2["A"], S2)
+    _, R2, lse2 = dart.dart_sma_fwd(d2["Q"], d2["C"], d2["E"], dH2, d2["Y"], d2["gate"], S2, want_R=True,
+                                    want_lse=True)
+    dout2 = synth.draw_grad_torch(tuple(d2["Y"].shape), "bf16", 43)
+
+    def work():
+        cs = dart.dart_chunk_states(d3["X"], d3["B"], d3["A"], 1024)
+        bw = dart.dart_sma_bwd(d2["Q"], d2["C"], d2["E"], dH2, d2["gate"], R2, lse2, dout2, S2)
+        return (cs,) + tuple(bw)
+
+    quiet = work()
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    noise, main = torch.cuda.Stream(), torch.cuda.Stream()
+    noise.wait_stream(torch.cuda.current_stream())
+    main.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(noise):
+        for _ in range(12):
+            dst.copy_(src)
+    with torch.cuda.stream(main):
+        loud = [work() for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep, res in enumerate(loud):
+        for name, x, y in zip(("dH (S = 1024)", "dQ", "dC", "dE", "d_dH", "dgate"), quiet, res):
+            same(x, y, f"under contention, run {rep}: {name}")
+    say("ring kernels under memory contention: bitwise equal to the quiet runs")
