@@ -22,9 +22,9 @@ Conventions (the paper's notation, 0-based indices):
 Readings where the paper leaves a step open (each is also listed in the
 design notes):
   * a token sees chunk c iff c < chunk(t) -- strictly earlier chunks only
-    [§3 Eq. 10, Algorithm 1 "for historical chunk j < i"];
+    [§3 Eq. 10; §4 Algorithm 1, loop over history chunks j < i];
   * a token with no visible chunk gets R_t = 0 and lse_t = -inf
-    [§3 text after Eq. 10; Algorithm 1 steps 15-16];
+    [§3 text after Eq. 10; §4 Algorithm 1, finalisation];
   * the gate is given after its activation, either one scalar per token
     (the paper's G_t) or one value per channel, and out = Y_ssm + g * R
     [§3 Eq. 11];
@@ -93,7 +93,7 @@ def _f64(x):
 
 
 def num_chunks(L: int, S: int) -> int:
-    """M = ceil(L / S)  [§4 "Training Complexity"; Algorithm 1 step 1]."""
+    """M = ceil(L / S)  [§4 "Training Complexity"; §4 Algorithm 1, chunking]."""
     return -(-L // S)
 
 

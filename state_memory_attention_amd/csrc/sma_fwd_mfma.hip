@@ -20,7 +20,7 @@
 //     l_t = sum_p W[t,p] E[t,p] / sqrt(N)      (= Q_t dH_j E_t / sqrt(N), Eq. 9)
 // is 32 in-lane FMAs plus one swap between the two half-waves, and the online
 // softmax (App. C Eq. 29-31) is purely per lane.  The paper forms the key
-// K = dH_j E_t first and then Q_t K (Algorithm 1 steps 8-9); taking Q_t dH_j
+// K = dH_j E_t first and then Q_t K (§4 Algorithm 1, key readout); taking Q_t dH_j
 // first is the same bilinear form by associativity, shares the dH_j operand
 // with the value product and costs P instead of N FMAs per (token, chunk).
 //

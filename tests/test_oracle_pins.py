@@ -153,7 +153,7 @@ def test_sma_first_chunk_empty_and_one_visible_chunk():
     L, S, N, P = 40, 8, 6, 4
     Q, C, E, dH = _random_head(rng, L, S, N, P)
     R, lse = O.sma_head(Q, C, E, dH, S)
-    # chunk 0: empty history => R = 0, lse = -inf  [§3 after Eq. 10; Alg. 1 steps 15-16]
+    # chunk 0: empty history => R = 0, lse = -inf  [§3 after Eq. 10; §4 Algorithm 1, finalisation]
     assert (R[:S] == 0).all() and np.isneginf(lse[:S]).all()
     # chunk 1: a single visible chunk => softmax weight 1 => R_t = C_t dH_0, lse = l_{t,0}
     for t in range(S, 2 * S):
