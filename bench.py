@@ -1,6 +1,6 @@
 """Benchmark of the DART hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = dart_chunk_states + dart_sma_fwd over one batch of synthetic input
 (the long-context bf16 forward: b=2, H=24, L=16384, S=256, N=128, P=64 by
@@ -150,11 +150,11 @@ def time_configs(torch, dart, synth, steps, warmup, skip):
     and the very long context (b1 H32 L65536), each with the step's
     tokens/s and the forward's and the path's bf16 MFMA fractions."""
     res = {}
-    for ci in (1, 2, 3):
-        if ci == skip:
+    for name in (synth.BLOCK, synth.LONG, synth.VLONG):
+        if name == skip:
             continue
-        cfg = dict(synth.CONFIGS[ci])
-        t_cs, t_fwd = time_step(torch, dart, synth, cfg, steps, warmup, sets=2 if ci == 1 else 1)
+        cfg = synth.workload(name)
+        t_cs, t_fwd = time_step(torch, dart, synth, cfg, steps, warmup, sets=2 if name == synth.BLOCK else 1)
         rec = step_record(cfg, t_cs, t_fwd)
         rec["traffic_sma_fwd"] = traffic_record("sma_fwd", cfg["name"])
         res[cfg["name"]] = rec
@@ -169,7 +169,7 @@ def time_chunk_sizes(torch, dart, synth, steps, warmup):
     see, which ``masked_frac`` counts."""
     res = {}
     for S in (64, 32):
-        cfg = dict(synth.CONFIGS[2], chunk=S, name=f"long_bf16_b2_h24_L16384_S{S}")
+        cfg = synth.workload(synth.LONG, chunk=S, name=f"long_bf16_b2_h24_L16384_S{S}")
         b, H, L = cfg["batch"], cfg["nheads"], cfg["seqlen"]
         t_cs, t_fwd = time_step(torch, dart, synth, cfg, steps, warmup)
         rec = step_record(cfg, t_cs, t_fwd)
@@ -444,7 +444,7 @@ def cpu_baseline(cfg, budget_s=12.0):
 
 
 def time_decode(torch, dart, synth, steps=20, warmup=3):
-    cfg = dict(synth.CONFIGS[4])
+    cfg = synth.workload(synth.DECODE)
     d = synth.draw_decode_torch(**cfg, seed=0)
     ws = torch.empty(dart.decode_workspace_bytes(cfg["batch"], cfg["nheads"], cfg["d_head"],
                                                  cfg["max_chunks"]), dtype=torch.uint8, device="cuda")
@@ -598,8 +598,8 @@ def profile_kernels(launches=3):
         assert probe.dart_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, stream) == 0
     torch.cuda.synchronize()
     del src, dst
-    for ci in (2, 3):
-        cfg = dict(synth.CONFIGS[ci])
+    for name in (synth.LONG, synth.VLONG):
+        cfg = synth.workload(name)
         d = synth.draw_fwd_torch(**cfg, seed=0)
         dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], cfg["chunk"])
         for _ in range(launches):
@@ -631,7 +631,7 @@ def profile_kernels(launches=3):
             del ga, gb, gc
         del d, dH, out
         torch.cuda.empty_cache()
-    cfg = dict(synth.CONFIGS[4])
+    cfg = synth.workload(synth.DECODE)
     d = synth.draw_decode_torch(**cfg, seed=0)
     for _ in range(launches):
         dart.dart_sma_decode(d["q"], d["c"], d["e"], d["cache"], d["y"], d["gate"])
@@ -643,7 +643,7 @@ def profile_kernels(launches=3):
     del d, upd
     torch.cuda.empty_cache()
     # backward of the long-context workload: the forward's R and lse first
-    cfg = dict(synth.CONFIGS[2])
+    cfg = synth.workload(synth.LONG)
     S = cfg["chunk"]
     d = synth.draw_fwd_torch(**cfg, seed=0)
     dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)
@@ -724,27 +724,27 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
         return (sum(sel_f) / len(sel_f) * 1024 * f_scale, sum(sel_w) / len(sel_w) * 1024 * w_scale)
 
     out = []
-    w2, w3, w4 = (synth.CONFIGS[i]["name"] for i in (2, 3, 4))
+    w_long, w_vlong, w_dec = synth.LONG, synth.VLONG, synth.DECODE
     # (file label, source set, kernel symbol, workload, index of the first
     # counted dispatch of that symbol in the --profile-kernels program)
-    plan = [("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w2, 1),
-            ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w2, 0),
-            ("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w3, 1 + launches + 1),
-            ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w3, launches),
-            ("decode", "decode", "sma_decode_partial_kernel", w4, 0),
-            ("state_update", "state_update", "decode_update_kernel", w4, 0),
-            ("sma_bwd_a", "sma_bwd", "sma_bwd_a_kernel", w2, 0),
-            ("sma_bwd_bc", "sma_bwd", "sma_bwd_bc_kernel", w2, 0),
-            ("sma_bwd_d", "sma_bwd", "sma_bwd_d_kernel", w2, 0),
-            ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w2, 0),
-            ("chunk_states_rms", "chunk_states_rms", "chunk_states_mfma_kernel<true>", w2, 0),
-            ("sma_fwd_rms", "sma_fwd_rms", "sma_fwd_rms_mfma_kernel", w2, 0),
-            ("sma_bwd_rms_a", "sma_bwd_rms", "sma_bwd_rms_a_kernel", w2, 0),
-            ("sma_bwd_rms_bc_q", "sma_bwd_rms", "sma_bwd_bc_kernel<1>", w2, 0),
-            ("sma_bwd_rms_bc_c", "sma_bwd_rms", "sma_bwd_bc_kernel<2>", w2, 0),
-            ("sma_bwd_rms_d", "sma_bwd_rms", "sma_bwd_d_kernel", w2, launches),
-            ("ssd_out", "ssd", "ssd_out_mfma_kernel", w2, 0),
-            ("ssd_state_pass", "ssd", "state_pass_kernel", w2, 0)]
+    plan = [("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w_long, 1),
+            ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w_long, 0),
+            ("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w_vlong, 1 + launches + 1),
+            ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w_vlong, launches),
+            ("decode", "decode", "sma_decode_partial_kernel", w_dec, 0),
+            ("state_update", "state_update", "decode_update_kernel", w_dec, 0),
+            ("sma_bwd_a", "sma_bwd", "sma_bwd_a_kernel", w_long, 0),
+            ("sma_bwd_bc", "sma_bwd", "sma_bwd_bc_kernel", w_long, 0),
+            ("sma_bwd_d", "sma_bwd", "sma_bwd_d_kernel", w_long, 0),
+            ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w_long, 0),
+            ("chunk_states_rms", "chunk_states_rms", "chunk_states_mfma_kernel<true>", w_long, 0),
+            ("sma_fwd_rms", "sma_fwd_rms", "sma_fwd_rms_mfma_kernel", w_long, 0),
+            ("sma_bwd_rms_a", "sma_bwd_rms", "sma_bwd_rms_a_kernel", w_long, 0),
+            ("sma_bwd_rms_bc_q", "sma_bwd_rms", "sma_bwd_bc_kernel<1>", w_long, 0),
+            ("sma_bwd_rms_bc_c", "sma_bwd_rms", "sma_bwd_bc_kernel<2>", w_long, 0),
+            ("sma_bwd_rms_d", "sma_bwd_rms", "sma_bwd_d_kernel", w_long, launches),
+            ("ssd_out", "ssd", "ssd_out_mfma_kernel", w_long, 0),
+            ("ssd_state_pass", "ssd", "state_pass_kernel", w_long, 0)]
     for label, kernel, sym, workload, first in plan:
         rd, wr = per_kernel(sym, first, launches)
         rec = {"kernel": sym, "workload": workload, "source_sha256_16": source_hash(KERNEL_SOURCES[kernel]),
@@ -764,7 +764,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3])
+    ap.add_argument("--workload", default="long_bf16_b2_h24_L16384",
+                    choices=["long_bf16_b2_h24_L16384", "vlong_bf16_b1_h32_L65536"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
@@ -784,7 +785,7 @@ def main():
         profile_kernels()
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build runs the "
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the library runs the "
               "hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
@@ -793,7 +794,7 @@ def main():
     import state_memory_attention_amd as dart
     from state_memory_attention_amd import synth
 
-    cfg = dict(synth.CONFIGS[args.config])
+    cfg = synth.workload(args.workload)
     b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
     d = synth.draw_fwd_torch(**cfg, seed=0)
     M = dart.num_chunks(L, S)
@@ -852,7 +853,7 @@ def main():
     torch.cuda.empty_cache()
     result["gemm_probe"] = time_gemm_probe(torch, args.steps, args.warmup, achieved)
     if not args.no_configs:
-        result["configs"] = time_configs(torch, dart, synth, args.steps, args.warmup, args.config)
+        result["configs"] = time_configs(torch, dart, synth, args.steps, args.warmup, args.workload)
         result["chunk_sizes"] = time_chunk_sizes(torch, dart, synth, args.steps, args.warmup)
     if not args.no_rms:
         result["rms"] = time_rms(torch, dart, synth, cfg)

@@ -34,8 +34,9 @@ import math
 import numpy as np
 
 # The five workloads: one tiny fp32 case, three bf16 forward cases and one
-# bf16 decode case.  a_lo/a_hi bound the per-head decay rate.
-CONFIGS = [
+# bf16 decode case, each named by its shape.  a_lo/a_hi bound the per-head
+# decay rate.
+WORKLOADS = [
     dict(name="tiny_fp32_L1024_S64_N16_P16", kind="fwd", batch=1, nheads=1, ngroups=1,
          seqlen=1024, chunk=64, d_state=16, d_head=16, dtype="f32", a_lo=1.0, a_hi=4.0),
     dict(name="block_bf16_b4_h24_L2048", kind="fwd", batch=4, nheads=24, ngroups=24,
@@ -47,6 +48,15 @@ CONFIGS = [
     dict(name="decode_bf16_b64_h24_M256", kind="decode", batch=64, nheads=24, ngroups=24,
          max_chunks=256, chunk=256, d_state=128, d_head=64, dtype="bf16"),
 ]
+TINY, BLOCK, LONG, VLONG, DECODE = (w["name"] for w in WORKLOADS)
+
+
+def workload(name: str, **changes) -> dict:
+    """A copy of the named workload's settings, with `changes` applied."""
+    for w in WORKLOADS:
+        if w["name"] == name:
+            return dict(w, **changes)
+    raise KeyError(f"no workload named {name!r}")
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -162,7 +162,7 @@ def test_mfma_bwd_repeat_bitwise_full_size():
     """Three backward calls at b2 H24 L16384 agree bit for bit: the d_dH
     pass streams up to 256 token sub-blocks per block through its LDS ring,
     each waited for before it is read."""
-    cfg = dict(synth.CONFIGS[2])
+    cfg = synth.workload(synth.LONG)
     S = cfg["chunk"]
     d = synth.draw_fwd_torch(**cfg, seed=12)
     dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)

@@ -40,11 +40,11 @@ def check_full(cfg, seed=0, path=dart.DART_PATH_AUTO, tol=None):
 
 
 def test_tiny_fp32_config():
-    check_full(dict(synth.CONFIGS[0]))
+    check_full(synth.workload(synth.TINY))
 
 
 def test_block_bf16_config():
-    check_full(dict(synth.CONFIGS[1]))
+    check_full(synth.workload(synth.BLOCK))
 
 
 @pytest.mark.parametrize("L,S,G,dtype,N,P", [
@@ -80,7 +80,7 @@ def test_decay_special_cases():
 
 
 def test_mfma_matches_general_kernel():
-    cfg = dict(synth.CONFIGS[1], batch=1, nheads=4, ngroups=2, seqlen=1100)
+    cfg = synth.workload(synth.BLOCK, batch=1, nheads=4, ngroups=2, seqlen=1100)
     d = synth.draw_fwd(**cfg, seed=5)
     fast = run_cs(d, cfg, dart.DART_PATH_AUTO)
     gen = run_cs(d, cfg, dart.DART_PATH_GENERAL)
@@ -94,7 +94,7 @@ def test_repeat_launches_bitwise_full_size():
     the LDS ring is waited for before it is read, whatever the timing of the
     loads still in flight."""
     for S in (256, 1024):
-        cfg = dict(synth.CONFIGS[3], chunk=S)
+        cfg = synth.workload(synth.VLONG, chunk=S)
         d = synth.draw_fwd_torch(**cfg, seed=11)
         runs = [dart.dart_chunk_states(d["X"], d["B"], d["A"], S) for _ in range(3)]
         torch.cuda.synchronize()
@@ -106,7 +106,7 @@ def test_repeat_launches_bitwise_full_size():
 
 
 def test_deterministic():
-    cfg = dict(synth.CONFIGS[1], batch=1, nheads=4, ngroups=4)
+    cfg = synth.workload(synth.BLOCK, batch=1, nheads=4, ngroups=4)
     d = synth.draw_fwd(**cfg, seed=9)
     a, b = run_cs(d, cfg), run_cs(d, cfg)
     assert np.array_equal(a, b)

@@ -98,7 +98,7 @@ def test_update_decode_workload_shape():
     middle of chunk 100 against a random float32 in-progress state, then a
     token that closes the chunk (its memory goes to cache row 100 and the
     state restarts from zero).  Every entry against the oracle's update."""
-    cfg = dict(synth.CONFIGS[4])
+    cfg = synth.workload(synth.DECODE)
     b, H, G, N, P, S = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["d_state"], cfg["d_head"], cfg["chunk"]
     say("decode update, decode workload shape", cfg["name"])
     gen = torch.Generator(device="cuda")

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 
 def test_decode_every_row():
-    cfg = dict(synth.CONFIGS[4])
+    cfg = synth.workload(synth.DECODE)
     say("full size", cfg["name"])
     b, H, G, M = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["max_chunks"]
     d = synth.draw_decode_torch(**cfg, seed=0)
@@ -49,7 +49,7 @@ def test_decode_rms_every_row():
     r of every cached memory from dart_chunk_rms, RMSNorm weights drawn in
     [0.5, 2], eps = 1e-6; out, R and lse of every (row, head) against the
     oracle's normalised decode on the cache as stored."""
-    cfg = dict(synth.CONFIGS[4])
+    cfg = synth.workload(synth.DECODE)
     say("full size, normalised branch", cfg["name"])
     b, H, G, M = cfg["batch"], cfg["nheads"], cfg["ngroups"], cfg["max_chunks"]
     N, P = cfg["d_state"], cfg["d_head"]

@@ -35,7 +35,7 @@ EPS = 1e-6
 @pytest.fixture(scope="module")
 def run():
     """Every GPU call of this module on one draw; results moved to the host."""
-    cfg = dict(synth.CONFIGS[2])
+    cfg = synth.workload(synth.LONG)
     say("full size", cfg["name"], "on the GPU")
     b, H, L, S, P = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"], cfg["d_head"]
     d = synth.draw_fwd_torch(**cfg, seed=0)

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def run():
-    cfg = dict(synth.CONFIGS[3])
+    cfg = synth.workload(synth.VLONG)
     say("full size", cfg["name"], "on the GPU")
     S = cfg["chunk"]
     d = synth.draw_fwd_torch(**cfg, seed=0)

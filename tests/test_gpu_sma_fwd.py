@@ -211,8 +211,8 @@ def end_to_end(cfg, seed=0):
 
 
 def test_end_to_end_tiny_fp32():
-    end_to_end(dict(synth.CONFIGS[0]))
+    end_to_end(synth.workload(synth.TINY))
 
 
 def test_end_to_end_block_bf16():
-    end_to_end(dict(synth.CONFIGS[1]))
+    end_to_end(synth.workload(synth.BLOCK))

@@ -77,19 +77,19 @@ def test_ring_kernels_under_memory_contention():
     each against a run on a quiet GPU.  A guard on run-to-run equality under
     load, not a detector of every wait error: a stage issued two iterations
     before it is read has almost always landed."""
-    cfg3 = dict(synth.CONFIGS[3], chunk=1024)
-    d3 = synth.draw_fwd_torch(**cfg3, seed=41)
-    cfg2 = dict(synth.CONFIGS[2])
-    S2 = cfg2["chunk"]
-    d2 = synth.draw_fwd_torch(**cfg2, seed=42)
-    dH2 = dart.dart_chunk_states(d2["X"], d2["B"], d2["A"], S2)
-    _, R2, lse2 = dart.dart_sma_fwd(d2["Q"], d2["C"], d2["E"], dH2, d2["Y"], d2["gate"], S2, want_R=True,
-                                    want_lse=True)
-    dout2 = synth.draw_grad_torch(tuple(d2["Y"].shape), "bf16", 43)
+    cfg_v = synth.workload(synth.VLONG, chunk=1024)
+    dv = synth.draw_fwd_torch(**cfg_v, seed=41)
+    cfg_l = synth.workload(synth.LONG)
+    S_l = cfg_l["chunk"]
+    dl = synth.draw_fwd_torch(**cfg_l, seed=42)
+    dH_l = dart.dart_chunk_states(dl["X"], dl["B"], dl["A"], S_l)
+    _, R_l, lse_l = dart.dart_sma_fwd(dl["Q"], dl["C"], dl["E"], dH_l, dl["Y"], dl["gate"], S_l, want_R=True,
+                                  want_lse=True)
+    dout_l = synth.draw_grad_torch(tuple(dl["Y"].shape), "bf16", 43)
 
     def work():
-        cs = dart.dart_chunk_states(d3["X"], d3["B"], d3["A"], 1024)
-        bw = dart.dart_sma_bwd(d2["Q"], d2["C"], d2["E"], dH2, d2["gate"], R2, lse2, dout2, S2)
+        cs = dart.dart_chunk_states(dv["X"], dv["B"], dv["A"], 1024)
+        bw = dart.dart_sma_bwd(dl["Q"], dl["C"], dl["E"], dH_l, dl["gate"], R_l, lse_l, dout_l, S_l)
         return (cs,) + tuple(bw)
 
     quiet = work()

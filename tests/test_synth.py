@@ -14,7 +14,7 @@ def test_round_bf16_matches_torch():
 
 
 def test_draw_fwd_deterministic_and_shaped():
-    cfg = dict(synth.CONFIGS[0])
+    cfg = synth.workload(synth.TINY)
     a = synth.draw_fwd(**cfg, seed=0)
     b = synth.draw_fwd(**cfg, seed=0)
     c = synth.draw_fwd(**cfg, seed=1)
@@ -31,7 +31,7 @@ def test_draw_fwd_deterministic_and_shaped():
 
 
 def test_draw_fwd_bf16_values_are_bf16():
-    cfg = dict(synth.CONFIGS[1], seqlen=512, batch=1, nheads=2, ngroups=1)
+    cfg = synth.workload(synth.BLOCK, seqlen=512, batch=1, nheads=2, ngroups=1)
     d = synth.draw_fwd(**cfg, seed=0, gate_per_channel=False)
     for k in ("X", "B", "C", "Q", "E", "Y", "gate"):
         np.testing.assert_array_equal(synth.round_bf16(d[k]), d[k])
@@ -39,7 +39,7 @@ def test_draw_fwd_bf16_values_are_bf16():
 
 
 def test_draw_decode_shapes():
-    cfg = dict(synth.CONFIGS[4], batch=2, max_chunks=3)
+    cfg = synth.workload(synth.DECODE, batch=2, max_chunks=3)
     d = synth.draw_decode(**cfg, seed=0)
     assert d["cache"].shape == (2, 24, 3, 64, 128)
     assert d["q"].shape == (2, 24, 128) and d["e"].shape == (2, 24, 64)
