@@ -51,12 +51,13 @@ WORKLOADS = [
 TINY, BLOCK, LONG, VLONG, DECODE = (w["name"] for w in WORKLOADS)
 
 
-def workload(name: str, **changes) -> dict:
-    """A copy of the named workload's settings, with `changes` applied."""
+def workload(key: str, /, **changes) -> dict:
+    """A copy of the settings of the workload named `key`, with `changes`
+    applied (a new `name` among them, for a variant)."""
     for w in WORKLOADS:
-        if w["name"] == name:
+        if w["name"] == key:
             return dict(w, **changes)
-    raise KeyError(f"no workload named {name!r}")
+    raise KeyError(f"no workload named {key!r}")
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -1,5 +1,6 @@
 """Seeded input generator: determinism, shapes, rounding and distributions."""
 import numpy as np
+import pytest
 import torch
 
 from state_memory_attention_amd import synth
@@ -43,3 +44,17 @@ def test_draw_decode_shapes():
     d = synth.draw_decode(**cfg, seed=0)
     assert d["cache"].shape == (2, 24, 3, 64, 128)
     assert d["q"].shape == (2, 24, 128) and d["e"].shape == (2, 24, 64)
+
+
+def test_workloads_by_name():
+    names = [w["name"] for w in synth.WORKLOADS]
+    assert names == [synth.TINY, synth.BLOCK, synth.LONG, synth.VLONG, synth.DECODE]
+    assert len(set(names)) == len(names)
+    w = synth.workload(synth.LONG)
+    assert (w["batch"], w["nheads"], w["seqlen"], w["chunk"]) == (2, 24, 16384, 256)
+    w["chunk"] = 1  # a copy: the table is unchanged
+    assert synth.workload(synth.LONG)["chunk"] == 256
+    v = synth.workload(synth.LONG, chunk=32, name="long_S32")
+    assert (v["name"], v["chunk"], v["seqlen"]) == ("long_S32", 32, 16384)
+    with pytest.raises(KeyError):
+        synth.workload("no_such_workload")
