@@ -609,7 +609,7 @@ def profile_kernels(launches=3):
         for _ in range(launches):
             dart.dart_sma_fwd(d["Q"], d["C"], d["E"], dH, d["Y"], d["gate"], cfg["chunk"], out=out)
         torch.cuda.synchronize()
-        if ci == 2:
+        if name == synth.LONG:
             # the matrix-core yardstick on the same operand values (time_mfma_probe)
             probe.dart_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                               ctypes.c_void_p]
