@@ -92,6 +92,24 @@ def path_bytes(cfg):
     return (tok_h + tok_g + b * L * H * 4 + mem) + (2 * tok_g + b * L * G * P * 2 + mem + 3 * tok_h)
 
 
+def bwd_flops(cfg):
+    """Algorithmic flops of the SMA backward: 12NP per (token, visible chunk)
+    pair (the recomputed W and V products 4NP, dQ and dC 4NP, the two d_dH
+    contractions 4NP)."""
+    b, H, L, S, N, P = (cfg[k] for k in ("batch", "nheads", "seqlen", "chunk", "d_state", "d_head"))
+    return 12 * N * P * fwd_pairs(b, H, L, S)
+
+
+def ssd_bytes(cfg):
+    """Compulsory HBM bytes of the SSM branch (bf16): X, B, C, A read, Y and
+    the chunk memories written, the state entering every chunk written and
+    read back."""
+    b, H, G, L, S, N, P = (cfg[k] for k in ("batch", "nheads", "ngroups", "seqlen", "chunk", "d_state", "d_head"))
+    M = -(-L // S)
+    tok_h, tok_g, mem = b * L * H * P * 2, b * L * G * N * 2, b * H * M * P * N * 2
+    return 2 * tok_h + 2 * tok_g + 3 * mem + b * L * H * 4
+
+
 def time_step(torch, dart, synth, cfg, steps, warmup, sets=1):
     """Events around dart_chunk_states and dart_sma_fwd of every step on the
     launch stream; ``sets`` input draws are used in turn (two keep a working
@@ -212,9 +230,8 @@ def time_gemm_probe(torch, steps, warmup, fwd_tflops):
 def time_backward(torch, dart, synth, cfg, steps=5, warmup=1):
     """The backward of the hot path on the same workload: dart_sma_bwd (the
     three matrix-core passes) from the forward's R and lse and a synthetic
-    loss gradient, then dart_chunk_states_bwd.  Algorithmic flops of the SMA
-    backward: 12NP per (token, visible chunk) pair (the recomputed W and V
-    products 4NP, dQ and dC 4NP, the two d_dH contractions 4NP)."""
+    loss gradient, then dart_chunk_states_bwd; algorithmic flops from
+    bwd_flops."""
     b, H, L, S = cfg["batch"], cfg["nheads"], cfg["seqlen"], cfg["chunk"]
     d = synth.draw_fwd_torch(**cfg, seed=0)
     dH = dart.dart_chunk_states(d["X"], d["B"], d["A"], S)
@@ -248,7 +265,7 @@ def time_backward(torch, dart, synth, cfg, steps=5, warmup=1):
     torch.cuda.synchronize()
     t_bwd = sum(e[0].elapsed_time(e[1]) for e in ev) / steps / 1e3
     t_csb = sum(e[1].elapsed_time(e[2]) for e in ev) / steps / 1e3
-    flops = 12 * cfg["d_state"] * cfg["d_head"] * fwd_pairs(b, H, L, S)
+    flops = bwd_flops(cfg)
     res = {"workload": cfg["name"], "kernel": "dart_sma_bwd", "us_per_call": t_bwd * 1e6,
            "flop_per_call": flops, "achieved_TFLOPs": flops / t_bwd / 1e12,
            "peak_TFLOPs": PEAK_BF16_TFLOPS, "frac": flops / t_bwd / 1e12 / PEAK_BF16_TFLOPS,
@@ -331,7 +348,7 @@ def time_rms(torch, dart, synth, cfg, steps=10, warmup=2, eps=1e-6):
         evb[k][1].record(st)
     torch.cuda.synchronize()
     t_bwd = sum(e[0].elapsed_time(e[1]) for e in evb) / bsteps / 1e3
-    fb = 12 * N * P * fwd_pairs(b, H, L, S)
+    fb = bwd_flops(cfg)
     res["backward"] = {"kernel": "dart_sma_bwd_rms", "us_per_call": t_bwd * 1e6, "flop_per_call": fb,
                        "achieved_TFLOPs": fb / t_bwd / 1e12, "peak_TFLOPs": PEAK_BF16_TFLOPS,
                        "frac": fb / t_bwd / 1e12 / PEAK_BF16_TFLOPS, "grad_dtype": "f32",
@@ -375,7 +392,7 @@ def time_ssd(torch, dart, synth, cfg, steps=10, warmup=2):
     e1.record(st)
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3 / steps
-    nbytes = 2 * (b * L * H * P * 2 + b * L * G * N * 2 + b * H * M * P * N * 3) + b * L * H * 4
+    nbytes = ssd_bytes(cfg)
     res = {"workload": cfg["name"], "kernel": "dart_ssd_fwd", "us_per_call": t * 1e6, "bytes_per_call": nbytes,
            "achieved_GBs": nbytes / t / 1e9, "peak_GBs": PEAK_HBM_GBS, "frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
            "tokens_per_s": b * L / t, "traffic_out_kernel": traffic_record("ssd_out", cfg["name"], "ssd")}

@@ -72,3 +72,16 @@ def test_path_bytes_of_the_long_workload():
     chunk_states = tok_h + tok_g + a + mem
     forward = 2 * tok_g + tok_h + mem + 3 * tok_h
     assert bench.path_bytes(LONG) == chunk_states + forward == 1211105280
+
+
+def test_backward_flops_are_three_forward_products():
+    # per pair: W and V recomputed (4NP), dQ and dC (4NP), the two d_dH terms (4NP)
+    assert bench.bwd_flops(LONG) == 3 * bench.fwd_flops(LONG)[0] == 2435246456832
+
+
+def test_ssd_bytes_of_the_long_workload():
+    x = y = 2 * 16384 * 24 * 64 * 2
+    b_in = c_in = 2 * 16384 * 24 * 128 * 2
+    a = 2 * 16384 * 24 * 4
+    mem = 2 * 24 * 64 * 64 * 128 * 2      # chunk memories out; entering states out and back in
+    assert bench.ssd_bytes(LONG) == x + b_in + c_in + a + y + 3 * mem == 758120448
