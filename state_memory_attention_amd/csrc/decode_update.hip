@@ -14,8 +14,9 @@
 //
 // Memory bound: the float32 state (N x P per head) is read and written once
 // per token, the dtype cache row is written only when a chunk closes.  One
-// block per (b, h); every thread owns 8 consecutive entries (one 16- or
-// 32-byte vector) of rows p of the [P][N] state at a time.
+// block per (b, h), the token's B and x rows staged in LDS; every thread owns
+// 8 consecutive entries (one 32-byte vector) of rows p of the [P][N] state
+// at a time, and issues the loads of four such steps together.
 #include "dart_internal.h"
 #include "dev_common.h"
 
@@ -41,35 +42,59 @@ __global__ __launch_bounds__(kThreads) void decode_update_kernel(
     n_chunks[b] = (int32_t)(done < max_chunks ? done : max_chunks);
   }
   const float at = a[bh];
-  const T* xr = x + bh * P;
-  const T* br = B + (b * G + g) * N;
   float* st = state + bh * (int64_t)P * N;
   T* dst = (closes && c < max_chunks) ? cache + (bh * max_chunks + c) * (int64_t)P * N : nullptr;
-  const int64_t total = (int64_t)P * N;
+  const int total = P * N;  // N, P <= 256
+  // the token's B row and x row, as float32, shared by the whole block
+  __shared__ __attribute__((aligned(16))) float s_b[256];
+  __shared__ float s_x[256];
+  const T* br = B + (b * G + g) * N;
+  const T* xr = x + bh * P;
+  for (int i = threadIdx.x; i < N; i += kThreads) s_b[i] = Elem<T>::ld(br, i);
+  for (int i = threadIdx.x; i < P; i += kThreads) s_x[i] = Elem<T>::ld(xr, i);
+  __syncthreads();
   if ((N & 7) == 0) {
-    // 8 entries of one row per step: state as 2 float4, cache as 8 elements
-    for (int64_t i = (int64_t)threadIdx.x * 8; i < total; i += (int64_t)kThreads * 8) {
-      const int p = (int)(i / N), n = (int)(i % N);
-      const float xp = Elem<T>::ld(xr, p);
-      float4 s0 = *(const float4*)(st + i), s1 = *(const float4*)(st + i + 4);
-      float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    // 8 entries of one row per step (state as 2 float4, cache as 8
+    // elements); the state loads of kSteps steps are issued together
+    constexpr int kSteps = 4;
+    for (int i0 = threadIdx.x * 8; i0 < total; i0 += kThreads * 8 * kSteps) {
+      float4 sv[kSteps][2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = fmaf(at, v[k], Elem<T>::ld(br, n + k) * xp);
-      if (closes) {
-        if (dst)
+      for (int u = 0; u < kSteps; ++u) {
+        const int i = i0 + u * kThreads * 8;
+        if (i < total) {
+          sv[u][0] = *(const float4*)(st + i);
+          sv[u][1] = *(const float4*)(st + i + 4);
+        }
+      }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) Elem<T>::st(dst, i + k, v[k]);
-        *(float4*)(st + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *(float4*)(st + i + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {
-        *(float4*)(st + i) = make_float4(v[0], v[1], v[2], v[3]);
-        *(float4*)(st + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      for (int u = 0; u < kSteps; ++u) {
+        const int i = i0 + u * kThreads * 8;
+        if (i >= total) break;
+        const int p = i / N, n = i - p * N;
+        const float xp = s_x[p];
+        const float4 b0 = *(const float4*)(s_b + n), b1 = *(const float4*)(s_b + n + 4);
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        float v[8] = {sv[u][0].x, sv[u][0].y, sv[u][0].z, sv[u][0].w,
+                      sv[u][1].x, sv[u][1].y, sv[u][1].z, sv[u][1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = fmaf(at, v[k], bv[k] * xp);
+        if (closes) {
+          if (dst)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) Elem<T>::st(dst, i + k, v[k]);
+          *(float4*)(st + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+          *(float4*)(st + i + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+          *(float4*)(st + i) = make_float4(v[0], v[1], v[2], v[3]);
+          *(float4*)(st + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
       }
     }
   } else {
-    for (int64_t i = threadIdx.x; i < total; i += kThreads) {
-      const int p = (int)(i / N), n = (int)(i % N);
-      const float v = fmaf(at, st[i], Elem<T>::ld(br, n) * Elem<T>::ld(xr, p));
+    for (int i = threadIdx.x; i < total; i += kThreads) {
+      const int p = i / N, n = i - p * N;
+      const float v = fmaf(at, st[i], s_b[n] * s_x[p]);
       if (closes) {
         if (dst) Elem<T>::st(dst, i, v);
         st[i] = 0.f;
