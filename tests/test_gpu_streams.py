@@ -73,10 +73,11 @@ def test_ring_kernels_under_memory_contention():
     """The kernels that stream through an LDS ring give the same bits while
     another stream saturates HBM with 1 GiB copies (longer and more varied
     load latencies): chunk states at b1 H32 L65536 with S = 1024 (16 ring
-    stages per chunk) and the backward (its d_dH pass) at b2 H24 L16384,
-    each against a run on a quiet GPU.  A guard on run-to-run equality under
-    load, not a detector of every wait error: a stage issued two iterations
-    before it is read has almost always landed."""
+    stages per chunk), and at b2 H24 L16384 the forward (with R and lse), the
+    normalised forward and the backward, each against a run on a quiet GPU.
+    A guard on run-to-run equality under load, not a detector of every wait
+    error: a stage issued two iterations before it is read has almost always
+    landed."""
     cfg_v = synth.workload(synth.VLONG, chunk=1024)
     dv = synth.draw_fwd_torch(**cfg_v, seed=41)
     cfg_l = synth.workload(synth.LONG)
@@ -87,10 +88,15 @@ def test_ring_kernels_under_memory_contention():
                                   want_lse=True)
     dout_l = synth.draw_grad_torch(tuple(dl["Y"].shape), "bf16", 43)
 
+    dHr, _, score = dart.dart_chunk_states_rms(dl["X"], dl["B"], dl["A"], S_l, 1e-6)
+
     def work():
         cs = dart.dart_chunk_states(dv["X"], dv["B"], dv["A"], 1024)
+        fw = dart.dart_sma_fwd(dl["Q"], dl["C"], dl["E"], dH_l, dl["Y"], dl["gate"], S_l, want_R=True,
+                               want_lse=True)
+        fr = dart.dart_sma_fwd_rms(dl["Q"], dl["C"], dl["E"], dHr, score, dl["Y"], dl["gate"], S_l, 1e-6)[0]
         bw = dart.dart_sma_bwd(dl["Q"], dl["C"], dl["E"], dH_l, dl["gate"], R_l, lse_l, dout_l, S_l)
-        return (cs,) + tuple(bw)
+        return (cs,) + tuple(fw) + (fr,) + tuple(bw)
 
     quiet = work()
     torch.cuda.synchronize()
@@ -106,6 +112,7 @@ def test_ring_kernels_under_memory_contention():
         loud = [work() for _ in range(2)]
     torch.cuda.synchronize()
     for rep, res in enumerate(loud):
-        for name, x, y in zip(("dH (S = 1024)", "dQ", "dC", "dE", "d_dH", "dgate"), quiet, res):
+        for name, x, y in zip(("dH (S = 1024)", "out", "R", "lse", "normalised out", "dQ", "dC", "dE", "d_dH",
+                               "dgate"), quiet, res):
             same(x, y, f"under contention, run {rep}: {name}")
     say("ring kernels under memory contention: bitwise equal to the quiet runs")
