@@ -524,8 +524,8 @@ def time_mfma_probe(torch, dH, Q, steps, warmup, fwd_tflops):
 
 def time_read_probe(torch, buf, steps, warmup, decode_gbs):
     """What a plain streaming read of the same bytes draws from HBM on this
-    device (libdart_probe.so: 16-byte vector loads, four in flight per lane,
-    16384 blocks): the practical ceiling for a read-bound call, beside the
+    device (libdart_probe.so: 16-byte non-temporal loads, eight in flight per
+    lane, 8192 blocks): the practical ceiling for a read-bound call, beside the
     8 TB/s figure."""
     import ctypes
 
@@ -754,7 +754,7 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
             ("sma_bwd_bc", "sma_bwd", "sma_bwd_bc_kernel", w_long, 0),
             ("sma_bwd_d", "sma_bwd", "sma_bwd_d_kernel", w_long, 0),
             ("chunk_states_bwd", "chunk_states_bwd", "chunk_states_bwd_mfma_kernel", w_long, 0),
-            ("chunk_states_rms", "chunk_states_rms", "chunk_states_mfma_kernel<true>", w_long, 0),
+            ("chunk_states_rms", "chunk_states_rms", "chunk_states_mfma_kernel<true,", w_long, 0),
             ("sma_fwd_rms", "sma_fwd_rms", "sma_fwd_rms_mfma_kernel", w_long, 0),
             ("sma_bwd_rms_a", "sma_bwd_rms", "sma_bwd_rms_a_kernel", w_long, 0),
             ("sma_bwd_rms_bc_q", "sma_bwd_rms", "sma_bwd_bc_kernel<1>", w_long, 0),

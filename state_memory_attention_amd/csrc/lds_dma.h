@@ -58,6 +58,12 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
                                            0, 0, 0);
 }
+// The same with the non-temporal policy, for operands that no other block
+// reads again (a stream read once sustains more bandwidth this way).
+__device__ __forceinline__ void buf_dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           0, 0, kNonTemporal);
+}
 
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt
 // in 11:8; a field at its maximum does not wait).  Issued as builtins, not as

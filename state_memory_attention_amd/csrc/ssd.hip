@@ -266,6 +266,9 @@ __device__ __forceinline__ void ssd_intra_block(f32x16_t (&y)[2], const bf16x8_t
 constexpr int kWavesOut = 8;
 constexpr int kThreadsOut = 64 * kWavesOut;
 
+// kNtB: B rows with the non-temporal policy (a group of one head: no other
+// block reads them); X and the entering state always (read by this block only)
+template <bool kNtB>
 __global__ __launch_bounds__(kThreadsOut) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void ssd_out_mfma_kernel(SsdArgs a) {
   // One LDS object (so that the compiler adds no waits of its own for the
@@ -311,7 +314,11 @@ void ssd_out_mfma_kernel(SsdArgs a) {
     uint8_t* st = s_lds + kOffB + (j % 3) * kBStage;
     const int r = 4 * wave + (lane >> 4);  // row within the block
     const int rr = 32 * j + r;             // row within the chunk
-    buf_dma16(rbb, (uint32_t)(rr * a.G * kN * 2 + (((lane & 15) ^ (r & 15)) << 4)), st + 4 * wave * 256);
+    const uint32_t off = (uint32_t)(rr * a.G * kN * 2 + (((lane & 15) ^ (r & 15)) << 4));
+    if constexpr (kNtB)
+      buf_dma16_nt(rbb, off, st + 4 * wave * 256);
+    else
+      buf_dma16(rbb, off, st + 4 * wave * 256);
   };
   {
     const auto rx = buf_rsrc(wave_uniform(a.X + ((row0 + s0) * a.H + h) * kP), (uint32_t)((clen - 1) * a.H * kP + kP) * 2);
@@ -323,13 +330,13 @@ void ssd_out_mfma_kernel(SsdArgs a) {
       const int rb = 8 * (wave + kWavesOut * i);  // first row of the group
       const int r = rb + (lane >> 3);
       const int piece = (lane & 7) ^ swz_x(r);
-      buf_dma16(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + rb * 128);
+      buf_dma16_nt(rx, (uint32_t)(r * a.H * kP + piece * 8) * 2, s_x + rb * 128);
     }
     const auto rh = buf_rsrc(wave_uniform(a.Hin + ((int64_t)bh * a.M + c) * (kP * kN)), kP * kN * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = 8 * wave + 4 * i + (lane >> 4);
-      buf_dma16(rh, (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4)), s_h + (8 * wave + 4 * i) * 256);
+      buf_dma16_nt(rh, (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4)), s_h + (8 * wave + 4 * i) * 256);
     }
     issue_b(0);
     issue_b(1);
@@ -492,7 +499,10 @@ hipError_t launch_ssd_fwd(const Shape& s, bool bf16, bool mfma, const void* X, c
     a.hpg = (int)(s.H / s.G);
     a.S = (int)s.S;
     a.M = (int)s.M;
-    ssd_out_mfma_kernel<<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kThreadsOut), 0, st>>>(a);
+    if (a.hpg == 1)
+      ssd_out_mfma_kernel<true><<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kThreadsOut), 0, st>>>(a);
+    else
+      ssd_out_mfma_kernel<false><<<dim3((unsigned)(s.b * s.H * s.M)), dim3(kThreadsOut), 0, st>>>(a);
     return hipGetLastError();
   }
   const int64_t gph = (s.L + 3) / 4;

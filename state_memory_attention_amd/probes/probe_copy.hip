@@ -3,9 +3,10 @@
 //   * a plain device copy of a known number of bytes (16-byte vector loads and
 //     stores, grid-stride), used to calibrate the hardware memory-traffic
 //     counters against kernels that access memory the same way;
-//   * a plain streaming read (16-byte vector loads, four in flight per lane,
-//     grid-stride), the yardstick for what a read-only kernel can draw from
-//     HBM on this device;
+//   * a streaming read (16-byte non-temporal vector loads, eight in flight
+//     per lane, 8192 blocks, grid-stride: the fastest of a sweep over 4-16
+//     loads in flight, 2048-65536 blocks, plain or non-temporal), the
+//     yardstick for what a read-only kernel can draw from HBM on this device;
 //   * a plain matrix-core loop (v_mfma_f32_32x32x16_bf16 on operands held in
 //     registers, two waves per SIMD, the forward's burst shape), the yardstick
 //     for what dense bf16 work sustains on this device at the clock it holds
@@ -16,6 +17,7 @@
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 probe_bf16x8_t;
 typedef float probe_f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int probe_u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 __global__ __launch_bounds__(256) void copy16_kernel(const uint4* __restrict__ src,
@@ -25,16 +27,19 @@ __global__ __launch_bounds__(256) void copy16_kernel(const uint4* __restrict__ s
 }
 // The loaded words are folded into one value per lane, written only if it
 // equals an impossible pattern, so that the loads are not optimised away.
-__global__ __launch_bounds__(256) void read16_kernel(const uint4* __restrict__ src, size_t n16,
+__global__ __launch_bounds__(256) void read16_kernel(const probe_u32x4_t* __restrict__ src, size_t n16,
                                                      unsigned* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   unsigned acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.w ^ b.y ^ b.z ^ c.x ^ c.w ^ d.y ^ d.z;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    probe_u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
   }
-  for (; i < n16; i += stride) acc ^= src[i].x;
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i).x;
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 // Each wave: 16 operand registers (8 A, 8 B) read once from `ops`, then
@@ -86,7 +91,8 @@ extern "C" int dart_probe_read(const void* src, size_t bytes, void* sink, void* 
   if (!src || !sink || (bytes & 15) || ((uintptr_t)src & 15)) return -1;
   const size_t n16 = bytes / 16;
   if (n16 == 0) return 0;
-  read16_kernel<<<dim3(16384), dim3(256), 0, (hipStream_t)stream>>>((const uint4*)src, n16, (unsigned*)sink);
+  read16_kernel<<<dim3(8192), dim3(256), 0, (hipStream_t)stream>>>((const probe_u32x4_t*)src, n16,
+                                                                  (unsigned*)sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
