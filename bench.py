@@ -35,7 +35,7 @@ _CSRC = "state_memory_attention_amd/csrc/"
 KERNEL_SOURCES = {
     "sma_fwd": [_CSRC + "sma_fwd_mfma.hip", _CSRC + "dev_common.h"],
     "chunk_states": [_CSRC + "chunk_states_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
-    "decode": [_CSRC + "sma_decode_mfma.hip", _CSRC + "dev_common.h"],
+    "decode": [_CSRC + "sma_decode_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "sma_bwd": [_CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "chunk_states_bwd": [_CSRC + "sma_bwd_mfma.hip", _CSRC + "dev_common.h", _CSRC + "lds_dma.h"],
     "state_update": [_CSRC + "decode_update.hip", _CSRC + "dev_common.h"],
@@ -748,7 +748,7 @@ def summarize_counters(fetch_csv, write_csv, launches=3):
             ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w_long, 0),
             ("chunk_states", "chunk_states", "chunk_states_mfma_kernel", w_vlong, 1 + launches + 1),
             ("sma_fwd", "sma_fwd", "sma_fwd_mfma_kernel", w_vlong, launches),
-            ("decode", "decode", "sma_decode_partial_kernel", w_dec, 0),
+            ("decode", "decode", "sma_decode_partial_lds_kernel", w_dec, 0),
             ("state_update", "state_update", "decode_update_kernel", w_dec, 0),
             ("sma_bwd_a", "sma_bwd", "sma_bwd_a_kernel", w_long, 0),
             ("sma_bwd_bc", "sma_bwd", "sma_bwd_bc_kernel", w_long, 0),

@@ -9,11 +9,18 @@
 // by HBM.  Design:
 //   * the chunk axis of each (b, h) is split into ranges; a block of 4 waves
 //     owns one range and each wave streams every 4th chunk of it;
-//   * per chunk a wave issues its sixteen 16-byte loads (the whole 16 KB
-//     memory) straight into MFMA B-operand registers and runs 16
-//     v_mfma_f32_16x16x32_bf16 with A = [q; c; 0 ...], so lanes 0..15 receive
-//     W = q dH and V = c dH for 16 values of p each -- the matrix core does the
-//     dot products and the VALU only runs the row-dot with e and the softmax;
+//   * per chunk a wave runs 16 v_mfma_f32_16x16x32_bf16 with A = [q; c; 0 ...]
+//     and the memory as B, so lanes 0..15 receive W = q dH and V = c dH for 16
+//     values of p each -- the matrix core does the dot products and the VALU
+//     only runs the row-dot with e and the softmax;
+//   * the plain decode stages each memory through a wave-private LDS ring in
+//     four 4 KB row groups, loaded as whole 256-byte rows with the
+//     non-temporal policy (6.9-7.0 TB/s on the decode workload, against
+//     6.1-6.2 when the sixteen 16-byte loads per memory went straight into
+//     the B-operand registers: each of those touched 16 rows x 64 bytes, so
+//     two instructions shared every 128-byte line, and the non-temporal
+//     policy then slowed them); the normalised branch, which also reads r_j
+//     per chunk, keeps the direct loads;
 //   * the 4 waves merge their (max, sum, O) states through LDS and write one
 //     partial per range to the workspace; a second kernel merges the ranges
 //     of each (b, h) in a fixed order (deterministic) and applies the gate.
@@ -30,6 +37,7 @@
 #include "dart.h"
 #include "dart_internal.h"
 #include "dev_common.h"
+#include "lds_dma.h"
 
 namespace dart {
 namespace {
@@ -39,6 +47,9 @@ constexpr int kP = 64;
 constexpr int kThreads = 256;
 constexpr int kMemBytes = kP * kN * 2;
 constexpr float kTau = 8.f;
+// LDS ring depth of the plain decode, per wave (4 KB stages: 64 KB a block, two
+// blocks per CU; 6 and 8 stages measured the same)
+constexpr int kDecStages = 4;
 
 struct DecArgs {
   const bf16_t* q;
@@ -231,6 +242,148 @@ __global__ __launch_bounds__(kThreads) void sma_decode_partial_kernel(DecArgs a)
   }
 }
 
+// Non-normalised decode with the cached memories staged through a wave-private
+// LDS ring: a stage is one 16-row group of a memory (4 KB, rows p = 16 pb ..
+// 16 pb + 15), loaded by four direct-to-LDS instructions of whole 256-byte
+// rows with the non-temporal policy; the MFMA B operands are read from there
+// (pieces XOR-swizzled by row, conflict-free).  Every stage index issues
+// exactly four loads (zero-length ones past the wave's last chunk), so the
+// wait before a stage always lets the next kStg - 1 stages stay in flight.
+template <int kStg>
+__global__ __launch_bounds__(kThreads) void sma_decode_partial_lds_kernel(DecArgs a) {
+  // one LDS object (the ring, then the merge area): with a single object the
+  // compiler adds no wait of its own for the ring loads before each read
+  constexpr int kRingBytes = 4 * kStg * 4096;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kRingBytes + (4 * kP + 8) * 4];
+  uint8_t* const s_ring = s_lds;
+  float (*const s_o)[kP] = (float (*)[kP])(s_lds + kRingBytes);
+  float* const s_m = (float*)(s_lds + kRingBytes + 4 * kP * 4);
+  float* const s_d = s_m + 4;
+
+  const int split = blockIdx.x % a.splits;
+  const int bh = blockIdx.x / a.splits;
+  const int b = bh / a.H, h = bh % a.H, g = h / a.hpg;
+  const int64_t nb = valid_chunks(a, b);
+  const int64_t c_begin = (int64_t)split * a.cps;
+  if (c_begin >= nb) return;  // whole block: this range holds no valid chunk
+  const int64_t c_end = (c_begin + a.cps < nb) ? c_begin + a.cps : nb;
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int row = lane & 15, kg = lane >> 4;
+  (void)h;
+
+  // this wave's chunks c_begin + wave + 4 k, k < n_my; stage s = 4 k + pb
+  const int64_t span = c_end - c_begin - wave;
+  const int n_my = span > 0 ? (int)((span + 3) / 4) : 0;
+  const int total = 4 * n_my;
+  const uint8_t* head = (const uint8_t*)(a.cache + (int64_t)bh * a.max_chunks * (kP * kN));
+  uint8_t* const ring = s_ring + wave * (kStg * 4096);
+  auto issue = [&](int s) {
+    const bool live = s < total;
+    const uint8_t* base = live ? head + (c_begin + wave + 4 * (int64_t)(s >> 2)) * kMemBytes + (s & 3) * 4096 : head;
+    const auto rs = buf_rsrc(wave_uniform(base), live ? 4096u : 0u);
+    uint8_t* dst = ring + (s % kStg) * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + (lane >> 4);  // row of the stage this lane fills
+      buf_dma16_nt(rs, (uint32_t)(r * 256 + (((lane & 15) ^ r) << 4)), dst + i * 1024);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kStg; ++s) issue(s);
+
+  // A operand rows: 0 = q, 1 = c, others zero; lane holds n = 32 kb + 8 kg + 0..7
+  bf16x8_t af[4];
+  {
+    const bool qrow = row == 0;
+    const bf16_t* src = qrow ? a.q : a.c;
+    const int64_t base = ((int64_t)b * a.G + g) * kN + 8 * kg;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qrow || row == 1) v = *(const uint4*)(src + base + 32 * kb);
+      af[kb] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  float ev[4];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+    ev[pb] = (lane < 16 ? bf16_to_f32(a.e[((int64_t)b * a.G + g) * kP + 16 * pb + lane]) : 0.f) * a.e_scale;
+
+  float m = -INFINITY, d = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n_my; ++k) {
+    float part = 0.f;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      const int s = 4 * k + pb;
+      // stage s has landed; stages s+1 .. s+kStg-1 may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (4 * (kStg - 1) & 15) | ((4 * (kStg - 1) >> 4) << 14));
+      asm volatile("" ::: "memory");
+      const uint8_t* src = ring + (s % kStg) * 4096 + row * 256;
+      bf16x8_t bf[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) bf[kb] = *(const bf16x8_t*)(src + (((4 * kb + kg) ^ row) << 4));
+      // the reads are done before the buffer is refilled
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      asm volatile("" ::: "memory");
+      issue(s + kStg);
+      acc[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kb], bf[kb], acc[pb], 0, 0, 0);
+      part = fmaf(acc[pb][0], ev[pb], part);
+    }
+    part += __shfl_xor(part, 8);
+    part += __shfl_xor(part, 4);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 1);
+    const float l2 = part;
+    const float mn = (l2 > m + kTau) ? l2 : m;
+    if (__any(mn != m)) {
+      const float alpha = (mn == m) ? 1.f : fast_exp2(m - mn);
+      d *= alpha;
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) o[pb] *= alpha;
+      m = mn;
+    }
+    const float pj = fast_exp2(l2 - m);
+    d += pj;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) o[pb] = fmaf(pj, acc[pb][1], o[pb]);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the stand-in stages have landed
+
+  if (lane < 16) {
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) s_o[wave][16 * pb + lane] = o[pb];
+  }
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_d[wave] = d;
+  }
+  __syncthreads();
+  if (tid < kP) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_d[w] > 0.f) M = fmaxf(M, s_m[w]);
+    float D = 0.f, Ov = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_d[w] > 0.f) {
+        const float f = fast_exp2(s_m[w] - M);
+        D = fmaf(s_d[w], f, D);
+        Ov = fmaf(s_o[w][tid], f, Ov);
+      }
+    float* dst = a.ws + ((int64_t)bh * a.splits + split) * (kP + 2);
+    if (tid == 0) {
+      dst[0] = M;
+      dst[1] = D;
+    }
+    dst[2 + tid] = Ov;
+  }
+}
+
 // Merge the chunk ranges of one (b, h) in range order; gate and write.
 __global__ __launch_bounds__(kP) void sma_decode_combine_kernel(
     DecArgs a, const bf16_t* __restrict__ y, const bf16_t* __restrict__ gate, int gate_pc,
@@ -340,7 +493,7 @@ hipError_t launch_sma_decode_mfma(const Shape& s, int64_t max_chunks, const Deco
     if (r_cache)
       sma_decode_partial_kernel<true><<<dim3((unsigned)(bh * plan.splits)), dim3(kThreads), 0, st>>>(a);
     else
-      sma_decode_partial_kernel<false><<<dim3((unsigned)(bh * plan.splits)), dim3(kThreads), 0, st>>>(a);
+      sma_decode_partial_lds_kernel<kDecStages><<<dim3((unsigned)(bh * plan.splits)), dim3(kThreads), 0, st>>>(a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
