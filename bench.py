@@ -523,7 +523,7 @@ def time_mfma_probe(torch, dH, Q, steps, warmup, fwd_tflops):
 
 
 def time_read_probe(torch, buf, steps, warmup, decode_gbs):
-    """What a plain streaming read of the same bytes draws from HBM on this
+    """What a streaming read of the same bytes draws from HBM on this
     device (libdart_probe.so: 16-byte non-temporal loads, eight in flight per
     lane, 8192 blocks): the practical ceiling for a read-bound call, beside the
     8 TB/s figure."""
